@@ -1,0 +1,198 @@
+/*
+ * kq.h — C ABI of the KronQ per-linear-layer quantization solver for MI355X (gfx950).
+ *
+ * The method (KronQ: LLM Quantization via Kronecker-Factored Hessian; summary
+ * on hyper.ai, section "Method"; explainer on gist.science, "Metodologia")
+ * models the Hessian of a linear layer y = W x as H ~ H_X (x) H_G and
+ * quantizes W column by column with the GPTAQ update, after bidirectional
+ * incoherence processing (BiIP). This library implements that per-layer path
+ * as five device stages plus a host-side allocator:
+ *
+ *   kq_accumulate_cov   H_X = X~^T X~ / N, D = dX^T X~ / N, H_G = G^T G / N
+ *   kq_biip             diagonal scalings S_X, S_G and random Hadamard U, V
+ *   kq_sensitivity      s = tr(H_G') * tr(H_X')
+ *   kq_cholesky_inv     upper U with U^T U = (H_X' + delta I)^-1
+ *   kq_gptaq_quantize   blocked column sweep onto a 2/3/4-bit grid
+ *   kq_allocate_bits    widths by descending s under an average-bit budget
+ *
+ * Conventions (all calls):
+ *  - Matrices are dense and row-major; the row stride equals the column
+ *    count. Token-major activations X (N x d_in) hold one token per row, so
+ *    X^T X is the page's E[x x^T] up to 1/N.
+ *  - Pointers are DEVICE pointers unless marked "host". The caller owns every
+ *    buffer; the library allocates nothing and keeps no state between calls.
+ *    Scratch memory is passed in as (ws, ws_bytes); kq_workspace_size gives
+ *    the size each call needs.
+ *  - Device work is enqueued on `stream` and is asynchronous, except calls
+ *    that return host values (kq_sensitivity, kq_cholesky_inv,
+ *    kq_layer_objective), which synchronize the stream before returning.
+ *  - Arguments are validated on the host before anything is launched;
+ *    errors return a kq_status and kq_last_error() gives a message (per
+ *    thread). Calls on disjoint buffers may run concurrently.
+ *  - Sizes are int64; every dimension must be >= 1 unless stated.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KQ_OK = 0,
+  KQ_ERR_ARG = 1,          /* null pointer, bad enum, bad scalar */
+  KQ_ERR_SHAPE = 2,        /* bad dimension or block size */
+  KQ_ERR_NOT_PD = 3,       /* factorisation met a non-positive pivot (see info) */
+  KQ_ERR_NONFINITE = 4,    /* NaN or Inf met where a finite value is required */
+  KQ_ERR_WORKSPACE = 5,    /* ws_bytes smaller than kq_workspace_size */
+  KQ_ERR_HIP = 6,          /* a HIP runtime call failed */
+  KQ_ERR_UNSUPPORTED = 7   /* valid request this build does not implement */
+} kq_status;
+
+typedef enum { KQ_BF16 = 0, KQ_F32 = 1 } kq_dtype;
+
+typedef enum {
+  KQ_OP_ACCUMULATE_COV = 0,
+  KQ_OP_BIIP = 1,
+  KQ_OP_SENSITIVITY = 2,
+  KQ_OP_CHOLESKY_INV = 3,
+  KQ_OP_FORM_P = 4,
+  KQ_OP_GPTAQ_QUANTIZE = 5,
+  KQ_OP_LAYER_OBJECTIVE = 6
+} kq_op;
+
+/* Grid and sweep configuration (KronQ summary, Method and experiments:
+ * uniform 2/3/4-bit weight-only grids, per output channel or in groups of
+ * 128 input columns; GPTAQ lazy block of 128 columns). */
+typedef struct {
+  int32_t bits;   /* 2, 3 or 4 (codes in [0, 2^bits - 1]) */
+  int32_t group;  /* 0 = one grid per output channel; else 128 (columns per group) */
+  int32_t block;  /* lazy-update block of the sweep; must be 128 */
+  int32_t flags;  /* reserved, must be 0 */
+} kq_quant_cfg;
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* kq_last_error(void);
+
+/* Library version string. */
+const char* kq_version(void);
+
+/* Bytes of scratch memory `op` needs for the given sizes (host output).
+ * n_tok and dtype matter for KQ_OP_ACCUMULATE_COV only; cfg for
+ * KQ_OP_GPTAQ_QUANTIZE only (may be NULL elsewhere). For square-matrix ops
+ * (CHOLESKY_INV, FORM_P) pass the matrix order as d_in. */
+kq_status kq_workspace_size(kq_op op, int64_t d_out, int64_t d_in, int64_t n_tok,
+                            kq_dtype dtype, const kq_quant_cfg* cfg, size_t* bytes);
+
+/* Stage 1 — covariances (KronQ summary, Method: Fisher equation and the
+ * K-FAC step H ~ H_X (x) H_G; GPTAQ objective: the asymmetric term dX X^T).
+ *   HX <- alpha * Xq^T Xq + beta * HX        (d_in x d_in, full symmetric)
+ *   D  <- alpha * dX^T Xq + beta * D         (d_in x d_in, not symmetric)
+ *   HG <- alpha * G^T G   + beta * HG        (d_out x d_out, full symmetric)
+ * X, Xq: n_tok x d_in token-major inputs of the full-precision and the
+ * quantized model; G: n_tok x d_out output gradients. dt = KQ_BF16 (uint16
+ * bf16 patterns) or KQ_F32. dX = X - Xq in fp32, rounded to bf16 (nearest
+ * even) when dt = KQ_BF16. Products are exact, sums are fp32.
+ * Stream chunks of tokens by calling with beta = 0 on the first chunk and
+ * beta = 1 after, alpha = 1 / (total tokens). HX, D, HG may each be NULL to
+ * skip that output (D needs X and Xq; HX needs Xq; HG needs G). */
+kq_status kq_accumulate_cov(const void* X, const void* Xq, const void* G, kq_dtype dt,
+                            int64_t n_tok, int64_t d_in, int64_t d_out,
+                            float alpha, float beta,
+                            float* HX, float* D, float* HG,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage 2 — bidirectional incoherence processing (KronQ summary, Method:
+ * BiIP scaling equation and rotation equation), in place:
+ *   s_j = (HX_jj / ||W_:,j||^2)^(1/4),  t_i = (HG_ii / ||W_i,:||^2)^(1/4)
+ *   (a zero diagonal or zero norm gives 1; both from the unscaled W)
+ *   W  <- U diag(t) W diag(s) V^T
+ *   HX <- V diag(1/s) HX diag(1/s) V^T,   D <- V diag(1/s) D diag(1/s) V^T
+ *   HG <- U diag(1/t) HG diag(1/t) U^T
+ * with V = blockdiag(H_b / sqrt(b)) diag(sign_in) over d_in (Sylvester H_b,
+ * b = blk_in) and U likewise over d_out with sign_out, blk_out. blk = 0
+ * selects the largest power of two dividing the dimension; a nonzero blk
+ * must be a power of two in [1, 8192] dividing it (blocks above 8192 return
+ * KQ_ERR_UNSUPPORTED). W: d_out x d_in; HX, D: d_in x d_in; HG:
+ * d_out x d_out; D may be NULL. sign_in, sign_out: int8 +-1 (device).
+ * s_x (d_in) and s_g (d_out) receive s and t (device, may be NULL). */
+kq_status kq_biip(float* W, float* HX, float* D, float* HG, int64_t d_out, int64_t d_in,
+                  const int8_t* sign_in, const int8_t* sign_out,
+                  int64_t blk_in, int64_t blk_out, float* s_x, float* s_g,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage 5 — sensitivity (KronQ summary, Method: s = tr(H_G) * tr(H_X), taken
+ * after BiIP). Reads the diagonals of HX (d_in x d_in) and HG (d_out x d_out)
+ * and sums them in fp64. trHX, trHG, s: host outputs (any may be NULL).
+ * Synchronizes the stream. */
+kq_status kq_sensitivity(const float* HX, const float* HG, int64_t d_in, int64_t d_out,
+                         double* trHX, double* trHG, double* s,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage 3 — inverse-Hessian factor for the OBS update (KronQ summary,
+ * Method: the column update uses rows of H_X^-1). With
+ * delta = damp * mean(diag H), computes the upper-triangular U (n x n, lower
+ * part set to 0) with U^T U = (H + delta I)^-1, so that U_pp * U_{p,p:} is
+ * row p of the inverse of the trailing block (H + delta I)_{p:,p:}.
+ * H: n x n symmetric; only its upper triangle (j >= i) is read. fp32 throughout. info (host, may be NULL)
+ * receives 0, or k+1 where k is the original column index of the first
+ * non-positive pivot (the factorisation proceeds from the last column to the
+ * first); that case returns KQ_ERR_NOT_PD and leaves U undefined.
+ * Synchronizes the stream. */
+kq_status kq_cholesky_inv(const float* H, int64_t n, float damp, float* U, int32_t* info,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The GPTAQ asymmetric correction (KronQ summary, Method: the matrix P of the
+ * OBS update, not written out on the pages). P = triu_1(D U^T) U (n x n,
+ * strictly upper, zeros elsewhere): row p equals D_{p,F} ((H+delta I)_{FF})^-1
+ * with F = {p+1, ..., n-1}. kq_gptaq_quantize forms it internally; this entry
+ * exposes it for inspection. */
+kq_status kq_form_p(const float* D, const float* U, int64_t n, float* P,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage 4 — GPTAQ column sweep (KronQ summary, Method: column-wise OBS
+ * update dW_{:,p+1:} = -delta_p [H_X^-1]_{p,p+1:} + W_{:,p} P_{p,p+1:};
+ * H_G cancels from it, gist.science Metodologia, Proposition 1).
+ * W: d_out x d_in; on entry the processed weights W0', on exit the
+ * dequantized W^'. U: the factor from kq_cholesky_inv. D: the processed
+ * drift term (NULL = plain GPTQ, P = 0). For each column p in order:
+ *   q = clamp(rint(w_p / scale) + zero, 0, 2^bits - 1),  w^_p = scale (q - zero)
+ *   w_{p+1:} -= ((w_p - w^_p) / U_pp) U_{p,p+1:} ;  w_{p+1:} += W0_p P_{p,p+1:}
+ * Grid (fp32): lo = min(v, 0), hi = max(v, 0) ([-1,1] if both 0),
+ * scale = (hi - lo) / (2^bits - 1), zero = rint(-lo / scale); per output
+ * channel from W0', or per group of 128 columns from the working values when
+ * the sweep reaches the group. Outputs: codes (d_out x d_in, uint8),
+ * scale, zero (d_out x n_groups fp32, n_groups = 1 per channel, else
+ * ceil(d_in / 128)). d_in must be a multiple of 128. */
+kq_status kq_gptaq_quantize(float* W, const float* U, const float* D,
+                            int64_t d_out, int64_t d_in, const kq_quant_cfg* cfg,
+                            uint8_t* codes, float* scale, float* zero,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Mixed-precision allocation (KronQ summary, Method: sublayers with larger
+ * s get wider codes). Host only, deterministic. Visits the L sublayers in
+ * descending s (ties by index) and gives each the widest of `widths` that
+ * still leaves every unvisited sublayer the narrowest width within
+ * sum(bits_l * n_params_l) <= avg_budget * sum(n_params_l).
+ * s, n_params, widths: host arrays; bits_out: host array of L. */
+kq_status kq_allocate_bits(const double* s, const int64_t* n_params, int32_t L,
+                           const int32_t* widths, int32_t n_widths, double avg_budget,
+                           int32_t* bits_out);
+
+/* Layer objective (KronQ summary, Method: Kronecker objective and its GPTAQ
+ * extension), a metric rather than a stage:
+ *   obj = tr[HG (dW HX dW^T + 2 W0 D dW^T)],  dW = W0 - What
+ * (D may be NULL). fp32 products, fp64 final sum. obj: host output.
+ * Synchronizes the stream. */
+kq_status kq_layer_objective(const float* W0, const float* What, const float* HX,
+                             const float* D, const float* HG, int64_t d_out, int64_t d_in,
+                             double* obj, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KQ_H */

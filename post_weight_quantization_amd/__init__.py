@@ -1,0 +1,19 @@
+"""KronQ per-linear-layer quantization solver, native on MI355X (gfx950).
+
+The computation lives in libkq.so (HIP kernels behind the C ABI of
+include/kq.h). ``api`` is a thin torch binding with the same entry-point
+names; ``layer`` chains the entry points for one layer. Importing this
+package raises if the library has not been built.
+"""
+from ._native import KQError, LIB_PATH  # noqa: F401
+from .api import (  # noqa: F401
+    kq_accumulate_cov,
+    kq_allocate_bits,
+    kq_biip,
+    kq_cholesky_inv,
+    kq_form_p,
+    kq_gptaq_quantize,
+    kq_layer_objective,
+    kq_sensitivity,
+    kq_workspace_size,
+)

@@ -1,0 +1,169 @@
+"""Thin torch binding of the C ABI in include/kq.h.
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: it reads shapes and device pointers from torch tensors, allocates
+outputs and scratch memory with torch when the caller passes none, and passes
+the current HIP stream. Every step of the computation runs in libkq's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native as N
+from ._native import KQError, check  # noqa: F401
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def kq_workspace_size(op: int, d_out: int, d_in: int, n_tok: int = 0, dtype: int = N.KQ_BF16,
+                      cfg: N.kq_quant_cfg | None = None) -> int:
+    out = ctypes.c_size_t(0)
+    check(N.lib.kq_workspace_size(op, d_out, d_in, n_tok, dtype,
+                                  ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out)))
+    return out.value
+
+
+def _ws(nbytes: int, device, ws):
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def kq_accumulate_cov(X, Xq, G, alpha: float, beta: float, HX=None, D=None, HG=None,
+                      ws=None, stream=None, want=("HX", "D", "HG")):
+    """HX, D, HG <- alpha * (covariance of this chunk) + beta * old (see kq.h).
+
+    X, Xq: (n_tok, d_in); G: (n_tok, d_out); uint16 (bf16 patterns) or float32.
+    Outputs listed in ``want`` are allocated when not given.
+    """
+    ref = Xq if Xq is not None else G
+    _need_cuda(X, Xq, G, HX, D, HG)
+    dt = N.KQ_F32 if ref.dtype == torch.float32 else N.KQ_BF16
+    n_tok = ref.shape[0]
+    d_in = Xq.shape[1] if Xq is not None else 8
+    d_out = G.shape[1] if G is not None else 8
+    dev = ref.device
+    if HX is None and "HX" in want and Xq is not None:
+        HX = torch.empty(d_in, d_in, dtype=torch.float32, device=dev)
+    if D is None and "D" in want and X is not None and Xq is not None:
+        D = torch.empty(d_in, d_in, dtype=torch.float32, device=dev)
+    if HG is None and "HG" in want and G is not None:
+        HG = torch.empty(d_out, d_out, dtype=torch.float32, device=dev)
+    if ws is None:
+        need = kq_workspace_size(N.KQ_OP_ACCUMULATE_COV, d_out, d_in, n_tok, dt)
+        ws = _ws(need, dev, None)
+    check(N.lib.kq_accumulate_cov(_ptr(X), _ptr(Xq), _ptr(G), dt, n_tok, d_in, d_out, alpha, beta,
+                                  _ptr(HX), _ptr(D), _ptr(HG), _ptr(ws), ws.numel(), _stream(stream)))
+    return HX, D, HG
+
+
+def kq_biip(W, HX, D, HG, sign_in, sign_out, blk_in: int = 0, blk_out: int = 0, s_x=None,
+            s_g=None, ws=None, stream=None):
+    """In-place bidirectional incoherence processing; returns (s_x, s_g)."""
+    _need_cuda(W, HX, D, HG, sign_in, sign_out)
+    d_out, d_in = W.shape
+    dev = W.device
+    if s_x is None:
+        s_x = torch.empty(d_in, dtype=torch.float32, device=dev)
+    if s_g is None:
+        s_g = torch.empty(d_out, dtype=torch.float32, device=dev)
+    ws = _ws(kq_workspace_size(N.KQ_OP_BIIP, d_out, d_in), dev, ws)
+    check(N.lib.kq_biip(_ptr(W), _ptr(HX), _ptr(D), _ptr(HG), d_out, d_in, _ptr(sign_in),
+                        _ptr(sign_out), blk_in, blk_out, _ptr(s_x), _ptr(s_g), _ptr(ws), ws.numel(),
+                        _stream(stream)))
+    return s_x, s_g
+
+
+def kq_sensitivity(HX, HG, ws=None, stream=None):
+    """(tr HX, tr HG, s) as Python floats (synchronizes the stream)."""
+    _need_cuda(HX, HG)
+    ws = _ws(kq_workspace_size(N.KQ_OP_SENSITIVITY, HG.shape[0], HX.shape[0]), HX.device, ws)
+    tx, tg, s = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    check(N.lib.kq_sensitivity(_ptr(HX), _ptr(HG), HX.shape[0], HG.shape[0], ctypes.byref(tx),
+                               ctypes.byref(tg), ctypes.byref(s), _ptr(ws), ws.numel(),
+                               _stream(stream)))
+    return tx.value, tg.value, s.value
+
+
+def kq_cholesky_inv(H, damp: float, U=None, ws=None, stream=None):
+    """Upper U with U^T U = (H + damp*mean(diag H) I)^-1 (synchronizes the stream)."""
+    _need_cuda(H, U)
+    n = H.shape[0]
+    if U is None:
+        U = torch.empty_like(H)
+    ws = _ws(kq_workspace_size(N.KQ_OP_CHOLESKY_INV, n, n), H.device, ws)
+    info = ctypes.c_int32(0)
+    st = N.lib.kq_cholesky_inv(_ptr(H), n, damp, _ptr(U), ctypes.byref(info), _ptr(ws), ws.numel(),
+                               _stream(stream))
+    check(st, info.value)
+    return U
+
+
+def kq_form_p(D, U, P=None, ws=None, stream=None):
+    _need_cuda(D, U, P)
+    n = D.shape[0]
+    if P is None:
+        P = torch.empty_like(D)
+    ws = _ws(kq_workspace_size(N.KQ_OP_FORM_P, n, n), D.device, ws)
+    check(N.lib.kq_form_p(_ptr(D), _ptr(U), n, _ptr(P), _ptr(ws), ws.numel(), _stream(stream)))
+    return P
+
+
+def kq_gptaq_quantize(W, U, D, bits: int, group: int = 0, block: int = 128, codes=None,
+                      scale=None, zero=None, ws=None, stream=None):
+    """In place W0' -> W^'; returns (codes, scale, zero)."""
+    _need_cuda(W, U, D, codes, scale, zero)
+    d_out, d_in = W.shape
+    dev = W.device
+    cfg = N.kq_quant_cfg(bits, group, block, 0)
+    ng = d_in // group if group else 1
+    if codes is None:
+        codes = torch.empty(d_out, d_in, dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(d_out, ng, dtype=torch.float32, device=dev)
+    if zero is None:
+        zero = torch.empty(d_out, ng, dtype=torch.float32, device=dev)
+    ws = _ws(kq_workspace_size(N.KQ_OP_GPTAQ_QUANTIZE, d_out, d_in, cfg=cfg), dev, ws)
+    check(N.lib.kq_gptaq_quantize(_ptr(W), _ptr(U), _ptr(D), d_out, d_in, ctypes.byref(cfg),
+                                  _ptr(codes), _ptr(scale), _ptr(zero), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return codes, scale, zero
+
+
+def kq_allocate_bits(s, n_params, widths=(2, 3, 4), avg_budget: float = 2.5):
+    L = len(s)
+    sa = (ctypes.c_double * L)(*[float(v) for v in s])
+    na = (ctypes.c_int64 * L)(*[int(v) for v in n_params])
+    wa = (ctypes.c_int32 * len(widths))(*[int(v) for v in widths])
+    out = (ctypes.c_int32 * L)()
+    check(N.lib.kq_allocate_bits(sa, na, L, wa, len(widths), avg_budget, out))
+    return [int(v) for v in out]
+
+
+def kq_layer_objective(W0, What, HX, D, HG, ws=None, stream=None) -> float:
+    _need_cuda(W0, What, HX, D, HG)
+    d_out, d_in = W0.shape
+    ws = _ws(kq_workspace_size(N.KQ_OP_LAYER_OBJECTIVE, d_out, d_in), W0.device, ws)
+    obj = ctypes.c_double()
+    check(N.lib.kq_layer_objective(_ptr(W0), _ptr(What), _ptr(HX), _ptr(D), _ptr(HG), d_out, d_in,
+                                   ctypes.byref(obj), _ptr(ws), ws.numel(), _stream(stream)))
+    return obj.value

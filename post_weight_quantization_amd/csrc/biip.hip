@@ -1,0 +1,336 @@
+// Stage 2: bidirectional incoherence processing (BiIP), and the trace
+// reduction of the sensitivity score.
+//
+// KronQ summary (hyper.ai), Method: W <- S_G W S_X with
+// S_X = diag(H_X,jj / ||W_:,j||^2)^(1/4), S_G = diag(H_G,ii / ||W_i,:||^2)^(1/4),
+// then W <- U W V^T, H_X <- V H_X V^T, H_G <- U H_G U^T, dX X^T <- V dX X^T V^T
+// with random Hadamard U, V. The covariances take the inverse scalings so the
+// Kronecker objective is unchanged.
+//
+// Each two-sided transform M <- A diag(f) M diag(g) B^T (Hadamard blocks,
+// signs and scalings folded into f, g) is done as
+//   * a row pass: every element is multiplied by f_i g_j and the gain, then
+//     each row is transformed blockwise (block b | cols) — rows are
+//     contiguous, so a workgroup loads an 8192-element chunk (whole blocks)
+//     with float4 loads into LDS, applies radix-8 butterfly passes there and
+//     writes it back: one HBM read and one write;
+//   * a column pass: the transform along the row index, in passes of at most
+//     6 row-index bits. Chunks are nr rows x W columns with nr*W <= 4096 and
+//     W >= 64 where the width allows (256-byte row segments). Blocks of up
+//     to 64 rows take one pass; larger blocks take an inner pass over the low
+//     row-index bits and outer passes over the higher bits (rows at a
+//     stride), each a read and a write.
+#include "kq_internal.h"
+
+namespace kq {
+
+namespace {
+
+constexpr int CH = 4096;   // elements per LDS chunk of the column pass
+constexpr int CHR = 8192;  // elements per LDS chunk of the row pass (Hadamard blocks up to 8192)
+__device__ __host__ constexpr int padi(int i) { return i + (i >> 5); }
+constexpr int CHP = CH + CH / 32;
+constexpr int CHRP = CHR + CHR / 32;
+
+__device__ inline void bfly8(float v[8], int nb) {
+  // nb radix-2 stages over the 3-bit register index (nb <= 3)
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (s >= nb) break;
+    const int h = 1 << s;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & h) continue;
+      const float a = v[j], b = v[j + h];
+      v[j] = a + b;
+      v[j + h] = a - b;
+    }
+  }
+}
+
+// Butterflies over bits [bit_lo, bit_lo + nbits) of the flat LDS index, for a
+// chunk of n_el (power of two) elements. Radix-8 register passes.
+__device__ void lds_fwht(float* s, int n_el, int bit_lo, int nbits) {
+  const int t = threadIdx.x;
+  for (int q = bit_lo; q < bit_lo + nbits; q += 3) {
+    const int nb = min(3, bit_lo + nbits - q);
+    const int span = 1 << nb;
+    const int ngroups = n_el >> nb;
+    for (int g = t; g < ngroups; g += blockDim.x) {
+      const int base = ((g >> q) << (q + nb)) | (g & ((1 << q) - 1));
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < span) v[j] = s[padi(base + (j << q))];
+      bfly8(v, nb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < span) s[padi(base + (j << q))] = v[j];
+    }
+    __syncthreads();
+  }
+}
+
+// Row pass: chunk = R rows x L cols (R*L = CHR, b | L, L | cols).
+__global__ __launch_bounds__(256) void fwht_rows_kernel(float* M, int64_t rows, int64_t cols,
+                                                        int lgL, int lgb, const float* rowf,
+                                                        const float* colf, float gain) {
+  __shared__ float s[CHRP];
+  const int L = 1 << lgL;
+  const int R = CHR >> lgL;
+  const int64_t chunks_per_row = cols >> lgL;
+  const int64_t rc = blockIdx.x / chunks_per_row;
+  const int64_t cc = blockIdx.x % chunks_per_row;
+  const int64_t r0 = rc * R;
+  const int64_t c0 = cc * L;
+  const int t = threadIdx.x;
+  for (int e = 4 * t; e < CHR; e += 4 * blockDim.x) {
+    const int rr = e >> lgL, c = e & (L - 1);
+    const int64_t row = r0 + rr;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < rows) {
+      v = *reinterpret_cast<const float4*>(M + row * cols + c0 + c);
+      const float f = gain * (rowf ? rowf[row] : 1.f);
+      if (colf) {
+        const float4 g = *reinterpret_cast<const float4*>(colf + c0 + c);
+        v.x *= f * g.x;
+        v.y *= f * g.y;
+        v.z *= f * g.z;
+        v.w *= f * g.w;
+      } else {
+        v.x *= f;
+        v.y *= f;
+        v.z *= f;
+        v.w *= f;
+      }
+    }
+    s[padi(e)] = v.x;
+    s[padi(e + 1)] = v.y;
+    s[padi(e + 2)] = v.z;
+    s[padi(e + 3)] = v.w;
+  }
+  __syncthreads();
+  lds_fwht(s, CHR, 0, lgb);
+  for (int e = 4 * t; e < CHR; e += 4 * blockDim.x) {
+    const int rr = e >> lgL, c = e & (L - 1);
+    const int64_t row = r0 + rr;
+    if (row < rows)
+      *reinterpret_cast<float4*>(M + row * cols + c0 + c) =
+          make_float4(s[padi(e)], s[padi(e + 1)], s[padi(e + 2)], s[padi(e + 3)]);
+  }
+}
+
+// Column pass: chunk = nr rows (at row stride rs, starting at a group base)
+// x W cols, nr * W <= CH. Transforms over the nr rows.
+__global__ __launch_bounds__(256) void fwht_cols_kernel(float* M, int64_t rows, int64_t cols,
+                                                        int lgnr, int lgW, int64_t rs,
+                                                        int64_t group_rows) {
+  __shared__ float s[CHP];
+  const int W = 1 << lgW;
+  const int n_el = 1 << (lgnr + lgW);
+  const int64_t col_chunks = cols >> lgW;
+  const int64_t rchunk = blockIdx.x / col_chunks;
+  const int64_t c0 = (blockIdx.x % col_chunks) * W;
+  // row chunks: groups of group_rows consecutive rows, each holding rs interleaved sets
+  const int64_t grp = rchunk / rs;
+  const int64_t off = rchunk % rs;
+  const int64_t rbase = grp * group_rows + off;
+  const int t = threadIdx.x;
+  for (int e = 4 * t; e < n_el; e += 4 * blockDim.x) {
+    const int a = e >> lgW, c = e & (W - 1);
+    const int64_t row = rbase + int64_t(a) * rs;
+    const float4 v = *reinterpret_cast<const float4*>(M + row * cols + c0 + c);
+    s[padi(e)] = v.x;
+    s[padi(e + 1)] = v.y;
+    s[padi(e + 2)] = v.z;
+    s[padi(e + 3)] = v.w;
+  }
+  __syncthreads();
+  lds_fwht(s, n_el, lgW, lgnr);
+  for (int e = 4 * t; e < n_el; e += 4 * blockDim.x) {
+    const int a = e >> lgW, c = e & (W - 1);
+    const int64_t row = rbase + int64_t(a) * rs;
+    *reinterpret_cast<float4*>(M + row * cols + c0 + c) =
+        make_float4(s[padi(e)], s[padi(e + 1)], s[padi(e + 2)], s[padi(e + 3)]);
+  }
+}
+
+// Sum of squares of each row (one wave per row).
+__global__ __launch_bounds__(256) void row_sumsq_kernel(const float* W, int64_t rows, int64_t cols,
+                                                        float* out) {
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float acc = 0.f;
+  const float* p = W + row * cols;
+  for (int64_t c = 4 * lane; c < cols; c += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(p + c);
+    acc += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) out[row] = acc;
+}
+
+// Column sums of squares over a chunk of rows: part[chunk][col].
+__global__ __launch_bounds__(256) void col_sumsq_kernel(const float* W, int64_t rows, int64_t cols,
+                                                        int64_t rows_per_chunk, float* part) {
+  const int64_t c = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t ch = blockIdx.y;
+  if (c >= cols) return;
+  const int64_t r0 = ch * rows_per_chunk;
+  const int64_t r1 = min(rows, r0 + rows_per_chunk);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t r = r0; r < r1; ++r) {
+    const float4 v = *reinterpret_cast<const float4*>(W + r * cols + c);
+    acc.x += v.x * v.x;
+    acc.y += v.y * v.y;
+    acc.z += v.z * v.z;
+    acc.w += v.w * v.w;
+  }
+  *reinterpret_cast<float4*>(part + ch * cols + c) = acc;
+}
+
+// Scale vectors. For each index k of a side (input or output):
+//   sc_k = (H_kk / n2_k)^(1/4)   (1 if H_kk <= 0 or n2_k <= 0)
+//   wf_k = sc_k * sign_k       (factor applied to W)
+//   hf_k = sign_k / sc_k       (factor applied to both sides of H)
+// n2 is the squared norm, summed here from nparts partial rows when given.
+__global__ void scales_kernel(const float* H, int64_t n, const float* n2, const float* part,
+                              int nparts, const int8_t* sign, float* sc_out, float* wf, float* hf) {
+  const int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  float nn;
+  if (part) {
+    nn = 0.f;
+    for (int p = 0; p < nparts; ++p) nn += part[p * n + k];
+  } else {
+    nn = n2[k];
+  }
+  const float h = H[k * n + k];
+  float sc = 1.f;
+  if (h > 0.f && nn > 0.f) sc = sqrtf(sqrtf(h / nn));
+  const float sg = float(sign[k]);
+  if (sc_out) sc_out[k] = sc;
+  wf[k] = sc * sg;
+  hf[k] = sg / sc;
+}
+
+__global__ __launch_bounds__(256) void diag_sum_kernel(const float* H, int64_t n, double* out) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) acc += double(H[i * n + i]);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+inline int ilog2(int64_t v) {
+  int k = 0;
+  while ((int64_t(1) << (k + 1)) <= v) ++k;
+  return k;
+}
+
+}  // namespace
+
+kq_status fwht_rows(float* M, int64_t rows, int64_t cols, int64_t blk, const float* rowf,
+                    const float* colf, float gain, hipStream_t s) {
+  // L: largest power of two with b | L, L | cols, L <= CH; rows per chunk R = CH / L.
+  int64_t L = blk;
+  while (L * 2 <= CHR && cols % (L * 2) == 0) L *= 2;
+  const int64_t R = CHR / L;
+  if (L > CHR) return fail(KQ_ERR_UNSUPPORTED, "biip: Hadamard blocks above %d are not supported", CHR);
+  const int64_t chunks = cdiv(rows, R) * (cols / L);
+  fwht_rows_kernel<<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, ilog2(L), ilog2(blk), rowf, colf, gain);
+  KQ_HIP(hipGetLastError());
+  return KQ_OK;
+}
+
+kq_status fwht_cols(float* M, int64_t rows, int64_t cols, int64_t blk, hipStream_t s) {
+  // passes over row-index bits [lo, lo + k) with at most 6 bits each; the
+  // chunk width W is the largest power of two <= 4096 / 2^k dividing cols
+  if (cols % 4) return fail(KQ_ERR_SHAPE, "biip: column count must be a multiple of 4");
+  const int lgb = ilog2(blk);
+  int lo = 0;
+  while (lo < lgb) {
+    const int k = std::min(6, lgb - lo);
+    const int64_t rs = int64_t(1) << lo;        // stride between transformed rows
+    const int64_t group_rows = rs << k;         // rows covered by one set of strided sets
+    int lgW = 12 - k;
+    while (lgW > 2 && cols % (int64_t(1) << lgW) != 0) --lgW;
+    const int64_t row_chunks = (rows / group_rows) * rs;
+    const int64_t chunks = row_chunks * (cols >> lgW);
+    fwht_cols_kernel<<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, k, lgW, rs, group_rows);
+    KQ_HIP(hipGetLastError());
+    lo += k;
+  }
+  return KQ_OK;
+}
+
+size_t biip_ws_bytes(int64_t d_out, int64_t d_in) {
+  Arena ar{nullptr, 0, 0};
+  const int64_t nchunk = std::min<int64_t>(64, d_out);
+  ar.take<float>(size_t(nchunk) * d_in);  // column partial sums
+  ar.take<float>(d_out);                  // row sums
+  ar.take<float>(d_in);                   // s (if caller passes no s_x)
+  ar.take<float>(d_out);                  // t
+  ar.take<float>(d_in);                   // W column factors
+  ar.take<float>(d_out);                  // W row factors
+  ar.take<float>(d_in);                   // H_X factors
+  ar.take<float>(d_out);                  // H_G factors
+  return ar.used;
+}
+
+kq_status biip_run(float* W, float* HX, float* D, float* HG, int64_t d_out, int64_t d_in,
+                   const int8_t* si, const int8_t* so, int64_t bi, int64_t bo, float* s_x,
+                   float* s_g, Arena& ws, hipStream_t s) {
+  const int64_t nchunk = std::min<int64_t>(64, d_out);
+  float* cpart = ws.take<float>(size_t(nchunk) * d_in);
+  float* rsum = ws.take<float>(d_out);
+  float* sx = s_x ? s_x : ws.take<float>(d_in);
+  float* sg = s_g ? s_g : ws.take<float>(d_out);
+  float* wcol = ws.take<float>(d_in);
+  float* wrow = ws.take<float>(d_out);
+  float* hxf = ws.take<float>(d_in);
+  float* hgf = ws.take<float>(d_out);
+  if (!cpart || !rsum || !sx || !sg || !wcol || !wrow || !hxf || !hgf)
+    return fail(KQ_ERR_WORKSPACE, "biip: workspace too small");
+
+  // squared norms of the unscaled W
+  row_sumsq_kernel<<<unsigned(cdiv(d_out, 4)), 256, 0, s>>>(W, d_out, d_in, rsum);
+  KQ_HIP(hipGetLastError());
+  const int64_t rpc = cdiv(d_out, nchunk);
+  col_sumsq_kernel<<<dim3(unsigned(cdiv(d_in, 1024)), unsigned(nchunk)), 256, 0, s>>>(W, d_out, d_in,
+                                                                                      rpc, cpart);
+  KQ_HIP(hipGetLastError());
+  scales_kernel<<<unsigned(cdiv(d_in, 256)), 256, 0, s>>>(HX, d_in, nullptr, cpart, int(nchunk), si,
+                                                          sx, wcol, hxf);
+  KQ_HIP(hipGetLastError());
+  scales_kernel<<<unsigned(cdiv(d_out, 256)), 256, 0, s>>>(HG, d_out, rsum, nullptr, 0, so, sg, wrow,
+                                                           hgf);
+  KQ_HIP(hipGetLastError());
+
+  const float gw = float(1.0 / std::sqrt(double(bi) * double(bo)));
+  KQ_TRY(fwht_rows(W, d_out, d_in, bi, wrow, wcol, gw, s));
+  KQ_TRY(fwht_cols(W, d_out, d_in, bo, s));
+  KQ_TRY(fwht_rows(HX, d_in, d_in, bi, hxf, hxf, float(1.0 / double(bi)), s));
+  KQ_TRY(fwht_cols(HX, d_in, d_in, bi, s));
+  if (D) {
+    KQ_TRY(fwht_rows(D, d_in, d_in, bi, hxf, hxf, float(1.0 / double(bi)), s));
+    KQ_TRY(fwht_cols(D, d_in, d_in, bi, s));
+  }
+  KQ_TRY(fwht_rows(HG, d_out, d_out, bo, hgf, hgf, float(1.0 / double(bo)), s));
+  KQ_TRY(fwht_cols(HG, d_out, d_out, bo, s));
+  return KQ_OK;
+}
+
+kq_status diag_sum(const float* H, int64_t n, double* out_dev, hipStream_t s) {
+  diag_sum_kernel<<<1, 256, 0, s>>>(H, n, out_dev);
+  KQ_HIP(hipGetLastError());
+  return KQ_OK;
+}
+
+}  // namespace kq

@@ -1,0 +1,95 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+validates arguments on the host before any launch, and its host-only
+allocator matches the oracle. No compute call reaches a GPU here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import layer_specs
+
+kqn = pytest.importorskip("post_weight_quantization_amd._native")
+N = kqn
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "kq.h")).read()
+    declared = set(re.findall(r"^\s*(?:kq_status|const char\*)\s+(kq_\w+)\s*\(", hdr, re.M))
+    assert declared == set(N.EXPORTS)
+    for name in declared:
+        assert hasattr(N.lib, name), name
+    assert N.lib.kq_version().startswith(b"kq")
+
+
+def _err(status):
+    return status, N.lib.kq_last_error().decode()
+
+
+def test_null_and_shape_validation():
+    cfg = N.kq_quant_cfg(2, 0, 128, 0)
+    st, msg = _err(N.lib.kq_gptaq_quantize(None, None, None, 4, 128, ctypes.byref(cfg), None, None,
+                                           None, None, 0, None))
+    assert st == N.KQ_ERR_ARG and "NULL" in msg
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+    st, msg = _err(N.lib.kq_gptaq_quantize(fake, fake, None, 4, 100, ctypes.byref(cfg), fake, fake,
+                                           fake, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_SHAPE and "128" in msg
+    bad = N.kq_quant_cfg(2, 64, 128, 0)
+    st, _ = _err(N.lib.kq_gptaq_quantize(fake, fake, None, 4, 128, ctypes.byref(bad), fake, fake,
+                                         fake, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_UNSUPPORTED
+    st, _ = _err(N.lib.kq_cholesky_inv(fake, 100, 0.01, ctypes.c_void_p(0x20000), None, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_SHAPE
+    st, _ = _err(N.lib.kq_cholesky_inv(fake, 128, 0.01, fake, None, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_ARG  # aliasing
+    st, _ = _err(N.lib.kq_cholesky_inv(fake, 128, float("nan"), ctypes.c_void_p(0x20000), None, fake,
+                                       1 << 30, None))
+    assert st == N.KQ_ERR_ARG
+    st, msg = _err(N.lib.kq_biip(fake, fake, None, fake, 96, 128, fake, fake, 0, 48, None, None,
+                                 fake, 1 << 30, None))
+    assert st == N.KQ_ERR_SHAPE and "power of two" in msg
+    st, _ = _err(N.lib.kq_biip(fake, fake, None, fake, 16384, 128, fake, fake, 0, 0, None, None,
+                               fake, 1 << 30, None))
+    assert st == N.KQ_ERR_UNSUPPORTED
+    st, _ = _err(N.lib.kq_accumulate_cov(fake, fake, fake, 7, 64, 256, 256, 1.0, 0.0, fake, fake,
+                                         fake, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_ARG
+    st, _ = _err(N.lib.kq_accumulate_cov(None, fake, None, N.KQ_BF16, 64, 256, 256, 1.0, 0.0, None,
+                                         fake, None, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_ARG  # D needs X
+    st, _ = _err(N.lib.kq_accumulate_cov(fake, fake, fake, N.KQ_BF16, 64, 250, 256, 1.0, 0.0, fake,
+                                         fake, fake, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_SHAPE
+
+
+def test_workspace_checked_before_launch():
+    fake = ctypes.c_void_p(0x10000)
+    cfg = N.kq_quant_cfg(2, 0, 128, 0)
+    need = ctypes.c_size_t()
+    assert N.lib.kq_workspace_size(N.KQ_OP_GPTAQ_QUANTIZE, 256, 512, 0, 0, ctypes.byref(cfg),
+                                   ctypes.byref(need)) == 0
+    assert need.value >= 256 * 512 * 4 + 2 * 512 * 512 * 4
+    st, msg = _err(N.lib.kq_gptaq_quantize(fake, fake, fake, 256, 512, ctypes.byref(cfg), fake, fake,
+                                           fake, fake, need.value - 1, None))
+    assert st == N.KQ_ERR_WORKSPACE and str(need.value) in msg
+    for op in range(7):
+        assert N.lib.kq_workspace_size(op, 1024, 4096, 8192, 0, ctypes.byref(cfg), ctypes.byref(need)) == 0
+    assert N.lib.kq_workspace_size(99, 1, 1, 1, 0, None, ctypes.byref(need)) == N.KQ_ERR_ARG
+
+
+def test_allocate_bits_matches_oracle():
+    api = pytest.importorskip("post_weight_quantization_amd.api")
+    rng = np.random.default_rng(0)
+    n = [sp.n_params for sp in layer_specs(4)]
+    for trial in range(200):
+        s = list(rng.lognormal(0, 2, 7))
+        if trial % 7 == 0:
+            s[3] = s[0]
+        avg = float(rng.uniform(2.0, 4.0))
+        assert api.kq_allocate_bits(s, n, (2, 3, 4), avg) == oracle.allocate_bits(s, n, (2, 3, 4), avg)
+    with pytest.raises(N.KQError):
+        api.kq_allocate_bits([1.0], [10], (2, 3, 4), 1.5)
