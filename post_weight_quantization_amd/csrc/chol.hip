@@ -11,12 +11,13 @@
 //   1. writes A = J (H + delta I) J (lower triangle) into U's buffer, with
 //      delta = damp * mean(diag H) computed on the device;
 //   2. factors A = L L^T in place, right-looking with 128-column blocks: a
-//      single-workgroup leaf factors the diagonal block and inverts it, the
-//      panel below is solved as a GEMM with that inverse, and the trailing
-//      lower triangle takes a rank-128 MFMA update;
-//   3. inverts L in place by recursive halving
-//      inv([[A,0],[B,C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]], whose two
-//      GEMMs per level are triangle-aware fp32 MFMA products;
+//      single-workgroup leaf factors the diagonal block (32-column panels,
+//      each by one wave with rows in registers) and inverts it, the panel
+//      below is solved as a GEMM with that inverse, and the trailing lower
+//      triangle takes a rank-128 MFMA update;
+//   3. inverts L in place by bottom-up doubling with
+//      inv([[A,0],[B,C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]]: every level
+//      is two batched, triangle-aware fp32 MFMA GEMMs;
 //   4. reverses indices in place to obtain U (upper, zeros below).
 // A non-positive (or NaN) pivot is reported through `info`.
 #include "kq_internal.h"
@@ -28,7 +29,6 @@ namespace kq {
 namespace {
 
 constexpr int NB = 128;
-constexpr int LP = NB + 1;  // padded LDS row
 
 // A[i][j] = H[n-1-i][n-1-j] + delta [i == j] for i >= j (reads H's upper triangle)
 __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, const double* dsum,
@@ -43,125 +43,217 @@ __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, cons
   }
 }
 
-// Factor the NB x NB diagonal block at (k0, k0) of A (ld n) in place and
-// write its inverse to Dinv (NB x NB, zeros above the diagonal).
-// Thread (bi, bj) = (t / 16, t % 16) keeps the 8 x 8 sub-block (bi, bj) in
-// registers; column j is published through LDS each step.
+// ---------------------------------------------------------------- the leaf
+// Factor the NB x NB diagonal block at (k0, k0) of A (ld n) in place (lower,
+// zeros written above the diagonal) and write its inverse to Dinv (NB x NB,
+// zeros above the diagonal). One workgroup of 4 waves; the block lives in LDS.
+//  * four 32-column panels; panel p is factored by wave 0 alone with rows
+//    lane and lane+64 in registers (column j is published to the other lanes
+//    through LDS, so no workgroup barrier sits inside the 32 column steps);
+//  * the rank-32 update of the trailing lower triangle runs on all 256
+//    threads with 4 x 4 register blocks;
+//  * the four 32 x 32 diagonal inverses are formed in parallel (one wave
+//    each, one column per lane by forward substitution), then the off-
+//    diagonal blocks X_ip = -X_ii sum_k L_ik X_kp, block row by block row.
+constexpr int LS = NB + 4;  // LDS row stride (floats), keeps float4 alignment
+
+__device__ inline float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ inline void wave_lds_fence() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ void leaf_panel(float* As, float* colbuf, int64_t k0, int* info, int P) {
+  const int C0 = 32 * P;
+  const int CS = C0 >> 6, CL = C0 & 63;  // register set / first lane of the diagonal block rows
+  const int lane = threadIdx.x & 63;
+  float ra[32], rb[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    ra[k] = As[lane * LS + C0 + k];
+    rb[k] = As[(lane + 64) * LS + C0 + k];
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int R = C0 + j;  // pivot row (compile-time after unrolling)
+    float piv = lane_value((R >> 6) ? rb[j] : ra[j], R & 63);
+    if (!(piv > 0.f)) {  // non-positive or NaN pivot
+      if (lane == 0) atomicMin(info, int(k0 + R) + 1);
+      piv = 1.f;
+    }
+    const float d = __builtin_amdgcn_sqrtf(piv);  // 1-ulp hardware square root
+    const float rinv = __builtin_amdgcn_rcpf(d);
+    ra[j] = lane > R ? ra[j] * rinv : (lane == R ? d : ra[j]);
+    rb[j] = lane + 64 > R ? rb[j] * rinv : (lane + 64 == R ? d : rb[j]);
+    // column j of the diagonal block, below the pivot, to every lane
+    const int kk = lane - CL;
+    if (kk >= 0 && kk < 32) colbuf[kk] = kk > j ? (CS ? rb[j] : ra[j]) : 0.f;
+    wave_lds_fence();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (4 * q + 3 <= j) continue;  // every column of this chunk is finished
+      const float4 v = *reinterpret_cast<const float4*>(colbuf + 4 * q);
+      const float cv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = 4 * q + u;
+        if (k <= j) continue;
+        ra[k] -= ra[j] * cv[u];
+        rb[k] -= rb[j] * cv[u];
+      }
+    }
+    wave_lds_fence();
+  }
+  // write back rows >= C0; zeros above the diagonal inside the diagonal block
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    if (lane >= C0) As[lane * LS + C0 + k] = (lane - C0 < k) ? 0.f : ra[k];
+    if (lane + 64 >= C0) As[(lane + 64) * LS + C0 + k] = (lane + 64 - C0 < k) ? 0.f : rb[k];
+  }
+}
+
+// As[r][c] -= sum_k As[r][c0+k] As[c][c0+k] (k < 32) for r >= c >= r0 (lower part only)
+__device__ void leaf_syrk(float* As, int c0, int r0) {
+  const int m4 = (NB - r0) / 4;
+  const int nblk = m4 * (m4 + 1) / 2;
+  for (int b = threadIdx.x; b < nblk; b += 256) {
+    int bi = int((sqrtf(8.f * float(b) + 1.f) - 1.f) * 0.5f);
+    while ((bi + 1) * (bi + 2) / 2 <= b) ++bi;
+    while (bi * (bi + 1) / 2 > b) --bi;
+    const int bj = b - bi * (bi + 1) / 2;
+    const int r = r0 + 4 * bi, c = r0 + 4 * bj;
+    float acc[4][4] = {};
+#pragma unroll
+    for (int k = 0; k < 32; k += 4) {
+      float4 x[4], y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = *reinterpret_cast<const float4*>(As + (r + u) * LS + c0 + k);
+        y[u] = *reinterpret_cast<const float4*>(As + (c + u) * LS + c0 + k);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc[u][v] += x[u].x * y[v].x + x[u].y * y[v].y + x[u].z * y[v].z + x[u].w * y[v].w;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) As[(r + u) * LS + c + v] -= acc[u][v];
+  }
+}
+
+// C(32 x 32) = alpha * A(32 x K) B(K x 32), all in LDS (ld LS); 2 x 2 outputs per thread.
+__device__ void leaf_mm32(const float* A, const float* B, float* C, int K, float alpha) {
+  const int t = threadIdx.x;
+  const int r = 2 * (t >> 4), c = 2 * (t & 15);
+  float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
+  for (int k = 0; k < K; k += 4) {
+    const float4 x0 = *reinterpret_cast<const float4*>(A + r * LS + k);
+    const float4 x1 = *reinterpret_cast<const float4*>(A + (r + 1) * LS + k);
+    const float xs0[4] = {x0.x, x0.y, x0.z, x0.w};
+    const float xs1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float2 y = *reinterpret_cast<const float2*>(B + (k + u) * LS + c);
+      a00 += xs0[u] * y.x;
+      a01 += xs0[u] * y.y;
+      a10 += xs1[u] * y.x;
+      a11 += xs1[u] * y.y;
+    }
+  }
+  C[r * LS + c] = alpha * a00;
+  C[r * LS + c + 1] = alpha * a01;
+  C[(r + 1) * LS + c] = alpha * a10;
+  C[(r + 1) * LS + c + 1] = alpha * a11;
+}
+
 __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t k0, float* Dinv,
                                                    int* info) {
-  __shared__ float colbuf[NB];
-  __shared__ float piv[1];
-  __shared__ float Ls[NB * LP];
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  float* As = sm;                    // NB x LS: the block, then L
+  float* Xs = sm + NB * LS;          // NB x LS: the inverse
+  float* Ts = Xs + NB * LS;          // 32 x LS: temporary block
+  float* colbuf = Ts + 32 * LS;      // 32
   const int t = threadIdx.x;
-  const int bi = t >> 4, bj = t & 15;
-  const bool act = bi >= bj;
-  float a[8][8];
+  const int w = t >> 6;
   float* base = A + k0 * n + k0;
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) a[r][c] = act ? base[(8 * bi + r) * n + 8 * bj + c] : 0.f;
-  if (t < NB) colbuf[t] = 0.f;
-  __syncthreads();
-
-  // ---- Cholesky: A = L L^T
-  for (int jb = 0; jb < 16; ++jb) {
-#pragma unroll
-    for (int jc = 0; jc < 8; ++jc) {
-      const int j = 8 * jb + jc;
-      if (bi == jb && bj == jb) {
-        float p = a[jc][jc];
-        if (!(p > 0.f)) {  // non-positive or NaN pivot
-          atomicMin(info, int(k0 + j) + 1);
-          p = 1.f;
-        }
-        const float d = sqrtf(p);
-        a[jc][jc] = d;
-        piv[0] = 1.f / d;
-      }
-      __syncthreads();
-      if (bj == jb && act) {
-        const float rinv = piv[0];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const bool below = (bi > jb) || (r > jc);
-          if (below) a[r][jc] *= rinv;
-          colbuf[8 * bi + r] = below ? a[r][jc] : 0.f;
-        }
-      }
-      __syncthreads();
-      if (act && (8 * bi + 7 > j) && (8 * bj + 7 > j)) {
-        float cr[8], cc[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) cr[r] = colbuf[8 * bi + r];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) cc[c] = colbuf[8 * bj + c];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) a[r][c] -= cr[r] * cc[c];
-      }
-    }
+  for (int e = t; e < NB * NB / 4; e += 256) {
+    const int r = e >> 5, c = (e & 31) * 4;
+    *reinterpret_cast<float4*>(As + r * LS + c) = *reinterpret_cast<const float4*>(base + r * n + c);
   }
-  // write L (zeros above the diagonal) to A and to LDS
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int row = 8 * bi + r, col = 8 * bj + c;
-      const float v = (act && col <= row) ? a[r][c] : 0.f;
-      if (act) base[row * n + col] = v;
-      Ls[row * LP + col] = v;
-    }
+  for (int e = t; e < NB * LS; e += 256) Xs[e] = 0.f;
   __syncthreads();
 
-  // ---- inverse: X = L^-1 by forward elimination on B = I, row j final at step j
-  float bm[8][8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) bm[r][c] = (bi == bj && r == c) ? 1.f : 0.f;
-  __shared__ float rowbuf[NB];
-  if (t < NB) rowbuf[t] = 0.f;
-  __syncthreads();
-  for (int jb = 0; jb < 16; ++jb) {
-#pragma unroll
-    for (int jc = 0; jc < 8; ++jc) {
-      const int j = 8 * jb + jc;
-      if (bi == jb && act) {
-        const float dinv = 1.f / Ls[j * LP + j];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          bm[jc][c] *= dinv;
-          rowbuf[8 * bj + c] = bm[jc][c];
-        }
-      }
-      __syncthreads();
-      if (act && 8 * bi + 7 > j) {
-        float cr[8], cc[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int row = 8 * bi + r;
-          cr[r] = row > j ? Ls[row * LP + j] : 0.f;
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) cc[c] = rowbuf[8 * bj + c];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) bm[r][c] -= cr[r] * cc[c];
-      }
+  // ---- Cholesky, four panels
+#pragma unroll 1
+  for (int p = 0; p < 4; ++p) {
+    if (w == 0) leaf_panel(As, colbuf, k0, info, p);
+    __syncthreads();
+    if (p < 3) {
+      leaf_syrk(As, 32 * p, 32 * p + 32);
       __syncthreads();
     }
   }
+
+  // ---- diagonal 32 x 32 inverses: wave w inverts block w, lane c < 32 owns column c
+  {
+    const int lane = t & 63;
+    const int b0 = 32 * w;
+    if (lane < 32) {
+      const int c = lane;
+      float x[32];
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
+      for (int i = 0; i < 32; ++i) {
+        float s = (i == c) ? 1.f : 0.f;
+        const float* Li = As + (b0 + i) * LS + b0;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int row = 8 * bi + r, col = 8 * bj + c;
-      Dinv[row * NB + col] = (act && col <= row) ? bm[r][c] : 0.f;
+        for (int k4 = 0; k4 < i; k4 += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(Li + k4);
+          s -= v.x * x[k4];
+          if (k4 + 1 < i) s -= v.y * x[k4 + 1];
+          if (k4 + 2 < i) s -= v.z * x[k4 + 2];
+          if (k4 + 3 < i) s -= v.w * x[k4 + 3];
+        }
+        x[i] = s / Li[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) Xs[(b0 + i) * LS + b0 + c] = x[i];
     }
+  }
+  __syncthreads();
+
+  // ---- off-diagonal blocks: X_ip = -X_ii sum_{k=p}^{i-1} L_ik X_kp
+  for (int i = 1; i < 4; ++i) {
+    for (int p = i - 1; p >= 0; --p) {
+      // Ts = L[i, p:i] X[p:i, p]
+      leaf_mm32(As + (32 * i) * LS + 32 * p, Xs + (32 * p) * LS + 32 * p, Ts, 32 * (i - p), 1.f);
+      __syncthreads();
+      leaf_mm32(Xs + (32 * i) * LS + 32 * i, Ts, Xs + (32 * i) * LS + 32 * p, 32, -1.f);
+      __syncthreads();
+    }
+  }
+
+  // ---- write L (lower, zeros above) and its inverse
+  for (int e = t; e < NB * NB / 4; e += 256) {
+    const int r = e >> 5, c = (e & 31) * 4;
+    const float4 l = *reinterpret_cast<const float4*>(As + r * LS + c);
+    const float4 x = *reinterpret_cast<const float4*>(Xs + r * LS + c);
+    // zero the strictly upper part (columns c..c+3 against row r)
+    const float4 lo = make_float4(c > r ? 0.f : l.x, c + 1 > r ? 0.f : l.y, c + 2 > r ? 0.f : l.z,
+                                  c + 3 > r ? 0.f : l.w);
+    const float4 xo = make_float4(c > r ? 0.f : x.x, c + 1 > r ? 0.f : x.y, c + 2 > r ? 0.f : x.z,
+                                  c + 3 > r ? 0.f : x.w);
+    *reinterpret_cast<float4*>(base + r * n + c) = lo;
+    *reinterpret_cast<float4*>(Dinv + r * NB + c) = xo;
+  }
 }
+
+constexpr size_t LEAF_LDS = sizeof(float) * (size_t(NB) * LS * 2 + 32 * LS + 32);
 
 // Copy the inverted diagonal blocks into place (block b at (b*NB, b*NB)).
 __global__ void place_diag_kernel(const float* __restrict__ Dinv, int64_t nblk, float* A,
@@ -195,23 +287,45 @@ __global__ void reverse_out_kernel(float* A, int64_t n) {
 
 __global__ void set_int_kernel(int* p, int v) { *p = v; }
 
-// L (ld n) holds inverted diagonal blocks; invert the block range [b0, b0+nb).
-kq_status trtri_rec(float* L, int64_t n, int64_t b0, int64_t nb, float* T, hipStream_t s) {
-  if (nb <= 1) return KQ_OK;
-  const int64_t n1 = (nb + 1) / 2, n2 = nb - n1;
-  KQ_TRY(trtri_rec(L, n, b0, n1, T, s));
-  KQ_TRY(trtri_rec(L, n, b0 + n1, n2, T, s));
-  const int64_t r1 = b0 * NB, r2 = (b0 + n1) * NB;
-  const int64_t m1 = n1 * NB, m2 = n2 * NB;
-  float* X11 = L + r1 * n + r1;
-  float* L21 = L + r2 * n + r1;
-  float* X22 = L + r2 * n + r2;
-  // T = L21 X11   (X11 lower: op(B)[k][c] = 0 for k < c)
-  GemmArgs g1 = gemm_args(L21, n, X11, n, T, m1, m2, m1, m1, 1.f, 0.f, G_B_LOWER);
-  KQ_TRY(gemm_f32(g1, s));
-  // X21 = -X22 T  (X22 lower: op(A)[r][k] = 0 for k > r)
-  GemmArgs g2 = gemm_args(X22, n, T, m1, L21, n, m2, m1, m2, -1.f, 0.f, G_A_LOWER);
-  KQ_TRY(gemm_f32(g2, s));
+// Invert the lower-triangular L (ld n) in place, its NB x NB diagonal blocks
+// already inverted: bottom-up doubling. Before the level of size sz, every
+// aligned block [k sz, (k+1) sz) and the trailing block [floor(n/sz) sz, n)
+// are inverted; adjacent pairs (A, C) are merged with
+//   X21 = -X22 (L21 X11),
+// all equal-size pairs of a level in one batched GEMM each.
+kq_status trtri_levels(float* L, int64_t n, float* T, hipStream_t s) {
+  for (int64_t sz = NB; sz < n; sz *= 2) {
+    const int64_t pair = 2 * sz;
+    const int64_t nfull = n / pair;
+    if (nfull > 0) {
+      GemmArgs g1 = gemm_args(L + sz * n, n, L, n, T, sz, sz, sz, sz, 1.f, 0.f, G_B_LOWER);
+      g1.batch = int(nfull);
+      g1.strideA = pair * n + pair;
+      g1.strideB = pair * n + pair;
+      g1.strideC = sz * sz;
+      KQ_TRY(gemm_f32(g1, s));
+      GemmArgs g2 = gemm_args(L + sz * n + sz, n, T, sz, L + sz * n, n, sz, sz, sz, -1.f, 0.f,
+                              G_A_LOWER | G_ORDER_MDESC);
+      g2.Cin = nullptr;
+      g2.batch = int(nfull);
+      g2.strideA = pair * (n + 1);
+      g2.strideB = sz * sz;
+      g2.strideC = pair * (n + 1);
+      KQ_TRY(gemm_f32(g2, s));
+    }
+    const int64_t r = nfull * pair;
+    const int64_t rest = n - r;
+    if (rest > sz) {
+      const int64_t s2 = rest - sz;
+      float* X11 = L + r * n + r;
+      float* L21 = L + (r + sz) * n + r;
+      float* X22 = L + (r + sz) * n + r + sz;
+      KQ_TRY(gemm_f32(gemm_args(L21, n, X11, n, T, sz, s2, sz, sz, 1.f, 0.f, G_B_LOWER), s));
+      GemmArgs g2 = gemm_args(X22, n, T, sz, L21, n, s2, sz, s2, -1.f, 0.f, G_A_LOWER | G_ORDER_MDESC);
+      g2.Cin = nullptr;
+      KQ_TRY(gemm_f32(g2, s));
+    }
+  }
   return KQ_OK;
 }
 
@@ -220,9 +334,7 @@ kq_status trtri_rec(float* L, int64_t n, int64_t b0, int64_t nb, float* T, hipSt
 size_t chol_ws_bytes(int64_t n) {
   Arena ar{nullptr, 0, 0};
   ar.take<float>(size_t(n) * NB);               // inverted diagonal blocks
-  const int64_t nb = cdiv(n, NB);
-  const int64_t n1 = (nb + 1) / 2;
-  ar.take<float>(size_t(n1 * NB) * (nb - n1) * NB + 4);  // recursion temporary
+  ar.take<float>(size_t(n) * n / 4 + 4);        // triangular-inverse temporary
   ar.take<double>(1);
   ar.take<int>(1);
   return ar.used;
@@ -232,8 +344,7 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
                        Arena& ws, hipStream_t s) {
   const int64_t nb = n / NB;
   float* Dinv = ws.take<float>(size_t(n) * NB);
-  const int64_t n1 = (nb + 1) / 2;
-  float* T = ws.take<float>(size_t(n1 * NB) * (nb - n1) * NB + 4);
+  float* T = ws.take<float>(size_t(n) * n / 4 + 4);
   double* dsum = ws.take<double>(1);
   int* dinfo = ws.take<int>(1);
   if (!Dinv || !T || !dsum || !dinfo) return fail(KQ_ERR_WORKSPACE, "cholesky_inv: workspace too small");
@@ -244,10 +355,12 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
   reverse_damp_kernel<<<dim3(unsigned(cdiv(n, 256)), unsigned(n)), 256, 0, s>>>(H, n, dsum, damp, U);
   KQ_HIP(hipGetLastError());
 
+  KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(leaf_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(LEAF_LDS)));
   float* A = U;
   for (int64_t k = 0; k < nb; ++k) {
     const int64_t k0 = k * NB;
-    leaf_kernel<<<1, 256, 0, s>>>(A, n, k0, Dinv + k * NB * NB, dinfo);
+    leaf_kernel<<<1, 256, LEAF_LDS, s>>>(A, n, k0, Dinv + k * NB * NB, dinfo);
     KQ_HIP(hipGetLastError());
     const int64_t m = n - k0 - NB;
     if (m <= 0) break;
@@ -264,7 +377,7 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
   // invert L in place
   place_diag_kernel<<<dim3(NB, unsigned(nb)), NB, 0, s>>>(Dinv, nb, A, n);
   KQ_HIP(hipGetLastError());
-  KQ_TRY(trtri_rec(A, n, 0, nb, T, s));
+  KQ_TRY(trtri_levels(A, n, T, s));
   reverse_out_kernel<<<dim3(unsigned(cdiv(n, 256)), unsigned(n)), 256, 0, s>>>(A, n);
   KQ_HIP(hipGetLastError());
 

@@ -39,9 +39,34 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   const float* __restrict__ B = g.B + z * g.strideB;
   float* C = g.C + z * g.strideC;
   const float* Cin = g.Cin ? g.Cin + z * g.strideC : nullptr;
-  const int64_t m0 = int64_t(blockIdx.y) * TM;
-  const int64_t n0 = int64_t(blockIdx.x) * TN;
   const uint32_t fl = g.flags;
+  // tile coordinates: dispatch order is blockIdx.x fastest; optionally remap so
+  // that the tiles with the longest K range start first
+  const int ntn = gridDim.x, ntm = gridDim.y;
+  int tn = blockIdx.x, tm = blockIdx.y;
+  if (fl & (G_ORDER_NDESC | G_ORDER_MDESC | G_ORDER_DIAG)) {
+    const int lin = blockIdx.y * ntn + blockIdx.x;
+    if (fl & G_ORDER_NDESC) {
+      tn = ntn - 1 - lin / ntm;
+      tm = lin % ntm;
+    } else if (fl & G_ORDER_MDESC) {
+      tm = ntm - 1 - lin / ntn;
+      tn = lin % ntn;
+    } else {
+      // diagonals e = tn - tm from ntn - 1 down to -(ntm - 1)
+      int rem = lin;
+      int e = ntn - 1;
+      for (;; --e) {
+        const int len = min(ntn - max(e, 0), ntm - max(-e, 0));
+        if (rem < len) break;
+        rem -= len;
+      }
+      tm = max(-e, 0) + rem;
+      tn = tm + e;
+    }
+  }
+  const int64_t m0 = int64_t(tm) * TM;
+  const int64_t n0 = int64_t(tn) * TN;
 
   // skip tiles outside the written triangle
   if ((fl & G_OUT_LOWER) && n0 > m0 + TM - 1) return;

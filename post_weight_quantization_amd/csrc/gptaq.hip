@@ -167,7 +167,8 @@ kq_status formp_run(const float* D, const float* U, int64_t n, float* P, Arena& 
   GemmArgs g1 = gemm_args(D, n, U, n, T, n, n, n, n, 1.f, 0.f, G_TRANS_B | G_B_LOWER | G_OUT_SUPPER);
   KQ_TRY(gemm_f32(g1, s));
   KQ_TRY(fill_f32(P, n * n, 0.f, s));
-  GemmArgs g2 = gemm_args(T, n, U, n, P, n, n, n, n, 1.f, 0.f, G_A_SUPPER | G_B_UPPER | G_OUT_SUPPER);
+  GemmArgs g2 = gemm_args(T, n, U, n, P, n, n, n, n, 1.f, 0.f,
+                          G_A_SUPPER | G_B_UPPER | G_OUT_SUPPER | G_ORDER_DIAG);
   KQ_TRY(gemm_f32(g2, s));
   return KQ_OK;
 }
@@ -203,7 +204,7 @@ kq_status gptaq_run(float* W, const float* U, const float* D, int64_t d_out, int
     if (!P) return fail(KQ_ERR_WORKSPACE, "gptaq_quantize: workspace too small");
     KQ_TRY(formp_run(D, U, n, P, ws, s));
     // W_bar = W0 + W0 P   (op(B) = P strictly upper: zero for k >= n)
-    GemmArgs gf = gemm_args(W, n, P, n, Wbar, n, d_out, n, n, 1.f, 1.f, G_B_UPPER);
+    GemmArgs gf = gemm_args(W, n, P, n, Wbar, n, d_out, n, n, 1.f, 1.f, G_B_UPPER | G_ORDER_NDESC);
     gf.Cin = W;
     KQ_TRY(gemm_f32(gf, s));
     if (group) {

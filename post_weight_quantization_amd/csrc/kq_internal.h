@@ -58,6 +58,10 @@ enum GemmFlag : uint32_t {
   G_OUT_UPPER = 1u << 7,    // write only n >= m
   G_OUT_SUPPER = 1u << 8,   // write only n > m
   G_A_SUPPER = 1u << 9,     // op(A)[m][k] = 0 for k <= m
+  // tile order (longest K range first when operands are triangular)
+  G_ORDER_NDESC = 1u << 12,  // column tiles in descending order
+  G_ORDER_MDESC = 1u << 13,  // row tiles in descending order
+  G_ORDER_DIAG = 1u << 14,   // by (column tile - row tile), descending
 };
 
 struct GemmArgs {

@@ -122,7 +122,7 @@ def test_sensitivity_exact_on_gpu_inputs():
 # ------------------------------------------------------------------ stage 3
 
 
-@pytest.mark.parametrize("n,cond", [(128, 1e2), (256, 1e3), (640, 1e4), (1024, 1e3)])
+@pytest.mark.parametrize("n,cond", [(128, 1e2), (256, 1e3), (384, 1e3), (640, 1e4), (896, 1e3), (1024, 1e3)])
 def test_cholesky_inv_backward_error(n, cond):
     rng = np.random.default_rng(n)
     H = spd(rng, n, cond).astype(np.float32)
