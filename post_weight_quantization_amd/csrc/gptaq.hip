@@ -16,11 +16,11 @@
 // in-group part of W0 P must not yet be present at that moment: the grid is
 // taken from W_bar - Z with Z = W0 blockdiag_128(P) (a batched GEMM).
 //
-// Per 128-column block: a panel kernel sweeps the block in registers
-// (16 lanes per row, 8 columns per lane; U's diagonal block sits in LDS,
-// permuted so each lane reads its 8 entries of row p as two 16-byte loads),
-// writes codes, W^ and the scaled errors E; then the lazy trailing update
-// W_bar[:, >blk] -= E U_{blk, >blk} runs as an fp32 MFMA GEMM.
+// Per 128-column block a panel kernel sweeps the block in registers (8 lanes
+// per row, 16 columns per lane, U's diagonal block in LDS) and writes codes,
+// W^ and the scaled errors E. The lazy update W_bar[:, >blk] -= E U_{blk,>blk}
+// runs as fp32 MFMA GEMMs, grouped in 512-column superblocks so the far part
+// of W_bar is read and written once per four panels.
 #include "kq_internal.h"
 
 namespace kq {
@@ -28,6 +28,7 @@ namespace kq {
 namespace {
 
 constexpr int BK = 128;  // block / group width
+constexpr int64_t SB = 512;  // superblock of the lazy trailing updates
 
 // Grid per output channel (fp32): lo = min(row, 0), hi = max(row, 0),
 // [-1, 1] for an all-zero row, scale = (hi - lo) / maxq, zero = rint(-lo / scale).
@@ -58,47 +59,96 @@ __global__ __launch_bounds__(256) void grid_rows_kernel(const float* W, int64_t 
   }
 }
 
-// The column sweep of one 128-column block.
-// Thread t: row r = blockIdx.x * 16 + t / 16, lane-in-row c = t % 16, holding
-// columns blk0 + 16 j + c (j = 0..7) of W_bar.
+// The column sweep of one 128-column block, for PR = 32 rows per workgroup.
+// Lane l of wave w: row row0 + 8 w + l / 8, position c = l % 8 in its group
+// of 8 lanes, holding columns blk0 + 16 c + j (j = 0..15) in registers. The
+// sweep runs an outer loop over the owning position c0 (not unrolled, which
+// keeps the code small enough for the instruction cache) and 16 unrolled
+// steps inside. Step p = 16 c0 + j0: every lane rounds its candidate w[j0];
+// the owner's scaled error reaches all 8 lanes of the row through a sum of
+// the masked errors with three DPP steps (quad_perm, quad_perm,
+// row_half_mirror), so the serial path has no LDS round trip; each lane then
+// applies it to its columns with U row p from LDS (diagonal and below stored
+// as zeros, each lane's 16 entries at a 20-float stride: conflict-free).
+constexpr int PR = 32;
+constexpr int USEG = 20;            // floats per lane segment of a staged U row
+constexpr int UROW = 8 * USEG;      // floats per staged U row
+
+__device__ inline float dpp_add(float v, int ctrl_sel) {
+  switch (ctrl_sel) {
+    case 0:  // quad_perm [1,0,3,2]
+      return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    case 1:  // quad_perm [2,3,0,1]
+      return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    default:  // row_half_mirror: lane i <-> 7 - i within each 8 lanes
+      return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  }
+}
+
+__device__ inline float group8_sum(float v) {
+  v = dpp_add(v, 0);
+  v = dpp_add(v, 1);
+  return dpp_add(v, 2);
+}
+
+constexpr size_t PANEL_LDS = sizeof(float) * (size_t(BK) * UROW + BK + 2 * PR * BK) + PR * BK;
+
 __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wbar,
                                                     const float* __restrict__ U,
                                                     const float* __restrict__ Z, float* Wout,
-                                                    uint8_t* codes, float* E, float* scale,
-                                                    float* zero, int64_t d_out, int64_t n,
-                                                    int64_t blk0, int ngroups, int grouped,
-                                                    float maxq) {
-  __shared__ float Us[BK * BK];  // Us[p][c][j] = U[blk0 + p][blk0 + 16 j + c]
-  __shared__ float uinv[BK];
+                                                    uint8_t* codes, float* E, int64_t ldE,
+                                                    float* scale, float* zero, int64_t d_out,
+                                                    int64_t n, int64_t blk0, int ngroups,
+                                                    int grouped, float maxq) {
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  float* Us = sm;                 // [p][c][j] = U[blk0 + p][blk0 + 16 c + j] if 16 c + j > p, else 0
+  float* uinv = Us + BK * UROW;   // 1 / U_pp
+  float* Wo = uinv + BK;          // PR x BK staged W^
+  float* Eo = Wo + PR * BK;       // PR x BK staged errors
+  uint8_t* Co = reinterpret_cast<uint8_t*>(Eo + PR * BK);  // PR x BK codes
   const int t = threadIdx.x;
-  // stage U's diagonal block (coalesced reads, permuted writes)
   for (int e = t; e < BK * BK; e += 256) {
     const int p = e >> 7, m = e & 127;
-    Us[p * BK + (m & 15) * 8 + (m >> 4)] = U[(blk0 + p) * n + blk0 + m];
+    const float v = m > p ? U[(blk0 + p) * n + blk0 + m] : 0.f;
+    Us[p * UROW + (m >> 4) * USEG + (m & 15)] = v;
   }
   if (t < BK) uinv[t] = 1.f / U[(blk0 + t) * n + blk0 + t];
 
-  const int c = t & 15;
-  const int64_t row = int64_t(blockIdx.x) * 16 + (t >> 4);
+  const int lane = t & 63;
+  const int c = lane & 7;
+  const int rloc = 8 * (t >> 6) + (lane >> 3);
+  const int64_t row = int64_t(blockIdx.x) * PR + rloc;
   const bool valid = row < d_out;
   const int64_t rr = valid ? row : d_out - 1;
-  float w[8];
+  const float* wsrc = Wbar + rr * n + blk0 + 16 * c;
+  float w[16], ev[16];
+  uint32_t cw[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = Wbar[rr * n + blk0 + 16 * j + c];
+  for (int j = 0; j < 16; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(wsrc + j);
+    w[j] = v.x;
+    w[j + 1] = v.y;
+    w[j + 2] = v.z;
+    w[j + 3] = v.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ev[j] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cw[k] = 0u;
 
   float sc, zr;
   if (grouped) {
     // grid of this group from the working values minus the in-group P terms
     float lo = 0.f, hi = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 16; ++j) {
       float v = w[j];
-      if (Z) v -= Z[rr * n + blk0 + 16 * j + c];
+      if (Z) v -= Z[rr * n + blk0 + 16 * c + j];
       lo = fminf(lo, v);
       hi = fmaxf(hi, v);
     }
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
+    for (int o = 1; o < 8; o <<= 1) {
       lo = fminf(lo, __shfl_xor(lo, o));
       hi = fmaxf(hi, __shfl_xor(hi, o));
     }
@@ -120,37 +170,72 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
   const float isc = 1.f / sc;
   __syncthreads();
 
-  float q_out[8], w_out[8], e_out[8];
-  const int base_lane = (threadIdx.x & 63) & ~15;
+  // U row p for this lane (16 entries) and 1 / U_pp, fetched one step ahead
+  auto fetch = [&](int p, float (&u)[16], float& ui) {
+    const float* up = Us + p * UROW + c * USEG;
 #pragma unroll
-  for (int p = 0; p < BK; ++p) {
-    const int j0 = p >> 4;
-    const int c0 = p & 15;
-    const float x = w[j0];
-    const float q = fminf(fmaxf(rintf(x * isc) + zr, 0.f), maxq);
-    const float wq = sc * (q - zr);
-    float e = (x - wq) * uinv[p];
-    e = __shfl(e, base_lane + c0, 64);
-    if (c == c0) {
-      q_out[j0] = q;
-      w_out[j0] = wq;
-      e_out[j0] = e;
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float4 v = *reinterpret_cast<const float4*>(up + 4 * k4);
+      u[4 * k4] = v.x;
+      u[4 * k4 + 1] = v.y;
+      u[4 * k4 + 2] = v.z;
+      u[4 * k4 + 3] = v.w;
     }
-    const float* up = Us + p * BK + c * 8;
+    ui = uinv[p];
+  };
+  float ua[16], ub[16], uia, uib;
+  fetch(0, ua, uia);
+#pragma unroll 1
+  for (int c0 = 0; c0 < 8; ++c0) {
+    const bool own = c == c0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (16 * j + 15 <= p) continue;  // every column of this register is finished
-      w[j] -= e * up[j];
+    for (int j0 = 0; j0 < 16; ++j0) {
+      const int p = 16 * c0 + j0;
+      float(&ucur)[16] = (j0 & 1) ? ub : ua;
+      float(&unxt)[16] = (j0 & 1) ? ua : ub;
+      const float ui = (j0 & 1) ? uib : uia;
+      float& uin = (j0 & 1) ? uia : uib;
+      if (p + 1 < BK) fetch(p + 1, unxt, uin);
+      const float x = w[j0];
+      const float q = fminf(fmaxf(rintf(x * isc) + zr, 0.f), maxq);
+      const float wq = sc * (q - zr);
+      const float el = (x - wq) * ui;
+      const float e = group8_sum(own ? el : 0.f);
+      w[j0] = own ? wq : w[j0];
+      ev[j0] = own ? el : ev[j0];
+      cw[j0 >> 2] |= own ? (uint32_t(q) << (8 * (j0 & 3))) : 0u;
+      // the next step's candidate first, then the rest of the row
+      if (j0 + 1 < 16) w[j0 + 1] -= e * ucur[j0 + 1];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j == j0 + 1) continue;
+        w[j] -= e * ucur[j];
+      }
     }
   }
-  if (valid) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t col = blk0 + 16 * j + c;
-      codes[row * n + col] = uint8_t(q_out[j]);
-      Wout[row * n + col] = w_out[j];
-      E[row * BK + 16 * j + c] = e_out[j];
-    }
+  for (int j = 0; j < 16; j += 4) {
+    *reinterpret_cast<float4*>(Wo + rloc * BK + 16 * c + j) = make_float4(w[j], w[j + 1], w[j + 2], w[j + 3]);
+    *reinterpret_cast<float4*>(Eo + rloc * BK + 16 * c + j) =
+        make_float4(ev[j], ev[j + 1], ev[j + 2], ev[j + 3]);
+  }
+  *reinterpret_cast<uint4*>(Co + rloc * BK + 16 * c) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+  __syncthreads();
+  const int64_t rows_here = min<int64_t>(PR, d_out - int64_t(blockIdx.x) * PR);
+  for (int e = t; e < PR * BK / 4; e += 256) {
+    const int r = e >> 5, col = (e & 31) * 4;
+    if (r >= rows_here) continue;
+    const int64_t grow = int64_t(blockIdx.x) * PR + r;
+    *reinterpret_cast<float4*>(Wout + grow * n + blk0 + col) =
+        *reinterpret_cast<const float4*>(Wo + r * BK + col);
+    *reinterpret_cast<float4*>(E + grow * ldE + col) = *reinterpret_cast<const float4*>(Eo + r * BK + col);
+  }
+  for (int e = t; e < PR * BK / 16; e += 256) {
+    const int r = e >> 3, col = (e & 7) * 16;
+    if (r >= rows_here) continue;
+    const int64_t grow = int64_t(blockIdx.x) * PR + r;
+    *reinterpret_cast<uint4*>(codes + grow * n + blk0 + col) =
+        *reinterpret_cast<const uint4*>(Co + r * BK + col);
   }
 }
 
@@ -177,7 +262,7 @@ size_t gptaq_ws_bytes(int64_t d_out, int64_t d_in, int group, bool has_d) {
   Arena ar{nullptr, 0, 0};
   const int64_t n = d_in;
   ar.take<float>(size_t(d_out) * n);  // W_bar
-  ar.take<float>(size_t(d_out) * BK); // E
+  ar.take<float>(size_t(d_out) * SB); // E (one superblock)
   if (has_d) {
     ar.take<float>(size_t(n) * n);    // P
     ar.take<float>(size_t(n) * n);    // T (inside form_p)
@@ -191,7 +276,7 @@ kq_status gptaq_run(float* W, const float* U, const float* D, int64_t d_out, int
   const int64_t n = d_in;
   const float maxq = float((1 << bits) - 1);
   float* Wbar = ws.take<float>(size_t(d_out) * n);
-  float* E = ws.take<float>(size_t(d_out) * BK);
+  float* E = ws.take<float>(size_t(d_out) * SB);
   if (!Wbar || !E) return fail(KQ_ERR_WORKSPACE, "gptaq_quantize: workspace too small");
   float* Z = nullptr;
 
@@ -223,18 +308,29 @@ kq_status gptaq_run(float* W, const float* U, const float* D, int64_t d_out, int
   }
 
   const int ngroups = group ? int(n / BK) : 1;
-  const int64_t nblk = n / BK;
-  for (int64_t b = 0; b < nblk; ++b) {
-    const int64_t blk0 = b * BK;
-    panel_kernel<<<unsigned(cdiv(d_out, 16)), 256, 0, s>>>(Wbar, U, Z, W, codes, E, scale, zero,
-                                                           d_out, n, blk0, ngroups, group ? 1 : 0,
-                                                           maxq);
-    KQ_HIP(hipGetLastError());
-    const int64_t rest = n - blk0 - BK;
-    if (rest > 0) {
-      // W_bar[:, blk0+BK:] -= E U[blk0:blk0+BK, blk0+BK:]
-      GemmArgs gt = gemm_args(E, BK, U + blk0 * n + blk0 + BK, n, Wbar + blk0 + BK, n, d_out, rest,
-                              BK, -1.f, 1.f, 0);
+  KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(panel_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(PANEL_LDS)));
+  // Lazy updates in superblocks of SB columns: after each panel only the rest
+  // of its superblock is updated (K = 128); the columns beyond the superblock
+  // take one update with K = SB once all its panels are done.
+  for (int64_t s0 = 0; s0 < n; s0 += SB) {
+    const int64_t s1 = std::min(s0 + SB, n);
+    for (int64_t b0 = s0; b0 < s1; b0 += BK) {
+      panel_kernel<<<unsigned(cdiv(d_out, PR)), 256, PANEL_LDS, s>>>(
+          Wbar, U, Z, W, codes, E + (b0 - s0), SB, scale, zero, d_out, n, b0, ngroups,
+          group ? 1 : 0, maxq);
+      KQ_HIP(hipGetLastError());
+      const int64_t near = s1 - b0 - BK;
+      if (near > 0) {
+        GemmArgs gt = gemm_args(E + (b0 - s0), SB, U + b0 * n + b0 + BK, n, Wbar + b0 + BK, n, d_out,
+                                near, BK, -1.f, 1.f, 0);
+        KQ_TRY(gemm_f32(gt, s));
+      }
+    }
+    const int64_t far = n - s1;
+    if (far > 0) {
+      GemmArgs gt = gemm_args(E, SB, U + s0 * n + s1, n, Wbar + s1, n, d_out, far, s1 - s0, -1.f,
+                              1.f, 0);
       KQ_TRY(gemm_f32(gt, s));
     }
   }
