@@ -6,14 +6,22 @@ sweep, for the LLaMA-2-7B q_proj workload (W 4096 x 4096, 131072 bf16
 calibration tokens, 2-bit per-channel grid, lazy block 128, 1% damping, full
 4096-point randomized Hadamard on both sides). The metric is milliseconds per
 layer (lower is better). Per-stage times come from HIP events recorded on the
-stream the kernels run on. The CPU baseline is the fp64 oracle timed on a
-bounded sample of the same workload on this host's cores.
+stream the kernels run on; the covariance kernel, the dominant one, is also
+timed alone through the library's event hook. The CPU baseline is the fp64
+oracle timed on a bounded sample of the same workload on this host's cores.
 
-    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--config 1] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload llama2-7b-q_proj]
+                    [--no-cpu] [--copy-calib MIB]
+
+--copy-calib runs one device-to-device copy of MIB mebibytes before the steps,
+so that a hardware-counter pass over the same command sees a kernel of known
+traffic next to the covariance kernel (the scaling factor for FETCH_SIZE and
+WRITE_SIZE).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +36,13 @@ if ROOT not in sys.path:
 PEAK_BF16 = 2.5e15      # dense MFMA, FLOP/s
 PEAK_FP32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12       # bytes/s
+
+# HBM traffic of one covariance-kernel launch on the LLaMA-2-7B q_proj
+# workload (4096 x 4096, 131072 bf16 tokens), from FETCH_SIZE and WRITE_SIZE
+# counter passes scaled by the same counters on a copy of known size. Valid
+# only for the kernel source it was measured on (sha256 of cov.hip).
+COV_TRAFFIC = {"cov_sha256": "af322c357f642f95eddf4622698ffeb00b7610f5650d2bde56c1493293c7f329",
+               "bytes": 22844305848}
 
 
 def stage_costs(spec):
@@ -74,11 +89,16 @@ def run_gpu(spec, steps, warmup, data):
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     names = ["cov", "biip", "sens", "chol", "gptaq"]
     stream = torch.cuda.current_stream()
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
 
-    def step(ev=None):
+    def step(ev=None, k=None):
         W.copy_(W0)
+        if k is not None:
+            kq.kq_set_kernel_events(N.KQ_OP_ACCUMULATE_COV, kev[k][0], kev[k][1], stream)
         if ev: ev[0].record(stream)
         kq.kq_accumulate_cov(X, Xq, G, 1.0 / spec.n_tok, 0.0, HX, D, HG, ws=ws)
+        if k is not None:
+            kq.kq_set_kernel_events(N.KQ_OP_ACCUMULATE_COV)
         if ev: ev[1].record(stream)
         kq.kq_biip(W, HX, D, HG, si, so, 0, 0, s_x, s_g, ws=ws)
         if ev: ev[2].record(stream)
@@ -94,13 +114,19 @@ def run_gpu(spec, steps, warmup, data):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    # create the hook's events before the timed region
+    for k in range(steps):
+        for e in kev[k]:
+            e.record(stream)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        sens = step(evs[k])
+        sens = step(evs[k], k)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage_ms = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
                 for i, nm in enumerate(names)}
+    cov_kernel_ms = float(np.mean([kev[k][0].elapsed_time(kev[k][1]) for k in range(steps)]))
     # quality check outside the timed region
     W0p = None
     obj = None
@@ -123,7 +149,20 @@ def run_gpu(spec, steps, warmup, data):
     except Exception as e:  # pragma: no cover - reporting only
         print(f"objective check failed: {e}", file=sys.stderr)
         obj_rtn = None
-    return dict(wall_s=wall, stage_ms=stage_ms, sens=sens, obj=obj, obj_rtn=obj_rtn)
+    return dict(wall_s=wall, stage_ms=stage_ms, cov_kernel_ms=cov_kernel_ms, sens=sens, obj=obj,
+                obj_rtn=obj_rtn)
+
+
+def copy_calibration(mib):
+    """One plain device-to-device copy of `mib` MiB (reads and writes that many bytes)."""
+    import torch
+
+    a = torch.ones(mib << 18, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
+    del a, b
 
 
 def cpu_baseline(spec, data, prefix):
@@ -164,8 +203,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--workload", default="llama2-7b-q_proj")
     ap.add_argument("--layer", type=int, default=0, help="sublayer index within the workload")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-prefix", type=int, default=4096)
     args = ap.parse_args()
@@ -174,22 +214,29 @@ def main():
               "(multi-GPU sharding is a design note, not built). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    from synth import layer_specs, make_layer
+    from synth import WORKLOADS, layer_specs, make_layer
 
-    spec = layer_specs(args.config)[args.layer]
+    spec = layer_specs(WORKLOADS[args.workload])[args.layer]
     t0 = time.perf_counter()
     data = make_layer(spec)
     print(f"[bench] generated {spec.name} {spec.d_out}x{spec.d_in}, N={spec.n_tok} "
           f"in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
     g = run_gpu(spec, args.steps, args.warmup, data)
     print(f"[bench] gpu stages (ms): {json.dumps(g['stage_ms'])}", file=sys.stderr, flush=True)
     costs = stage_costs(spec)
     ms = g["wall_s"] * 1e3 / args.steps
-    cov_ms = g["stage_ms"]["cov"]
+    cov_ms = g["cov_kernel_ms"]
     achieved = costs["cov_flops"] / (cov_ms * 1e-3)
-    roof = {"kernel": "cov_bf16_kernel (+ split reduction)", "bound": "mfma",
+    src = open(os.path.join(ROOT, "post_weight_quantization_amd", "csrc", "cov.hip"), "rb").read()
+    traffic = None
+    if (COV_TRAFFIC["cov_sha256"] == hashlib.sha256(src).hexdigest()
+            and (spec.d_out, spec.d_in, spec.n_tok) == (4096, 4096, 131072)):
+        traffic = COV_TRAFFIC["bytes"]
+    roof = {"kernel": "cov_bf16_kernel", "kernel_ms": round(cov_ms, 4), "bound": "mfma",
             "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16, 4), "traffic": None}
+            "frac": round(achieved / PEAK_BF16, 4), "traffic": traffic}
     st = g["stage_ms"]
     stages = {
         "cov_ms": round(st["cov"], 3),
@@ -214,7 +261,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{spec.name} {spec.d_out}x{spec.d_in} (config {spec.cfg})",
+        "config": {"workload": f"{args.workload}: {spec.name} W {spec.d_out}x{spec.d_in}, "
+                               f"{spec.n_tok} {spec.dtype} tokens, {spec.bits}-bit "
+                               f"{'per-channel' if not spec.group else f'group {spec.group}'}",
                    "d_out": spec.d_out, "d_in": spec.d_in, "n_tok": spec.n_tok,
                    "inputs": spec.dtype, "bits": spec.bits, "group": spec.group,
                    "block": spec.block, "damp": spec.damp},

@@ -81,6 +81,23 @@ const char* kq_last_error(void);
 /* Library version string. */
 const char* kq_version(void);
 
+/* Measurement hook; not part of the method and not needed to use it.
+ * After kq_set_kernel_events(op, start, stop), every later call of `op` made
+ * from this thread records `start` on its stream right before the op's main
+ * kernel is enqueued and `stop` right after, so the caller can time that one
+ * kernel with hipEventElapsedTime on the stream it actually ran on. This is
+ * the only state the library keeps between calls (per thread).
+ *   op     KQ_OP_ACCUMULATE_COV only: the main kernel is the covariance
+ *          kernel (bf16 inputs: the tile kernel that computes H_X, D and H_G
+ *          together; the drift pre-pass and the split reduction lie outside
+ *          the bracket). For fp32 inputs the bracket holds the three
+ *          products and the drift pass.
+ *   start, stop  events created by the caller (who owns and destroys them);
+ *          both NULL switches the hook off.
+ * Errors: KQ_ERR_UNSUPPORTED for other ops, KQ_ERR_ARG if exactly one event
+ * is NULL. */
+kq_status kq_set_kernel_events(kq_op op, hipEvent_t start, hipEvent_t stop);
+
 /* Bytes of scratch memory `op` needs for the given sizes (host output).
  * n_tok and dtype matter for KQ_OP_ACCUMULATE_COV only; cfg for
  * KQ_OP_GPTAQ_QUANTIZE only (may be NULL elsewhere). For square-matrix ops

@@ -15,5 +15,6 @@ from .api import (  # noqa: F401
     kq_gptaq_quantize,
     kq_layer_objective,
     kq_sensitivity,
+    kq_set_kernel_events,
     kq_workspace_size,
 )

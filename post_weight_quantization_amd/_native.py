@@ -22,7 +22,7 @@ KQ_BF16, KQ_F32 = 0, 1
 # every symbol include/kq.h declares
 EXPORTS = ("kq_last_error", "kq_version", "kq_workspace_size", "kq_accumulate_cov", "kq_biip",
            "kq_sensitivity", "kq_cholesky_inv", "kq_form_p", "kq_gptaq_quantize",
-           "kq_allocate_bits", "kq_layer_objective")
+           "kq_allocate_bits", "kq_layer_objective", "kq_set_kernel_events")
 
 
 class kq_quant_cfg(ctypes.Structure):
@@ -38,7 +38,7 @@ class KQError(RuntimeError):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m post_weight_quantization_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python post_weight_quantization_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -73,6 +73,9 @@ _sig("kq_allocate_bits", _st, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ct
      ctypes.POINTER(ctypes.c_int32))
 _sig("kq_layer_objective", _st, _p, _p, _p, _p, _p, _i64, _i64, ctypes.POINTER(ctypes.c_double),
      _p, _sz, _p)
+
+
+_sig("kq_set_kernel_events", _st, ctypes.c_int, _p, _p)
 
 
 def check(status: int, info: int = 0) -> None:

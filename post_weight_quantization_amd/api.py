@@ -167,3 +167,18 @@ def kq_layer_objective(W0, What, HX, D, HG, ws=None, stream=None) -> float:
     check(N.lib.kq_layer_objective(_ptr(W0), _ptr(What), _ptr(HX), _ptr(D), _ptr(HG), d_out, d_in,
                                    ctypes.byref(obj), _ptr(ws), ws.numel(), _stream(stream)))
     return obj.value
+
+
+def kq_set_kernel_events(op: int, start=None, stop=None, stream=None):
+    """Bracket the main kernel of later `op` calls on this thread with two
+    torch.cuda.Event objects (None, None switches the hook off). The events
+    are recorded once here first so that their HIP handles exist."""
+    if start is None and stop is None:
+        check(N.lib.kq_set_kernel_events(op, None, None))
+        return
+    s = stream or torch.cuda.current_stream()
+    for e in (start, stop):
+        if not e.cuda_event:
+            e.record(s)
+    check(N.lib.kq_set_kernel_events(op, ctypes.c_void_p(start.cuda_event),
+                                      ctypes.c_void_p(stop.cuda_event)))

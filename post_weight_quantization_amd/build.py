@@ -1,6 +1,6 @@
 """Build libkq.so (the HIP C-ABI library) in-tree for gfx950.
 
-    python -m post_weight_quantization_amd.build
+    python post_weight_quantization_amd/build.py
 
 Every source under csrc/ is compiled with hipcc to an object under _build/,
 then linked into post_weight_quantization_amd/libkq.so. Packed fp32 vector

@@ -475,6 +475,7 @@ kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int
     const float* x = static_cast<const float*>(X);
     const float* xq = static_cast<const float*>(Xq);
     const float* g = static_cast<const float*>(G);
+    KQ_TRY(mark_kernel(KQ_OP_ACCUMULATE_COV, 0, s));
     if (HX) {
       GemmArgs a = gemm_args(xq, d_in, xq, d_in, HX, d_in, d_in, d_in, n_tok, alpha, beta, G_TRANS_A);
       KQ_TRY(gemm_f32(a, s));
@@ -492,7 +493,7 @@ kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int
       GemmArgs a = gemm_args(g, d_out, g, d_out, HG, d_out, d_out, d_out, n_tok, alpha, beta, G_TRANS_A);
       KQ_TRY(gemm_f32(a, s));
     }
-    return KQ_OK;
+    return mark_kernel(KQ_OP_ACCUMULATE_COV, 1, s);
   }
 
   CovArgs a{};
@@ -541,8 +542,10 @@ kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int
   }
   KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(cov_bf16_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(COV_LDS)));
+  KQ_TRY(mark_kernel(KQ_OP_ACCUMULATE_COV, 0, s));
   cov_bf16_kernel<<<unsigned(tiles * ns), 256, COV_LDS, s>>>(a);
   KQ_HIP(hipGetLastError());
+  KQ_TRY(mark_kernel(KQ_OP_ACCUMULATE_COV, 1, s));
   if (ns > 1) {
     float* outs[3] = {HX, D, HG};
     const int64_t dims[3] = {d_in, d_in, d_out};

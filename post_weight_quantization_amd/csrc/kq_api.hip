@@ -31,6 +31,16 @@ kq_status hip_fail(hipError_t e, const char* where) {
 void clear_error() { g_err[0] = 0; }
 
 namespace {
+thread_local hipEvent_t g_cov_ev[2] = {nullptr, nullptr};
+}
+
+kq_status mark_kernel(kq_op op, int edge, hipStream_t s) {
+  if (op != KQ_OP_ACCUMULATE_COV || g_cov_ev[edge] == nullptr) return KQ_OK;
+  KQ_HIP(hipEventRecord(g_cov_ev[edge], s));
+  return KQ_OK;
+}
+
+namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -77,6 +87,17 @@ extern "C" {
 const char* kq_last_error(void) { return g_err; }
 
 const char* kq_version(void) { return "kq 0.1 gfx950"; }
+
+kq_status kq_set_kernel_events(kq_op op, hipEvent_t start, hipEvent_t stop) {
+  clear_error();
+  if (op != KQ_OP_ACCUMULATE_COV)
+    return fail(KQ_ERR_UNSUPPORTED, "set_kernel_events: only KQ_OP_ACCUMULATE_COV has a timed kernel");
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(KQ_ERR_ARG, "set_kernel_events: pass both events or neither");
+  g_cov_ev[0] = start;
+  g_cov_ev[1] = stop;
+  return KQ_OK;
+}
 
 kq_status kq_workspace_size(kq_op op, int64_t d_out, int64_t d_in, int64_t n_tok, kq_dtype dtype,
                             const kq_quant_cfg* cfg, size_t* bytes) {

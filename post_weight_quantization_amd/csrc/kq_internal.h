@@ -14,6 +14,10 @@ kq_status fail(kq_status st, const char* fmt, ...);
 kq_status hip_fail(hipError_t e, const char* where);
 void clear_error();
 
+// measurement hook: records the caller's event (edge 0: start, 1: stop) for
+// `op` on stream s, if one is set on this thread
+kq_status mark_kernel(kq_op op, int edge, hipStream_t s);
+
 #define KQ_HIP(expr)                                        \
   do {                                                      \
     hipError_t _e = (expr);                                 \

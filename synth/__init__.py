@@ -6,7 +6,10 @@ processing, the factorisation, the column sweep and the sensitivity score are
 each implemented separately under ``oracle/`` and in the native library.
 """
 from .gen import (  # noqa: F401
+    BLOCK_BUDGET_BITS,
+    BLOCK_WIDTHS,
     CONFIGS,
+    WORKLOADS,
     LayerSpec,
     bf16_bits_to_f32,
     f32_to_bf16_bits,

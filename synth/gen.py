@@ -90,6 +90,15 @@ CONFIGS: dict[int, list[LayerSpec]] = {
         _spec(4, "down_proj", 8192, 28672, x_stream=3, g_stream=6, sub=6)],
 }
 
+# names of the workloads, as used on command lines
+WORKLOADS: dict[str, int] = {
+    "toy-256": 0,
+    "llama2-7b-q_proj": 1,
+    "llama2-7b-mlp": 2,
+    "llama3-70b-q-down": 3,
+    "llama3-70b-block": 4,
+}
+
 # average bits per parameter available to the decoder block of workload 4
 BLOCK_BUDGET_BITS = 2.5
 BLOCK_WIDTHS = (2, 3, 4)

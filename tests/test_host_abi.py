@@ -66,6 +66,13 @@ def test_null_and_shape_validation():
     assert st == N.KQ_ERR_SHAPE
 
 
+def test_kernel_event_hook_validation():
+    fake = ctypes.c_void_p(0x10000)  # never recorded: the hook only stores it
+    assert N.lib.kq_set_kernel_events(N.KQ_OP_BIIP, None, None) == N.KQ_ERR_UNSUPPORTED
+    assert N.lib.kq_set_kernel_events(N.KQ_OP_ACCUMULATE_COV, fake, None) == N.KQ_ERR_ARG
+    assert N.lib.kq_set_kernel_events(N.KQ_OP_ACCUMULATE_COV, None, None) == N.KQ_OK
+
+
 def test_workspace_checked_before_launch():
     fake = ctypes.c_void_p(0x10000)
     cfg = N.kq_quant_cfg(2, 0, 128, 0)
