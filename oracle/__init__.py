@@ -22,18 +22,23 @@ from .kronq import (  # noqa: F401
     apply_hadamard_right,
     bf16_rne,
     biip,
+    biip_scales,
+    covariance_diagonals,
     covariances,
     cv_in_out,
     damped,
     decode_inputs,
     form_p,
+    form_p_rows,
     grid_fp32,
     hadamard_block,
+    hadamard_rows,
     inv_factor,
     mu_incoherence,
     objective,
     quantize_layer,
     rtn,
+    scaled_traces,
     sensitivity,
     sweep,
     sylvester,

@@ -92,6 +92,29 @@ def hadamard_block(d: int) -> int:
     return d & (-d)
 
 
+def hadamard_rows(rows, sign: np.ndarray, b: int) -> np.ndarray:
+    """Dense rows ``rows`` of V = blockdiag(H_b / sqrt(b), ...) @ diag(sign).
+
+    Entry (r, c) of the Sylvester matrix is (-1)^popcount(r & c); row i of V
+    is nonzero only on its own block. For checks of single entries of
+    V M V^T without forming the whole transform.
+    """
+    sign = np.asarray(sign, dtype=np.float64)
+    d = sign.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.shape[0], d))
+    c = np.arange(b, dtype=np.int64)
+    for k, i in enumerate(rows):
+        blk = (int(i) // b) * b
+        bits = np.bitwise_and(int(i) - blk, c)
+        par = np.zeros(b, dtype=np.int64)
+        while np.any(bits):
+            par ^= bits & 1
+            bits >>= 1
+        out[k, blk:blk + b] = (1 - 2 * par) * sign[blk:blk + b] / np.sqrt(b)
+    return out
+
+
 def apply_hadamard_left(M: np.ndarray, sign: np.ndarray, b: int) -> np.ndarray:
     """V @ M with V = blockdiag(H_b / sqrt(b), ...) @ diag(sign).
 
@@ -169,6 +192,47 @@ def sensitivity(HX, HG):
     return tx, tg, tx * tg
 
 
+def covariance_diagonals(Xq, G, n_total: int | None = None):
+    """diag(H_X) and diag(H_G) alone: sum over tokens of x~_j^2 (g_i^2) / N.
+
+    The diagonals of the covariances in covariances(), without the O(N d^2)
+    products, for layers too wide for the full fp64 matrices on a host.
+    """
+    dx = dg = None
+    if Xq is not None:
+        xq = decode_inputs(Xq).astype(np.float64)
+        n = xq.shape[0] if n_total is None else n_total
+        dx = np.einsum("tj,tj->j", xq, xq) / n
+    if G is not None:
+        g = decode_inputs(G).astype(np.float64)
+        n = g.shape[0] if n_total is None else n_total
+        dg = np.einsum("ti,ti->i", g, g) / n
+    return dx, dg
+
+
+def biip_scales(diag_hx, W, diag_hg):
+    """(s_x, s_g): the BiIP scalings of [KS] Method from the diagonals and W."""
+    W = np.asarray(W, dtype=np.float64)
+    return (_quarter_scale(np.asarray(diag_hx, np.float64), np.sum(W * W, axis=0)),
+            _quarter_scale(np.asarray(diag_hg, np.float64), np.sum(W * W, axis=1)))
+
+
+def scaled_traces(diag_hx, W, diag_hg):
+    """(tr H_X', tr H_G', s) from the diagonals and W, without forming BiIP.
+
+    [KS] Method, BiIP: the scaling takes H_X to S_X^-1 H_X S_X^-1 (reading of
+    biip()), whose trace is sum_j [H_X]_jj / s_j^2; the Hadamard rotation is
+    orthogonal and leaves the trace unchanged. Same on the output side. The
+    sensitivity is the product ([KS] Method, sensitivity).
+    """
+    dhx = np.asarray(diag_hx, np.float64)
+    dhg = np.asarray(diag_hg, np.float64)
+    s_x, s_g = biip_scales(dhx, W, dhg)
+    tx = float(np.sum(dhx / (s_x * s_x)))
+    tg = float(np.sum(dhg / (s_g * s_g)))
+    return tx, tg, tx * tg
+
+
 # --------------------------------------------------------------------------
 # inverse-Hessian factor and the asymmetric correction
 # --------------------------------------------------------------------------
@@ -208,6 +272,21 @@ def form_p(D, U) -> np.ndarray:
     """
     T = np.triu(np.asarray(D, np.float64) @ np.asarray(U, np.float64).T, 1)
     return T @ np.asarray(U, np.float64)
+
+
+def form_p_rows(D_rows, rows, U) -> np.ndarray:
+    """Rows ``rows`` of P = triu_1(D U^T) U, from the same rows of D.
+
+    Row p of P needs row p of D only: t = D_p U^T with t_k = 0 for k <= p,
+    then t U (the definition of form_p() restricted to some rows).
+    """
+    U = np.asarray(U, dtype=np.float64)
+    T = np.asarray(D_rows, dtype=np.float64) @ U.T
+    n = U.shape[0]
+    k = np.arange(n)
+    for r, p in enumerate(np.asarray(rows, dtype=np.int64)):
+        T[r, k <= p] = 0.0
+    return T @ U
 
 
 # --------------------------------------------------------------------------

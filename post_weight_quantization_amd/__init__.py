@@ -5,6 +5,7 @@ include/kq.h). ``api`` is a thin torch binding with the same entry-point
 names; ``layer`` chains the entry points for one layer. Importing this
 package raises if the library has not been built.
 """
+from . import layer  # noqa: F401
 from ._native import KQError, LIB_PATH  # noqa: F401
 from .api import (  # noqa: F401
     kq_accumulate_cov,

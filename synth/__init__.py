@@ -8,6 +8,7 @@ each implemented separately under ``oracle/`` and in the native library.
 from .gen import (  # noqa: F401
     BLOCK_BUDGET_BITS,
     BLOCK_WIDTHS,
+    CHUNK,
     CONFIGS,
     WORKLOADS,
     LayerSpec,

@@ -1,0 +1,348 @@
+"""GPU parity at the workloads' full sizes (131072 bf16 tokens, real layer
+shapes), in the launch configuration of the benchmark: all tokens in one
+covariance call, default Hadamard blocks, then BiIP, sensitivity, factor, P
+and the sweep.
+
+The oracle cannot form these layers whole on a host, so each stage is checked
+on sampled outputs that the oracle computes one by one from the stage's own
+inputs (the GPU's output of the stage before, as in forced replay), plus
+properties that hold at any size:
+
+* covariances: a 128 x 128 sub-block of H_X and D over channels that include
+  the outliers, a sub-block of H_G, and the full diagonals, all in fp64 from
+  the bf16 tokens (<= 1e-4 relative Frobenius);
+* BiIP: the scalings, and 32 x 32 entries of H_X', D', H_G' and W' in the
+  first block pair and in a far block pair (<= 1e-5), the traces, and the
+  sensitivity against the closed form on the raw data (<= 1e-5);
+* inverse factor: upper triangle; U (H + delta I) U^T z = z for random probes
+  within the fp32 bound; the trailing 1024 x 1024 block against the factor of
+  the trailing block of H (the OBS-row property);
+* P: sampled rows from the GPU's D' and U;
+* sweep: forced replay of sampled rows on the GPU's own W0', U and P (codes
+  >= 99.99% identical, every mismatch within 1e-4 of a step of a midpoint);
+* objective: fp64 oracle where the products fit a host in seconds, else
+  GPTAQ below round-to-nearest on the same grid.
+
+The LLaMA-3-70B block runs all seven sublayers: sensitivities against the
+closed form on the raw data, the allocation against the oracle's, and the
+sweep of two sublayers at their allocated widths by forced replay.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import BLOCK_BUDGET_BITS, BLOCK_WIDTHS, CHUNK, WORKLOADS, layer_specs, make_layer
+from tests.gpu_util import code_report, dev, have_gpu, host, rel_fro
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900),
+              pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+if have_gpu():
+    import torch
+
+    import post_weight_quantization_amd as kq
+    from post_weight_quantization_amd import layer as kql
+
+LAYERS = [("llama2-7b-q_proj", 0), ("llama2-7b-mlp", 0), ("llama2-7b-mlp", 2),
+          ("llama3-70b-q-down", 0), ("llama3-70b-q-down", 1)]
+REPLAY_ROWS = 32
+
+
+def _spec(workload, idx):
+    return layer_specs(WORKLOADS[workload])[idx]
+
+
+def _diagonals(Xq, G, n):
+    """Full diag(H_X), diag(H_G) in fp64, a token chunk at a time."""
+    dx = np.zeros(Xq.shape[1]) if Xq is not None else None
+    dg = np.zeros(G.shape[1]) if G is not None else None
+    for t0 in range(0, n, CHUNK):
+        a, b = oracle.covariance_diagonals(None if Xq is None else Xq[t0:t0 + CHUNK],
+                                           None if G is None else G[t0:t0 + CHUNK], n_total=n)
+        if dx is not None:
+            dx += a
+        if dg is not None:
+            dg += b
+    return dx, dg
+
+
+def _matmul64(A32, B64, rows=4096):
+    """A (fp32, host) @ B in fp64, a row panel at a time."""
+    out = np.empty((A32.shape[0], B64.shape[1]))
+    for r0 in range(0, A32.shape[0], rows):
+        out[r0:r0 + rows] = A32[r0:r0 + rows].astype(np.float64) @ B64
+    return out
+
+
+def _pipeline(spec):
+    print(f"\n[fullsize] {spec.name} {spec.d_out}x{spec.d_in} N={spec.n_tok}", flush=True)
+    L = make_layer(spec)
+    X, Xq, G = dev(L["x"]), dev(L["xq"]), dev(L["g"])
+    HX, D, HG = kq.kq_accumulate_cov(X, Xq, G, 1.0 / spec.n_tok, 0.0)
+    del X, Xq, G
+    pre = dict(HX=HX.clone(), D=D.clone(), HG=HG.clone())
+    W = dev(L["W"])
+    s_x, s_g = kq.kq_biip(W, HX, D, HG, dev(L["sign_in"]), dev(L["sign_out"]))
+    sens = kq.kq_sensitivity(HX, HG)
+    W0p = W.clone()
+    U = kq.kq_cholesky_inv(HX, spec.damp)
+    P = kq.kq_form_p(D, U)
+    codes, scale, zero = kq.kq_gptaq_quantize(W, U, D, spec.bits, spec.group)
+    torch.cuda.synchronize()
+    return dict(spec=spec, L=L, pre=pre, HX=HX, D=D, HG=HG, s_x=s_x, s_g=s_g, sens=sens, W0p=W0p,
+                What=W, U=U, P=P, codes=codes, scale=scale, zero=zero)
+
+
+@pytest.fixture(scope="module", params=LAYERS, ids=lambda p: f"{p[0]}-{p[1]}")
+def run(request):
+    r = _pipeline(_spec(*request.param))
+    yield r
+    r.clear()
+    torch.cuda.empty_cache()
+
+
+def _channels(d, rng, n=128, first=16):
+    c = np.concatenate([np.arange(min(first, d)), rng.choice(np.arange(first, d), n - first,
+                                                              replace=False)])
+    return np.sort(c)
+
+
+def test_covariances_sampled(run):
+    spec, L, pre = run["spec"], run["L"], run["pre"]
+    rng = np.random.default_rng(1)
+    C = _channels(spec.d_in, rng)
+    R = _channels(spec.d_out, rng, first=0)
+    HXs, Ds, _ = oracle.covariances(L["x"][:, C], L["xq"][:, C], None)
+    _, _, HGs = oracle.covariances(None, None, L["g"][:, R])
+    ix = torch.as_tensor(C, device="cuda")
+    ig = torch.as_tensor(R, device="cuda")
+    gx = host(pre["HX"][ix][:, ix])
+    gd = host(pre["D"][ix][:, ix])
+    gg = host(pre["HG"][ig][:, ig])
+    errs = dict(HX=rel_fro(gx, HXs), D=rel_fro(gd, Ds), HG=rel_fro(gg, HGs))
+    dx, dg = _diagonals(L["xq"], L["g"], spec.n_tok)
+    errs["diagX"] = rel_fro(host(torch.diagonal(pre["HX"])), dx)
+    errs["diagG"] = rel_fro(host(torch.diagonal(pre["HG"])), dg)
+    print(f"covariance errors {errs}")
+    assert max(errs.values()) <= 1e-4, errs
+    # both triangles are written and mirror each other exactly
+    np.testing.assert_array_equal(gx, gx.T)
+    np.testing.assert_array_equal(gg, gg.T)
+    run["diag"] = (dx, dg)
+
+
+def _block_entries(M_pre_dev, s_left, s_right, sign_l, sign_r, bl, br, I, J):
+    """Expected (V_l S_l^-1 M S_r^-1 V_r^T)[I, J] from the GPU's pre-BiIP M (fp64)."""
+    Vi = oracle.hadamard_rows(I, sign_l, bl)
+    Vj = oracle.hadamard_rows(J, sign_r, br)
+    bi0, bj0 = (I[0] // bl) * bl, (J[0] // br) * br
+    sub = host(M_pre_dev[bi0:bi0 + bl, bj0:bj0 + br]).astype(np.float64)
+    sub = sub / np.outer(s_left[bi0:bi0 + bl], s_right[bj0:bj0 + br])
+    return Vi[:, bi0:bi0 + bl] @ sub @ Vj[:, bj0:bj0 + br].T
+
+
+def _pick(d, b, rng, first_block, k=32):
+    b0 = 0 if first_block else (d // b - 1) * b
+    idx = np.concatenate([[b0, b0 + b - 1], b0 + rng.choice(np.arange(1, b - 1), k - 2,
+                                                           replace=False)])
+    return np.sort(idx)
+
+
+def test_biip_sampled(run):
+    spec, L, pre = run["spec"], run["L"], run["pre"]
+    n, m = spec.d_in, spec.d_out
+    bi, bo = oracle.hadamard_block(n), oracle.hadamard_block(m)
+    si = L["sign_in"].astype(np.float64)
+    so = L["sign_out"].astype(np.float64)
+    dxg = host(torch.diagonal(pre["HX"])).astype(np.float64)
+    dgg = host(torch.diagonal(pre["HG"])).astype(np.float64)
+    s_x, s_g = oracle.biip_scales(dxg, L["W"], dgg)
+    errs = dict(s_x=rel_fro(host(run["s_x"]), s_x), s_g=rel_fro(host(run["s_g"]), s_g))
+    rng = np.random.default_rng(2)
+    for tag, f1, f2 in (("first", True, True), ("far", True, False)):
+        I, J = _pick(n, bi, rng, f1), _pick(n, bi, rng, f2)
+        want = _block_entries(pre["HX"], s_x, s_x, si, si, bi, bi, I, J)
+        got = host(run["HX"][torch.as_tensor(I, device="cuda")][:, torch.as_tensor(J, device="cuda")])
+        errs[f"HX_{tag}"] = rel_fro(got, want)
+        want = _block_entries(pre["D"], s_x, s_x, si, si, bi, bi, I, J)
+        got = host(run["D"][torch.as_tensor(I, device="cuda")][:, torch.as_tensor(J, device="cuda")])
+        errs[f"D_{tag}"] = rel_fro(got, want)
+        Io, Jo = _pick(m, bo, rng, f1), _pick(m, bo, rng, f2)
+        want = _block_entries(pre["HG"], s_g, s_g, so, so, bo, bo, Io, Jo)
+        got = host(run["HG"][torch.as_tensor(Io, device="cuda")][:, torch.as_tensor(Jo, device="cuda")])
+        errs[f"HG_{tag}"] = rel_fro(got, want)
+        # W' = V_out S_G W S_X V_in^T (the scalings multiply W)
+        Wt = torch.from_numpy(L["W"]).cuda()
+        want = _block_entries(Wt, 1.0 / s_g, 1.0 / s_x, so, si, bo, bi, Io, J)
+        got = host(run["W0p"][torch.as_tensor(Io, device="cuda")][:, torch.as_tensor(J, device="cuda")])
+        errs[f"W_{tag}"] = rel_fro(got, want)
+    tx, tg, s = run["sens"]
+    otx, otg, _ = oracle.scaled_traces(dxg, L["W"], dgg)
+    errs["trHX"] = abs(tx / otx - 1)
+    errs["trHG"] = abs(tg / otg - 1)
+    print(f"BiIP errors {errs}")
+    assert max(errs.values()) <= 1e-5, errs
+
+
+def test_sensitivity_against_raw_data(run):
+    spec, L = run["spec"], run["L"]
+    dx, dg = run.get("diag") or _diagonals(L["xq"], L["g"], spec.n_tok)
+    _, _, s_want = oracle.scaled_traces(dx, L["W"], dg)
+    s = run["sens"][2]
+    print(f"s gpu {s:.9g} oracle {s_want:.9g} rel {abs(s / s_want - 1):.3g}")
+    assert s == pytest.approx(s_want, rel=1e-5)
+
+
+def test_inverse_factor_probes_and_trailing_block(run):
+    spec = run["spec"]
+    n = spec.d_in
+    U = run["U"]
+    assert float(torch.tril(U, -1).abs().max()) == 0.0
+    assert float(torch.diagonal(U).min()) > 0.0
+    H = host(run["HX"])
+    delta = spec.damp * float(np.mean(np.diag(H).astype(np.float64)))
+    Uh = host(U)
+    rng = np.random.default_rng(3)
+    Z = rng.standard_normal((n, 8))
+    # y = U (H + delta I) U^T z, in fp64 a panel at a time
+    t = _matmul64(np.ascontiguousarray(Uh.T), Z)
+    y = _matmul64(Uh, _matmul64(H, t) + delta * t)
+    resid = float(np.linalg.norm(y - Z) / np.linalg.norm(Z))
+    # kappa bound: lambda_min >= delta (H is a covariance, PSD); lambda_max by
+    # power iteration (an estimate: fp32 products suffice), doubled for margin
+    v = rng.standard_normal(n).astype(np.float32)
+    for _ in range(30):
+        v = H @ v + np.float32(delta) * v
+        lam = float(np.linalg.norm(v))
+        v /= np.float32(lam)
+    kappa = 2.0 * lam / delta
+    # trailing block: U_FF^T U_FF = (H_FF + delta I)^-1 (rows of U are OBS rows)
+    k = min(1024, n)
+    F = slice(n - k, n)
+    HFF = H[F, F].astype(np.float64) + delta * np.eye(k)
+    UFF = oracle.inv_factor(HFF, 0.0)
+    fwd = rel_fro(Uh[F, F], UFF)
+    kff = float(np.linalg.cond(HFF))
+    print(f"n={n} probe resid {resid:.3g} kappa<= {kappa:.3g}; trailing fwd {fwd:.3g} kappa {kff:.3g}")
+    assert resid < 1e-6 * kappa
+    assert fwd < 1e-6 * kff
+
+
+def test_form_p_sampled_rows(run):
+    spec = run["spec"]
+    n = spec.d_in
+    rng = np.random.default_rng(4)
+    rows = np.sort(np.concatenate([[0, 127, 128, n // 2, n - 129, n - 2, n - 1],
+                                   rng.choice(n, 9, replace=False)]))
+    it = torch.as_tensor(rows, device="cuda")
+    Uh = host(run["U"]).astype(np.float64)
+    want = oracle.form_p_rows(host(run["D"][it]), rows, Uh)
+    got = host(run["P"][it])
+    err = rel_fro(got, want)
+    print(f"P rows error {err:.3g}")
+    assert err <= 1e-4
+    for r, p in enumerate(rows):
+        assert np.all(got[r, :p + 1] == 0)
+
+
+def test_sweep_forced_replay_sampled_rows(run):
+    spec = run["spec"]
+    m = spec.d_out
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([[0, m - 1], rng.choice(np.arange(1, m - 1), REPLAY_ROWS - 2,
+                                                          replace=False)]))
+    it = torch.as_tensor(rows, device="cuda")
+    W0 = host(run["W0p"][it])
+    codes = host(run["codes"][it])
+    scale, zero = host(run["scale"][it]), host(run["zero"][it])
+    Uh = host(run["U"]).astype(np.float64)
+    Ph = host(run["P"]).astype(np.float64)
+    grid0 = None if spec.group else (scale[:, 0], zero[:, 0])
+    ref = oracle.sweep(W0, Uh, Ph, spec.bits, spec.group, spec.block, forced_codes=codes,
+                       forced_grid=(scale, zero) if spec.group else None, grid0=grid0)
+    rep = code_report(ref, codes.size)
+    print(f"replay {spec.name}: {rep}")
+    assert rep["n"] <= max(1, int(1e-4 * codes.size)), rep
+    assert rep["worst"] <= 1e-4, rep
+    if spec.group:
+        for smax, nz in ref["grid_mismatch"]:
+            assert smax < 1e-5 and nz == 0
+    else:
+        sc, zr = oracle.grid_fp32(W0, spec.bits)
+        np.testing.assert_array_equal(scale[:, 0], sc)
+        np.testing.assert_array_equal(zero[:, 0], zr)
+    np.testing.assert_allclose(host(run["What"][it]), ref["what"], rtol=1e-5, atol=1e-6)
+
+
+def _rtn_dev(W0, scale, zero, bits, group):
+    g = group or W0.shape[1]
+    sc = scale.repeat_interleave(g, dim=1)
+    zr = zero.repeat_interleave(g, dim=1)
+    return (sc * (torch.clamp(torch.round(W0 / sc) + zr, 0, 2 ** bits - 1) - zr)).contiguous()
+
+
+def test_objective(run):
+    spec = run["spec"]
+    obj = kq.kq_layer_objective(run["W0p"], run["What"], run["HX"], run["D"], run["HG"])
+    if max(spec.d_in, spec.d_out) <= 4096 or spec.d_in * spec.d_in * spec.d_out <= 2e11:
+        want = oracle.objective(host(run["W0p"]), host(run["What"]), host(run["HX"]),
+                                host(run["D"]), host(run["HG"]))
+        print(f"objective gpu {obj:.9g} oracle {want:.9g}")
+        assert obj == pytest.approx(want, rel=1e-3)
+    # round-to-nearest on the same grid (for groups: the sweep's own group grids)
+    Wr = _rtn_dev(run["W0p"], run["scale"], run["zero"], spec.bits, spec.group)
+    obj_rtn = kq.kq_layer_objective(run["W0p"], Wr, run["HX"], run["D"], run["HG"])
+    print(f"objective {obj:.6g} vs round-to-nearest {obj_rtn:.6g}")
+    assert obj < obj_rtn
+
+
+# ------------------------------------------------------------ decoder block
+
+
+def test_llama3_70b_block_allocation_and_quantization():
+    specs = layer_specs(WORKLOADS["llama3-70b-block"])
+    prepared, s_want, data = [], [], {}
+    x_cache = {}
+    for sp in specs:
+        print(f"\n[block] {sp.name} {sp.d_out}x{sp.d_in}", flush=True)
+        if sp.x_stream not in x_cache:
+            x_cache.clear()
+            x_cache[sp.x_stream] = make_layer(sp, parts=("x", "xq"))
+        Lx = x_cache[sp.x_stream]
+        Lg = make_layer(sp, parts=("g",))
+        dx, dg = _diagonals(Lx["xq"], Lg["g"], sp.n_tok)
+        s_want.append(oracle.scaled_traces(dx, Lg["W"], dg)[2])
+        p = kql.prepare_layer(dev(Lx["x"]), dev(Lx["xq"]), dev(Lg["g"]), dev(Lg["W"]),
+                              dev(Lg["sign_in"]), dev(Lg["sign_out"]))
+        torch.cuda.empty_cache()
+        prepared.append(p)
+        data[sp.name] = p.W.clone()
+    x_cache.clear()
+    s_got = [p.s for p in prepared]
+    for sp, a, b in zip(specs, s_got, s_want):
+        print(f"s[{sp.name}] gpu {a:.9g} oracle {b:.9g}")
+        assert a == pytest.approx(b, rel=1e-5)
+    n_params = [sp.n_params for sp in specs]
+    bits_want = oracle.allocate_bits(s_want, n_params, BLOCK_WIDTHS, BLOCK_BUDGET_BITS)
+    bits, outs = kql.quantize_block(prepared, BLOCK_WIDTHS, BLOCK_BUDGET_BITS)
+    print(f"widths {dict(zip([sp.name for sp in specs], bits))}")
+    assert bits == bits_want
+    assert sum(b * n for b, n in zip(bits, n_params)) <= BLOCK_BUDGET_BITS * sum(n_params)
+    # forced replay of sampled rows for two sublayers at their allocated widths
+    rng = np.random.default_rng(6)
+    for name in ("k_proj", "gate_proj"):
+        k = [sp.name for sp in specs].index(name)
+        sp, p, o = specs[k], prepared[k], outs[k]
+        rows = np.sort(rng.choice(sp.d_out, 16, replace=False))
+        it = torch.as_tensor(rows, device="cuda")
+        P = kq.kq_form_p(p.D, o["U"])
+        codes = host(o["codes"][it])
+        scale, zero = host(o["scale"][it]), host(o["zero"][it])
+        ref = oracle.sweep(host(data[name][it]), host(o["U"]).astype(np.float64),
+                           host(P).astype(np.float64), bits[k], 0, sp.block, forced_codes=codes,
+                           grid0=(scale[:, 0], zero[:, 0]))
+        rep = code_report(ref, codes.size)
+        print(f"replay {name} at {bits[k]} bits: {rep}")
+        assert rep["n"] <= max(1, int(1e-4 * codes.size)), rep
+        assert rep["worst"] <= 1e-4, rep
+        assert int(codes.max()) <= 2 ** bits[k] - 1

@@ -198,6 +198,52 @@ def test_biip_closed_form_traces_and_sensitivity():
     np.testing.assert_allclose(s_g, (np.diag(HG) / r) ** 0.25, rtol=1e-13)
 
 
+def test_diagonal_shortcuts_match_full_forms():
+    """covariance_diagonals / scaled_traces (used where the full fp64 matrices
+    do not fit a host) agree with the full covariances, BiIP and traces."""
+    x, xq, g, W, si, so = _small_problem()
+    HX, D, HG = oracle.covariances(x, xq, g)
+    dx, dg = oracle.covariance_diagonals(xq, g)
+    np.testing.assert_allclose(dx, np.diag(HX), rtol=1e-13)
+    np.testing.assert_allclose(dg, np.diag(HG), rtol=1e-13)
+    W2, HX2, D2, HG2, s_x, s_g = oracle.biip(W, HX, D, HG, si, so)
+    tx, tg, s = oracle.scaled_traces(dx, W, dg)
+    assert tx == pytest.approx(np.trace(HX2), rel=1e-12)
+    assert tg == pytest.approx(np.trace(HG2), rel=1e-12)
+    assert s == pytest.approx(oracle.sensitivity(HX2, HG2)[2], rel=1e-12)
+    # a zero column of W leaves its diagonal entry unscaled
+    W0 = W.copy()
+    W0[:, 3] = 0
+    tx0, _, _ = oracle.scaled_traces(dx, W0, dg)
+    c = np.sum(W0 * W0, axis=0)
+    want = np.sum(np.where(c > 0, np.sqrt(dx * c), dx))
+    assert tx0 == pytest.approx(want, rel=1e-12)
+
+
+def test_row_forms_match_whole_matrix_forms():
+    """hadamard_rows and form_p_rows (single-entry checks at full size) agree
+    with the dense Sylvester construction and with form_p."""
+    rng = np.random.default_rng(21)
+    for d, b in ((48, 16), (64, 64), (40, 8)):
+        sign = rng.choice([-1, 1], d)
+        Vd = oracle.apply_hadamard_left(np.eye(d), sign, b)
+        rows = rng.choice(d, 7, replace=False)
+        np.testing.assert_array_equal(oracle.hadamard_rows(rows, sign, b), Vd[rows])
+    n = 96
+    H = _spd(rng, n)
+    U = oracle.inv_factor(H, 0.01)
+    D = rng.standard_normal((n, n))
+    rows = np.array([0, 5, 47, 94, 95])
+    np.testing.assert_allclose(oracle.form_p_rows(D[rows], rows, U), oracle.form_p(D, U)[rows],
+                               rtol=1e-12, atol=1e-12)
+    x, xq, g, W, si, so = _small_problem()
+    HX, D, HG = oracle.covariances(x, xq, g)
+    _, _, _, _, s_x, s_g = oracle.biip(W, HX, D, HG, si, so)
+    bx, bg = oracle.biip_scales(np.diag(HX), W, np.diag(HG))
+    np.testing.assert_array_equal(bx, s_x)
+    np.testing.assert_array_equal(bg, s_g)
+
+
 def test_biip_rotation_preserves_traces():
     rng = np.random.default_rng(7)
     M = _spd(rng, 16)
