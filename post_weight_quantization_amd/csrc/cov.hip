@@ -6,26 +6,29 @@
 // per row), each output is a "TN" product C[i][j] = sum_t A[t][i] B[t][j].
 //
 // bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   * one launch covers every output tile of all three matrices (H_X and H_G
-//     lower-triangle tiles only, D full), times `nsplit` token splits;
-//     blockIdx % nsplit selects the split so that, with nsplit | 8, all
-//     workgroups on one XCD stream the same token range through its L2;
-//   * workgroup tile 256 x 256, 4 waves of 128 x 128 (4 x 4 MFMA blocks,
-//     256 accumulator registers per lane), 64 tokens per LDS stage, two
-//     stages of LDS (128 KB) with the next stage's global loads in flight
-//     while the current one feeds the MFMAs;
-//   * each thread loads 8 tokens x 8 channels (16 bytes per token row, 32
-//     threads cover a 512-byte row segment) and transposes them in registers
-//     with v_perm so LDS holds [channel][token]; an MFMA operand (8
-//     consecutive tokens of one channel) is then one 16-byte LDS read. The
-//     16-byte chunks of each channel row are XOR-swizzled so the transposed
-//     stores and the operand reads are both bank-conflict free;
-//   * for D the A operand is formed on the fly: dX = bf16_rne(X - Xq), the
-//     rounding done by the packed fp32->bf16 conversion (nearest even);
-//   * with nsplit == 1 the epilogue applies alpha/beta and mirrors the lower
-//     tiles of H_X and H_G into the upper triangle; otherwise partial sums go
-//     to scratch and a reduction kernel does the same.
+//   * a drift pre-pass writes dX = bf16_rne(X - Xq) once (packed fp32 -> bf16
+//     conversion, nearest even);
+//   * work items are 256 x 256 output tiles over a token range; H_X and H_G
+//     take lower-triangle tiles only, D all tiles; one launch covers all three;
+//   * a workgroup (4 waves of 128 x 128, 256 accumulator registers per lane)
+//     streams stages of 32 tokens x 256 channels per operand from HBM straight
+//     into LDS with global_load_lds_dwordx4 through a 4-deep ring, and reads
+//     MFMA operands with transposing LDS reads (ds_read_b64_tr_b16) from an
+//     XOR-swizzled layout (16-byte chunk c of token row r at c ^ 4(r & 3));
+//   * the host builds the schedule: tiles are enumerated in bands of 8 tile
+//     rows so that 32 consecutive tiles form an 8 x 4 block touching 12
+//     channel strips; each group of 32 tiles and token split fills the 32
+//     CUs of one XCD for one round (workgroup b runs on XCD b % 8), so those
+//     workgroups stream the same tokens of few strips through one L2; the
+//     items left for a last, partial round are cut into shorter token pieces
+//     spread over all XCDs so no CU idles while a few finish;
+//   * an item that covers all tokens of its tile applies alpha/beta and
+//     mirrors lower tiles of H_X and H_G itself; otherwise it writes its
+//     partial tile to a slot of a pool and a reduction kernel sums each
+//     tile's slots in a fixed order (deterministic), then does the same.
 // fp32 path (small workloads): the generic fp32 MFMA GEMM with transposed A.
+#include <vector>
+
 #include "kq_internal.h"
 
 namespace kq {
@@ -44,34 +47,34 @@ constexpr int STB = KS * ROWB;     // bytes per operand stage (16 KB)
 enum Kind { K_HX = 0, K_D = 1, K_HG = 2 };
 enum Mode { M_DIAG = 0, M_PAIR = 1 };
 
+// One work item: tile (I, J) of matrix `kind` over tokens [t0, t1). slot < 0:
+// write the output tile directly; else write the partial to pool slot `slot`.
+struct CovItem {
+  int32_t kind, I, J, slot;
+  int64_t t0, t1;
+};
+
+// A tile whose partials sit in pool slots slot0 .. slot0 + count - 1.
+struct CovRed {
+  int32_t kind, I, J, count;
+  int64_t slot0;
+};
+
 struct CovArgs {
   const uint16_t* Xq;
   const uint16_t* dX;  // bf16 drift, token-major (written by the drift pre-pass)
   const uint16_t* G;
-  int64_t n_tok, d_in, d_out;
+  int64_t d_in, d_out;
   float alpha, beta;
-  float* out[3];       // final outputs (direct mode)
-  float* part;         // partial sums (split mode): [split][HX | D | HG]
-  int64_t part_stride; // floats per split
-  int64_t part_off[3]; // offset of each matrix inside one split
-  int nt_in, nt_out;   // tiles per dimension
-  int tasks[3];        // tiles per matrix (0 when skipped)
-  int nsplit;
-  int64_t tok_chunk;   // tokens per split (multiple of KS)
+  float* out[3];       // H_X, D, H_G
+  const CovItem* items;
+  float* pool;         // partial tiles, 256 x 256 floats per slot
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-__device__ inline void tri_decode(int t, int& I, int& J) {
-  int i = int((sqrtf(8.f * float(t) + 1.f) - 1.f) * 0.5f);
-  while ((i + 1) * (i + 2) / 2 <= t) ++i;
-  while (i * (i + 1) / 2 > t) --i;
-  I = i;
-  J = t - i * (i + 1) / 2;
-}
 
 // Raw tiles keep the global layout (token rows of 256 channels); the 16-byte
 // chunk c of row r sits at slot c ^ (4 (r & 3)). A transposing operand read
@@ -224,33 +227,42 @@ __device__ inline void tile_loop(const uint16_t* srcA, const uint16_t* srcB, int
   }
   if (n_full == 0) return;
 
-  // ---- full stages through the DMA ring (KS = 2 k-steps per stage).
-  // Stage s: MFMAs of k-step 0 run while k-step 1 operands are read; then the
-  // data of stage s+1 is awaited (own DMA: vmcnt; other waves: barrier), the
-  // DMA of stage s+3 is issued into the slot stage s-1 used, and the MFMAs of
-  // k-step 1 run while stage s+1's k-step 0 operands are read.
+  // ---- full stages through the DMA ring (KS = 2 k-steps per stage, NST
+  // slots, stage s in slot s % NST). Iteration s: the MFMAs of k-step 0 run
+  // while the k-step 1 operands of stage s are read; stage s+1 is awaited
+  // (own DMA: vmcnt; other waves: the barrier, which also retires every read
+  // of slot s); stage s+NST is issued into slot s; the MFMAs of k-step 1 run
+  // while stage s+1's k-step 0 operands are read. NST - 1 stages stay in
+  // flight behind the one being consumed.
   constexpr int PER = 4 * NOP;  // DMA instructions per stage per wave
-  for (int k = 0; k < NST - 1; ++k)
+  auto wait_stages = [&](int64_t k) {  // at most k stages may stay outstanding
+    if (k >= 3) wait_vm<3 * PER>();
+    else if (k == 2) wait_vm<2 * PER>();
+    else if (k == 1) wait_vm<PER>();
+    else wait_vm<0>();
+  };
+  static_assert(NST <= 4, "wait_stages covers at most 3 outstanding stages");
+  for (int k = 0; k < NST; ++k)
     if (k < n_full) issue(k, k);
-  if (n_full >= 3) wait_vm<2 * PER>();
-  else if (n_full == 2) wait_vm<PER>();
-  else wait_vm<0>();
+  wait_stages(min<int64_t>(n_full, NST) - 1);
   __syncthreads();
   Frags f0, f1;
   read(f0, 0, 0);
+  int slot = 0;
   for (int64_t s = 0; s + 1 < n_full; ++s) {
-    read(f1, int(s % NST), 1);
+    const int nslot = slot + 1 == NST ? 0 : slot + 1;
+    read(f1, slot, 1);
     mma(f0);
     interleave();
-    if (s + 2 < n_full) wait_vm<PER>();
-    else wait_vm<0>();
+    wait_stages(min<int64_t>(n_full, s + NST) - (s + 2));
     __syncthreads();
-    if (s + 3 < n_full) issue(s + 3, int((s + 3) % NST));
-    read(f0, int((s + 1) % NST), 0);
+    if (s + NST < n_full) issue(s + NST, slot);
+    read(f0, nslot, 0);
     mma(f1);
     interleave();
+    slot = nslot;
   }
-  read(f1, int((n_full - 1) % NST), 1);
+  read(f1, slot, 1);
   mma(f0);
   mma(f1);
 }
@@ -258,28 +270,12 @@ __device__ inline void tile_loop(const uint16_t* srcA, const uint16_t* srcB, int
 __global__ __launch_bounds__(256) void cov_bf16_kernel(CovArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
-  const int b = blockIdx.x;
-  const int split = b % a.nsplit;
-  int tile = b / a.nsplit;
-  int kind, I, J;
-  if (tile < a.tasks[0]) {
-    kind = K_HX;
-    tri_decode(tile, I, J);
-  } else if ((tile -= a.tasks[0]) < a.tasks[1]) {
-    kind = K_D;
-    I = tile / a.nt_in;
-    J = tile % a.nt_in;
-  } else {
-    tile -= a.tasks[1];
-    kind = K_HG;
-    tri_decode(tile, I, J);
-  }
+  const CovItem it = a.items[blockIdx.x];
+  if (it.kind < 0) return;
+  const int kind = it.kind, I = it.I, J = it.J;
   const uint16_t* srcB = kind == K_HG ? a.G : a.Xq;
   const uint16_t* srcA = kind == K_D ? a.dX : srcB;
   const int64_t width = kind == K_HG ? a.d_out : a.d_in;
-
-  const int64_t t_begin = int64_t(split) * a.tok_chunk;
-  const int64_t t_end = min(a.n_tok, t_begin + a.tok_chunk);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -297,19 +293,19 @@ __global__ __launch_bounds__(256) void cov_bf16_kernel(CovArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (t_begin < t_end) {
+  if (it.t0 < it.t1) {
     const int64_t I0 = int64_t(I) * CT, J0 = int64_t(J) * CT;
     if (kind != K_D && I == J)
-      tile_loop<M_DIAG>(srcA, srcB, width, width, I0, J0, t_begin, t_end, lds, acc);
+      tile_loop<M_DIAG>(srcA, srcB, width, width, I0, J0, it.t0, it.t1, lds, acc);
     else
-      tile_loop<M_PAIR>(srcA, srcB, width, width, I0, J0, t_begin, t_end, lds, acc);
+      tile_loop<M_PAIR>(srcA, srcB, width, width, I0, J0, it.t0, it.t1, lds, acc);
   }
 
   // acc[i][j][r] holds C[I*CT + wm + 32i + 8(r/4) + 4lk + r%4][J*CT + wn + 32j + lr]
-  const int64_t dim = width;
-  const int64_t row0 = int64_t(I) * CT + wm;
-  const int64_t col0 = int64_t(J) * CT + wn;
-  if (a.nsplit == 1) {
+  if (it.slot < 0) {
+    const int64_t dim = width;
+    const int64_t row0 = int64_t(I) * CT + wm;
+    const int64_t col0 = int64_t(J) * CT + wn;
     float* C = a.out[kind];
     const float alpha = a.alpha, beta = a.beta;
     const bool mirror = (kind != K_D) && (I != J);
@@ -348,16 +344,17 @@ __global__ __launch_bounds__(256) void cov_bf16_kernel(CovArgs a) {
           }
         }
   } else {
-    float* P = a.part + split * a.part_stride + a.part_off[kind];
+    // partial tile, row-major 256 x 256 in its slot
+    float* P = a.pool + it.slot * int64_t(CT * CT);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t m = row0 + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
-          const int64_t n = col0 + 32 * j + lr;
-          if (m < dim && n < dim) P[m * dim + n] = acc[i][j][r];
+          const int m = wm + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
+          const int n = wn + 32 * j + lr;
+          P[m * CT + n] = acc[i][j][r];
         }
   }
 }
@@ -381,42 +378,42 @@ __global__ __launch_bounds__(256) void drift_bf16_kernel(const uint4* __restrict
   }
 }
 
-// Sum the split partials of one matrix, apply alpha/beta, mirror lower tiles
-// of symmetric outputs. 64 x 64 tiles; for symmetric matrices only lower
-// tiles are scheduled and each writes both (I, J) and (J, I).
-__global__ __launch_bounds__(256) void cov_reduce_kernel(const float* __restrict__ part,
-                                                         int64_t part_stride, int nsplit,
-                                                         float* C, int64_t dim, float alpha,
-                                                         float beta, int sym, int ntile) {
+// Sum the pool slots of one tile in slot order, apply alpha/beta, write the
+// tile and, for off-diagonal tiles of H_X and H_G, its transpose. One
+// workgroup per 64 x 64 sub-block of a 256 x 256 tile.
+__global__ __launch_bounds__(256) void cov_pool_reduce_kernel(const CovRed* __restrict__ reds,
+                                                              const float* __restrict__ pool,
+                                                              float* HX, float* D, float* HG,
+                                                              int64_t d_in, int64_t d_out,
+                                                              float alpha, float beta) {
   __shared__ float tileT[64][65];
-  int I, J;
-  if (sym) {
-    tri_decode(blockIdx.x, I, J);
-  } else {
-    I = blockIdx.x / ntile;
-    J = blockIdx.x % ntile;
-  }
+  const CovRed rd = reds[blockIdx.x >> 4];
+  const int sub = blockIdx.x & 15;
+  float* C = rd.kind == K_HX ? HX : rd.kind == K_D ? D : HG;
+  const int64_t dim = rd.kind == K_HG ? d_out : d_in;
+  const int lr0 = (sub >> 2) * 64, lc0 = (sub & 3) * 64;
   const int tx = threadIdx.x & 63;
   const int ty = threadIdx.x >> 6;  // 0..3
-  const int64_t c = int64_t(J) * 64 + tx;
+  const int64_t c = int64_t(rd.J) * CT + lc0 + tx;
   for (int rr = ty; rr < 64; rr += 4) {
-    const int64_t r = int64_t(I) * 64 + rr;
+    const int64_t r = int64_t(rd.I) * CT + lr0 + rr;
+    const float* src = pool + rd.slot0 * int64_t(CT * CT) + (lr0 + rr) * CT + lc0 + tx;
     float s = 0.f;
+    for (int k = 0; k < rd.count; ++k) s += src[int64_t(k) * CT * CT];
+    s *= alpha;
     if (r < dim && c < dim) {
-      for (int k = 0; k < nsplit; ++k) s += part[k * part_stride + r * dim + c];
-      float o = alpha * s;
+      float o = s;
       if (beta != 0.f) o += beta * C[r * dim + c];
       C[r * dim + c] = o;
-      s = alpha * s;
     }
     tileT[rr][tx] = s;
   }
-  if (!sym || I == J) return;
+  if (rd.kind == K_D || rd.I == rd.J) return;
   __syncthreads();
-  // write the transpose: element (J*64 + rr, I*64 + tx) = tile[tx][rr]
-  const int64_t c2 = int64_t(I) * 64 + tx;
+  // transpose: element (J*CT + lc0 + rr, I*CT + lr0 + tx) = tile[tx][rr]
+  const int64_t c2 = int64_t(rd.I) * CT + lr0 + tx;
   for (int rr = ty; rr < 64; rr += 4) {
-    const int64_t r2 = int64_t(J) * 64 + rr;
+    const int64_t r2 = int64_t(rd.J) * CT + lc0 + rr;
     if (r2 < dim && c2 < dim) {
       float o = tileT[tx][rr];
       if (beta != 0.f) o += beta * C[r2 * dim + c2];
@@ -433,20 +430,137 @@ __global__ void drift_f32_kernel(const float* __restrict__ X, const float* __res
     dX[i] = X[i] - Xq[i];
 }
 
-int choose_split(int tiles) {
-  // Aim for >= ~4 workgroups per CU (256 CUs); splits stay a divisor of the 8 XCDs.
+// ------------------------------------------------------------ schedule
+
+constexpr int XCDS = 8;       // workgroup b runs on XCD b % 8
+constexpr int XCD_CUS = 32;   // CUs per XCD: one round of items per XCD
+constexpr int GROUP = 32;     // tiles per group (one round on one XCD)
+constexpr int64_t MIN_PIECE = 4 * KS;  // shortest token piece of the last round
+
+struct Tile {
+  int kind, I, J;
+};
+
+// Tiles in bands of 8 tile rows; inside a band column by column, so 32
+// consecutive tiles form an 8 x 4 block (lower: clipped at the diagonal).
+void band_order(std::vector<Tile>& out, int kind, int nt, bool lower) {
+  for (int u0 = 0; u0 < nt; u0 += 8) {
+    const int u1 = std::min(u0 + 8, nt);
+    const int jn = lower ? u1 : nt;
+    for (int J = 0; J < jn; ++J)
+      for (int I = lower ? std::max(u0, J) : u0; I < u1; ++I) out.push_back({kind, I, J});
+  }
+}
+
+struct CovSchedule {
+  std::vector<CovItem> items;  // by blockIdx
+  std::vector<CovRed> reds;    // tiles with partials
+  int64_t slots = 0;
+};
+
+int choose_split(int64_t tiles) {
+  // One token range per tile when the tiles fill at least one round of the
+  // chip (the last round is balanced by pieces); smaller problems split the
+  // tokens for at least ~4 items per CU, at most 8 ways.
+  if (tiles >= XCDS * XCD_CUS) return 1;
   int s = 1;
   while (s < 8 && tiles * s < 1024) s *= 2;
   return s;
 }
 
-int cov_tiles(int64_t d_in, int64_t d_out, bool hx, bool d, bool hg) {
-  const int64_t ti = cdiv(d_in, CT), to = cdiv(d_out, CT);
-  int64_t n = 0;
-  if (hx) n += ti * (ti + 1) / 2;
-  if (d) n += ti * ti;
-  if (hg) n += to * (to + 1) / 2;
-  return int(n);
+CovSchedule build_schedule(int64_t n_tok, int64_t d_in, int64_t d_out, bool hx, bool d, bool hg) {
+  std::vector<Tile> tiles;
+  const int ti = int(cdiv(d_in, CT)), to = int(cdiv(d_out, CT));
+  if (hx) band_order(tiles, K_HX, ti, true);
+  if (d) band_order(tiles, K_D, ti, false);
+  if (hg) band_order(tiles, K_HG, to, true);
+  CovSchedule S;
+  const int64_t T = int64_t(tiles.size());
+  if (T == 0) return S;
+  int ns = choose_split(T);
+  while (ns > 1 && cdiv(n_tok, ns) < KS) ns /= 2;
+  const int64_t chunk = cdiv(cdiv(n_tok, ns), KS) * KS;
+  auto range = [&](int s, int64_t& t0, int64_t& t1) {
+    t0 = std::min<int64_t>(n_tok, s * chunk);
+    t1 = std::min<int64_t>(n_tok, t0 + chunk);
+  };
+  const int64_t G = cdiv(T, GROUP);
+  const int64_t Q = G * ns;          // group-splits
+  const int64_t R = Q / XCDS;        // full rounds
+  struct Raw {
+    int tile;
+    int64_t t0, t1;
+  };
+  std::vector<Raw> raw;  // by blockIdx, tile -1 = idle
+  raw.assign(size_t(R * XCDS * XCD_CUS), Raw{-1, 0, 0});
+  for (int64_t j = 0; j < R * XCDS; ++j) {
+    const int64_t g = j / ns;
+    const int s = int(j % ns);
+    const int64_t x = j % XCDS, round = j / XCDS;
+    for (int k = 0; k < GROUP; ++k) {
+      const int64_t tile = g * GROUP + k;
+      if (tile >= T) continue;
+      Raw r{int(tile), 0, 0};
+      range(s, r.t0, r.t1);
+      raw[size_t(XCDS * (round * XCD_CUS + k) + x)] = r;
+    }
+  }
+  // last partial round: cut the remaining items into pieces over every CU
+  std::vector<Raw> left;
+  for (int64_t j = R * XCDS; j < Q; ++j) {
+    const int64_t g = j / ns;
+    const int s = int(j % ns);
+    for (int k = 0; k < GROUP; ++k) {
+      const int64_t tile = g * GROUP + k;
+      if (tile >= T) continue;
+      Raw r{int(tile), 0, 0};
+      range(s, r.t0, r.t1);
+      left.push_back(r);
+    }
+  }
+  if (!left.empty()) {
+    const int64_t L = int64_t(left.size());
+    const int64_t len = left[0].t1 - left[0].t0;
+    int64_t f = std::max<int64_t>(1, (XCDS * XCD_CUS) / L);
+    f = std::max<int64_t>(1, std::min<int64_t>(f, len / MIN_PIECE));
+    const int64_t plen = cdiv(cdiv(len, f), KS) * KS;
+    std::vector<Raw> pieces;
+    for (const Raw& r : left)
+      for (int64_t p = 0; p < f; ++p) {
+        const int64_t t0 = std::min(r.t1, r.t0 + p * plen);
+        const int64_t t1 = std::min(r.t1, t0 + plen);
+        if (t0 < t1 || p == 0) pieces.push_back(Raw{r.tile, t0, t1});
+      }
+    // piece q -> XCD q % 8, in order within each XCD
+    const int64_t base = int64_t(raw.size());
+    const int64_t nrow = cdiv(int64_t(pieces.size()), XCDS);
+    raw.resize(size_t(base + nrow * XCDS), Raw{-1, 0, 0});
+    for (int64_t q = 0; q < int64_t(pieces.size()); ++q) raw[size_t(base + q)] = pieces[size_t(q)];
+  }
+  // items per tile: direct if one item covers all tokens, else pool slots
+  std::vector<std::vector<int64_t>> per_tile(static_cast<size_t>(T));
+  for (int64_t b = 0; b < int64_t(raw.size()); ++b)
+    if (raw[size_t(b)].tile >= 0) per_tile[size_t(raw[size_t(b)].tile)].push_back(b);
+  S.items.assign(raw.size(), CovItem{-1, 0, 0, -1, 0, 0});
+  for (int64_t tix = 0; tix < T; ++tix) {
+    const Tile& tl = tiles[size_t(tix)];
+    const auto& bs = per_tile[size_t(tix)];
+    const bool direct = bs.size() == 1 && raw[size_t(bs[0])].t0 == 0 && raw[size_t(bs[0])].t1 == n_tok;
+    if (!direct) S.reds.push_back(CovRed{tl.kind, tl.I, tl.J, int32_t(bs.size()), S.slots});
+    for (int64_t b : bs) {
+      const Raw& r = raw[size_t(b)];
+      S.items[size_t(b)] = CovItem{tl.kind, tl.I, tl.J, direct ? -1 : int32_t(S.slots++), r.t0, r.t1};
+    }
+  }
+  return S;
+}
+
+size_t sched_bytes(const CovSchedule& S) {
+  Arena ar{nullptr, 0, 0};
+  ar.take<CovItem>(S.items.size());
+  ar.take<CovRed>(S.reds.size());
+  ar.take<float>(size_t(S.slots) * CT * CT);
+  return ar.used;
 }
 
 }  // namespace
@@ -459,13 +573,7 @@ size_t cov_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out, kq_dtype dt, boo
     return ar.used;
   }
   if (d) ar.take<uint16_t>(size_t(n_tok) * d_in);  // bf16 drift
-  const int tiles = cov_tiles(d_in, d_out, hx, d, hg);
-  const int ns = choose_split(tiles);
-  if (ns > 1) {
-    const size_t per = (hx ? d_in * d_in : 0) + (d ? d_in * d_in : 0) + (hg ? d_out * d_out : 0);
-    ar.take<float>(per * ns);
-  }
-  return ar.used;
+  return ar.used + 256 + sched_bytes(build_schedule(n_tok, d_in, d_out, hx, d, hg));
 }
 
 kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int64_t n_tok,
@@ -496,6 +604,8 @@ kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int
     return mark_kernel(KQ_OP_ACCUMULATE_COV, 1, s);
   }
 
+  const CovSchedule S = build_schedule(n_tok, d_in, d_out, HX != nullptr, D != nullptr, HG != nullptr);
+  if (S.items.empty()) return KQ_OK;
   CovArgs a{};
   a.Xq = static_cast<const uint16_t*>(Xq);
   if (D) {
@@ -507,8 +617,17 @@ kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int
     KQ_HIP(hipGetLastError());
     a.dX = dx;
   }
+  CovItem* items = ws.take<CovItem>(S.items.size());
+  CovRed* reds = ws.take<CovRed>(S.reds.size());
+  float* pool = ws.take<float>(size_t(S.slots) * CT * CT);
+  if (!items || (!S.reds.empty() && !reds) || (S.slots && !pool))
+    return fail(KQ_ERR_WORKSPACE, "accumulate_cov: workspace too small");
+  KQ_HIP(hipMemcpyAsync(items, S.items.data(), S.items.size() * sizeof(CovItem),
+                        hipMemcpyHostToDevice, s));
+  if (!S.reds.empty())
+    KQ_HIP(hipMemcpyAsync(reds, S.reds.data(), S.reds.size() * sizeof(CovRed),
+                          hipMemcpyHostToDevice, s));
   a.G = static_cast<const uint16_t*>(G);
-  a.n_tok = n_tok;
   a.d_in = d_in;
   a.d_out = d_out;
   a.alpha = alpha;
@@ -516,48 +635,18 @@ kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int
   a.out[0] = HX;
   a.out[1] = D;
   a.out[2] = HG;
-  a.nt_in = int(cdiv(d_in, CT));
-  a.nt_out = int(cdiv(d_out, CT));
-  a.tasks[0] = HX ? a.nt_in * (a.nt_in + 1) / 2 : 0;
-  a.tasks[1] = D ? a.nt_in * a.nt_in : 0;
-  a.tasks[2] = HG ? a.nt_out * (a.nt_out + 1) / 2 : 0;
-  const int tiles = a.tasks[0] + a.tasks[1] + a.tasks[2];
-  if (tiles == 0) return KQ_OK;
-  int ns = choose_split(tiles);
-  // each split needs at least one stage of tokens
-  while (ns > 1 && cdiv(n_tok, ns) < KS) ns /= 2;
-  a.nsplit = ns;
-  a.tok_chunk = cdiv(cdiv(n_tok, ns), KS) * KS;
-  if (ns > 1) {
-    int64_t off = 0;
-    a.part_off[0] = off;
-    if (HX) off += d_in * d_in;
-    a.part_off[1] = off;
-    if (D) off += d_in * d_in;
-    a.part_off[2] = off;
-    if (HG) off += d_out * d_out;
-    a.part_stride = off;
-    a.part = ws.take<float>(size_t(off) * ns);
-    if (!a.part) return fail(KQ_ERR_WORKSPACE, "accumulate_cov: workspace too small");
-  }
+  a.items = items;
+  a.pool = pool;
   KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(cov_bf16_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(COV_LDS)));
   KQ_TRY(mark_kernel(KQ_OP_ACCUMULATE_COV, 0, s));
-  cov_bf16_kernel<<<unsigned(tiles * ns), 256, COV_LDS, s>>>(a);
+  cov_bf16_kernel<<<unsigned(S.items.size()), 256, COV_LDS, s>>>(a);
   KQ_HIP(hipGetLastError());
   KQ_TRY(mark_kernel(KQ_OP_ACCUMULATE_COV, 1, s));
-  if (ns > 1) {
-    float* outs[3] = {HX, D, HG};
-    const int64_t dims[3] = {d_in, d_in, d_out};
-    for (int k = 0; k < 3; ++k) {
-      if (!outs[k]) continue;
-      const int nt = int(cdiv(dims[k], 64));
-      const int sym = k != 1;
-      const int blocks = sym ? nt * (nt + 1) / 2 : nt * nt;
-      cov_reduce_kernel<<<unsigned(blocks), 256, 0, s>>>(a.part + a.part_off[k], a.part_stride, ns,
-                                                         outs[k], dims[k], alpha, beta, sym, nt);
-      KQ_HIP(hipGetLastError());
-    }
+  if (!S.reds.empty()) {
+    cov_pool_reduce_kernel<<<unsigned(S.reds.size() * 16), 256, 0, s>>>(reds, pool, HX, D, HG, d_in,
+                                                                     d_out, alpha, beta);
+    KQ_HIP(hipGetLastError());
   }
   return KQ_OK;
 }

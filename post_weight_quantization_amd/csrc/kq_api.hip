@@ -109,7 +109,9 @@ kq_status kq_workspace_size(kq_op op, int64_t d_out, int64_t d_in, int64_t n_tok
     case KQ_OP_ACCUMULATE_COV:
       if (d_out < 1 || n_tok < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
       if (dtype != KQ_BF16 && dtype != KQ_F32) return fail(KQ_ERR_ARG, "workspace_size: bad dtype");
-      *bytes = cov_ws_bytes(n_tok, d_in, d_out, dtype, true, true, true);
+      // the largest need over every subset of outputs a call may request
+      for (int m = 1; m < 8; ++m)
+        *bytes = std::max(*bytes, cov_ws_bytes(n_tok, d_in, d_out, dtype, m & 1, m & 2, m & 4));
       return KQ_OK;
     case KQ_OP_BIIP:
       if (d_out < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
