@@ -182,9 +182,20 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
   const int t = threadIdx.x;
   const int w = t >> 6;
   float* base = A + k0 * n + k0;
-  for (int e = t; e < NB * NB / 4; e += 256) {
-    const int r = e >> 5, c = (e & 31) * 4;
-    *reinterpret_cast<float4*>(As + r * LS + c) = *reinterpret_cast<const float4*>(base + r * n + c);
+  {
+    // the diagonal block: 16 float4 loads per thread, all in flight together
+    constexpr int NV = NB * NB / 4 / 256;
+    float4 v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int e = t + 256 * k;
+      v[k] = *reinterpret_cast<const float4*>(base + (e >> 5) * n + (e & 31) * 4);
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int e = t + 256 * k;
+      *reinterpret_cast<float4*>(As + (e >> 5) * LS + (e & 31) * 4) = v[k];
+    }
   }
   for (int e = t; e < NB * LS; e += 256) Xs[e] = 0.f;
   __syncthreads();

@@ -74,14 +74,16 @@ constexpr int PR = 32;
 constexpr int USEG = 20;            // floats per lane segment of a staged U row
 constexpr int UROW = 8 * USEG;      // floats per staged U row
 
+// v + (v of another lane); with bound_ctrl set the move can fold into the
+// add as a DPP source operand (one instruction per level)
 __device__ inline float dpp_add(float v, int ctrl_sel) {
   switch (ctrl_sel) {
     case 0:  // quad_perm [1,0,3,2]
-      return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+      return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
     case 1:  // quad_perm [2,3,0,1]
-      return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+      return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
     default:  // row_half_mirror: lane i <-> 7 - i within each 8 lanes
-      return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+      return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
   }
 }
 
@@ -91,7 +93,12 @@ __device__ inline float group8_sum(float v) {
   return dpp_add(v, 2);
 }
 
-constexpr size_t PANEL_LDS = sizeof(float) * (size_t(BK) * UROW + BK + 2 * PR * BK) + PR * BK;
+// per-row strides of the staged errors (floats) and codes (bytes): padded so
+// the owners of one column in 8 rows write 8 different banks
+constexpr int ESTR = BK + 4;
+constexpr int CSTR = BK + 16;  // keeps 16-byte row alignment
+constexpr size_t PANEL_LDS =
+    sizeof(float) * (size_t(BK) * UROW + BK + PR * BK + PR * ESTR) + PR * CSTR;
 
 __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wbar,
                                                     const float* __restrict__ U,
@@ -104,15 +111,33 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
   float* Us = sm;                 // [p][c][j] = U[blk0 + p][blk0 + 16 c + j] if 16 c + j > p, else 0
   float* uinv = Us + BK * UROW;   // 1 / U_pp
   float* Wo = uinv + BK;          // PR x BK staged W^
-  float* Eo = Wo + PR * BK;       // PR x BK staged errors
-  uint8_t* Co = reinterpret_cast<uint8_t*>(Eo + PR * BK);  // PR x BK codes
+  float* Eo = Wo + PR * BK;       // PR x BK staged errors (row stride ESTR)
+  uint8_t* Co = reinterpret_cast<uint8_t*>(Eo + PR * ESTR);  // PR x BK codes (row stride CSTR)
   const int t = threadIdx.x;
-  for (int e = t; e < BK * BK; e += 256) {
-    const int p = e >> 7, m = e & 127;
-    const float v = m > p ? U[(blk0 + p) * n + blk0 + m] : 0.f;
-    Us[p * UROW + (m >> 4) * USEG + (m & 15)] = v;
+  {
+    // U's diagonal block: 16 float4 loads per thread, all in flight together
+    constexpr int NV = BK * BK / 4 / 256;
+    float4 v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int e4 = t + 256 * k;
+      const int p = e4 >> 5, m = (e4 & 31) * 4;
+      v[k] = *reinterpret_cast<const float4*>(U + (blk0 + p) * n + blk0 + m);
+    }
+    const float ud = t < BK ? U[(blk0 + t) * n + blk0 + t] : 1.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int e4 = t + 256 * k;
+      const int p = e4 >> 5, m = (e4 & 31) * 4;
+      float4 x = v[k];
+      x.x = m > p ? x.x : 0.f;
+      x.y = m + 1 > p ? x.y : 0.f;
+      x.z = m + 2 > p ? x.z : 0.f;
+      x.w = m + 3 > p ? x.w : 0.f;
+      *reinterpret_cast<float4*>(Us + p * UROW + (m >> 4) * USEG + (m & 15)) = x;
+    }
+    if (t < BK) uinv[t] = 1.f / ud;
   }
-  if (t < BK) uinv[t] = 1.f / U[(blk0 + t) * n + blk0 + t];
 
   const int lane = t & 63;
   const int c = lane & 7;
@@ -121,8 +146,7 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
   const bool valid = row < d_out;
   const int64_t rr = valid ? row : d_out - 1;
   const float* wsrc = Wbar + rr * n + blk0 + 16 * c;
-  float w[16], ev[16];
-  uint32_t cw[4];
+  float w[16];
 #pragma unroll
   for (int j = 0; j < 16; j += 4) {
     const float4 v = *reinterpret_cast<const float4*>(wsrc + j);
@@ -131,10 +155,6 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
     w[j + 2] = v.z;
     w[j + 3] = v.w;
   }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) ev[j] = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) cw[k] = 0u;
 
   float sc, zr;
   if (grouped) {
@@ -170,8 +190,23 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
   const float isc = 1.f / sc;
   __syncthreads();
 
-  // U row p for this lane (16 entries) and 1 / U_pp, fetched one step ahead
-  auto fetch = [&](int p, float (&u)[16], float& ui) {
+  // 1 / U_pp and the superdiagonal U_{p,p+1} of this lane's own 16 columns:
+  // only the lane owning column p uses them, and they stay in registers so
+  // the dependent chain of a step (quantize -> scaled error -> row sum ->
+  // next candidate) never waits for LDS
+  float uiv[16], sup[15];
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(uinv + 16 * c + j);
+    uiv[j] = v.x;
+    uiv[j + 1] = v.y;
+    uiv[j + 2] = v.z;
+    uiv[j + 3] = v.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 15; ++j) sup[j] = Us[(16 * c + j) * UROW + c * USEG + j + 1];
+  // U row p for this lane (16 entries), fetched one step ahead
+  auto fetch = [&](int p, float (&u)[16]) {
     const float* up = Us + p * UROW + c * USEG;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
@@ -181,10 +216,11 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
       u[4 * k4 + 2] = v.z;
       u[4 * k4 + 3] = v.w;
     }
-    ui = uinv[p];
   };
-  float ua[16], ub[16], uia, uib;
-  fetch(0, ua, uia);
+  float ua[16], ub[16];
+  fetch(0, ua);
+  float* erow = Eo + rloc * ESTR;
+  uint8_t* crow = Co + rloc * CSTR;
 #pragma unroll 1
   for (int c0 = 0; c0 < 8; ++c0) {
     const bool own = c == c0;
@@ -193,33 +229,33 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
       const int p = 16 * c0 + j0;
       float(&ucur)[16] = (j0 & 1) ? ub : ua;
       float(&unxt)[16] = (j0 & 1) ? ua : ub;
-      const float ui = (j0 & 1) ? uib : uia;
-      float& uin = (j0 & 1) ? uia : uib;
-      if (p + 1 < BK) fetch(p + 1, unxt, uin);
+      // zero on the lanes not owning column p, so their scaled error is 0
+      // without a select on the dependent chain
+      const float ui = own ? uiv[j0] : 0.f;
+      if (p + 1 < BK) fetch(p + 1, unxt);
       const float x = w[j0];
-      const float q = fminf(fmaxf(rintf(x * isc) + zr, 0.f), maxq);
+      const float q = __builtin_amdgcn_fmed3f(rintf(x * isc) + zr, 0.f, maxq);
       const float wq = sc * (q - zr);
       const float el = (x - wq) * ui;
-      const float e = group8_sum(own ? el : 0.f);
-      w[j0] = own ? wq : w[j0];
-      ev[j0] = own ? el : ev[j0];
-      cw[j0 >> 2] |= own ? (uint32_t(q) << (8 * (j0 & 3))) : 0u;
-      // the next step's candidate first, then the rest of the row
-      if (j0 + 1 < 16) w[j0 + 1] -= e * ucur[j0 + 1];
+      const float e = group8_sum(el);
+      if (own) {
+        w[j0] = wq;
+        erow[p] = el;
+        crow[p] = uint8_t(q);
+      }
+      // the owner's next candidate from the register superdiagonal, then
+      // the rest of the row from the LDS copy of U row p
+      if (j0 + 1 < 16) w[j0 + 1] -= e * (own ? sup[j0] : 0.f);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (j == j0 + 1) continue;
-        w[j] -= e * ucur[j];
+        if (j == j0 + 1) w[j] -= e * (own ? 0.f : ucur[j]);
+        else w[j] -= e * ucur[j];
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 16; j += 4) {
+  for (int j = 0; j < 16; j += 4)
     *reinterpret_cast<float4*>(Wo + rloc * BK + 16 * c + j) = make_float4(w[j], w[j + 1], w[j + 2], w[j + 3]);
-    *reinterpret_cast<float4*>(Eo + rloc * BK + 16 * c + j) =
-        make_float4(ev[j], ev[j + 1], ev[j + 2], ev[j + 3]);
-  }
-  *reinterpret_cast<uint4*>(Co + rloc * BK + 16 * c) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
   __syncthreads();
   const int64_t rows_here = min<int64_t>(PR, d_out - int64_t(blockIdx.x) * PR);
   for (int e = t; e < PR * BK / 4; e += 256) {
@@ -228,14 +264,14 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
     const int64_t grow = int64_t(blockIdx.x) * PR + r;
     *reinterpret_cast<float4*>(Wout + grow * n + blk0 + col) =
         *reinterpret_cast<const float4*>(Wo + r * BK + col);
-    *reinterpret_cast<float4*>(E + grow * ldE + col) = *reinterpret_cast<const float4*>(Eo + r * BK + col);
+    *reinterpret_cast<float4*>(E + grow * ldE + col) = *reinterpret_cast<const float4*>(Eo + r * ESTR + col);
   }
   for (int e = t; e < PR * BK / 16; e += 256) {
     const int r = e >> 3, col = (e & 7) * 16;
     if (r >= rows_here) continue;
     const int64_t grow = int64_t(blockIdx.x) * PR + r;
     *reinterpret_cast<uint4*>(codes + grow * n + blk0 + col) =
-        *reinterpret_cast<const uint4*>(Co + r * BK + col);
+        *reinterpret_cast<const uint4*>(Co + r * CSTR + col);
   }
 }
 
