@@ -377,7 +377,8 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
     if (m <= 0) break;
     float* panel = A + (k0 + NB) * n + k0;
     // panel <- panel * Dinv_k^T   (in place: each tile reads its rows before writing them)
-    GemmArgs gt = gemm_args(panel, n, Dinv + k * NB * NB, NB, panel, n, m, NB, NB, 1.f, 0.f, G_TRANS_B);
+    GemmArgs gt = gemm_args(panel, n, Dinv + k * NB * NB, NB, panel, n, m, NB, NB, 1.f, 0.f,
+                            G_TRANS_B | G_C_ALIASES_A);
     KQ_TRY(gemm_f32(gt, s));
     // trailing lower triangle -= panel panel^T
     float* trail = A + (k0 + NB) * n + (k0 + NB);

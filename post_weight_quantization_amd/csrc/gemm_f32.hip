@@ -6,12 +6,13 @@
 // operands restrict each tile's K range and are masked at load, so the
 // algorithmic (triangle-aware) flop counts are what the kernel executes.
 //
-// Tiling: 128 x 128 output tile per workgroup of 4 waves (2 x 2), each wave a
-// 64 x 64 sub-tile held as 2 x 2 v_mfma_f32_32x32x2_f32 accumulators
-// (64 AGPRs/lane). K advances 16 per stage through double-buffered LDS stored
-// k-major, so the MFMA operand reads (32 consecutive m or n per k) are
-// conflict-free. Global loads are float4; all callers pass 16-byte aligned
-// pointers and leading dimensions that are multiples of 4.
+// Tiling: T x T output tile per workgroup of 4 waves (2 x 2), T = 128 (each
+// wave 64 x 64 as 2 x 2 v_mfma_f32_32x32x2_f32 accumulators) or T = 64 for
+// problems whose 128-tile grid would leave CUs idle (each wave one 32 x 32
+// block). K advances 16 per stage through double-buffered LDS stored k-major,
+// so the MFMA operand reads (32 consecutive m or n per k) are conflict-free.
+// Global loads are float4; all callers pass 16-byte aligned pointers and
+// leading dimensions that are multiples of 4.
 #include "kq_internal.h"
 
 namespace kq {
@@ -20,20 +21,22 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int TM = 128;
-constexpr int TN = 128;
 constexpr int TK = 16;
-constexpr int LDSP = TM + 4;  // padded LDS row (floats)
 
+template <int T>
 struct Stage {
-  float4 a[2];
-  float4 b[2];
+  float4 a[T / 64];
+  float4 b[T / 64];
 };
 
 __device__ inline float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-template <bool TA, bool TB>
+template <bool TA, bool TB, int T>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+  constexpr int TM = T, TN = T;
+  constexpr int LDSP = T + 4;   // padded LDS row (floats)
+  constexpr int H = T / 64;     // float4 loads per operand per thread per stage
+  constexpr int FD = T / 64;    // 32 x 32 MFMA blocks per wave and dimension
   const int z = blockIdx.z;
   const float* __restrict__ A = g.A + z * g.strideA;
   const float* __restrict__ B = g.B + z * g.strideB;
@@ -88,25 +91,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
-  const int wm = (w >> 1) * 64;
-  const int wn = (w & 1) * 64;
+  const int wm = (w >> 1) * (T / 2);
+  const int wn = (w & 1) * (T / 2);
   const int lr = lane & 31;
   const int lk = lane >> 5;
 
   // load coordinates
-  // non-transposed A / transposed B: one row (m or n) per thread pair, 8 k's
-  const int r_row = t >> 1;
-  const int r_k = (t & 1) * 8;
-  // transposed A / non-transposed B: one k per 16 threads, 8 m's (or n's)
+  // non-transposed A / transposed B: one row (m or n) per 256/T threads,
+  // T/16 consecutive k's each
+  const int r_row = t / (256 / T);
+  const int r_k = (t % (256 / T)) * (T / 16);
+  // transposed A / non-transposed B: one k per 16 threads, T/16 m's (or n's)
   const int c_k = t >> 4;
-  const int c_col = (t & 15) * 8;
+  const int c_col = (t & 15) * (T / 16);
 
-  auto load = [&](int64_t k0, Stage& st) {
+  auto load = [&](int64_t k0, Stage<T>& st) {
     // A
     if (!TA) {
       const int64_t m = m0 + r_row;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < H; ++h) {
         const int64_t k = k0 + r_k + 4 * h;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (m < g.M && k < khi) v = ld4(A + m * g.lda + k);
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     } else {
       const int64_t k = k0 + c_k;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < H; ++h) {
         const int64_t m = m0 + c_col + 4 * h;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (m < g.M && k < khi) v = ld4(A + k * g.lda + m);
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     if (!TB) {
       const int64_t k = k0 + c_k;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < H; ++h) {
         const int64_t n = n0 + c_col + 4 * h;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (n < g.N && k < khi) v = ld4(B + k * g.ldb + n);
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     } else {
       const int64_t n = n0 + r_row;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < H; ++h) {
         const int64_t k = k0 + r_k + 4 * h;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (n < g.N && k < khi) v = ld4(B + n * g.ldb + k);
@@ -158,11 +162,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   const bool amask = fl & (G_A_UPPER | G_A_LOWER | G_A_SUPPER);
   const bool bmask = fl & (G_B_UPPER | G_B_LOWER);
 
-  auto store = [&](int64_t k0, const Stage& st, int buf) {
+  auto store = [&](int64_t k0, const Stage<T>& st, int buf) {
     if (!TA) {
       const int64_t m = m0 + r_row;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < H; ++h) {
         float e[4] = {st.a[h].x, st.a[h].y, st.a[h].z, st.a[h].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     } else {
       const int kk = c_k;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < H; ++h) {
         float e[4] = {st.a[h].x, st.a[h].y, st.a[h].z, st.a[h].w};
         if (amask) {
 #pragma unroll
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     if (!TB) {
       const int kk = c_k;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < H; ++h) {
         float e[4] = {st.b[h].x, st.b[h].y, st.b[h].z, st.b[h].w};
         if (bmask) {
 #pragma unroll
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     } else {
       const int64_t n = n0 + r_row;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < H; ++h) {
         float e[4] = {st.b[h].x, st.b[h].y, st.b[h].z, st.b[h].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -211,16 +215,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[FD][FD];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FD; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FD; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   if (klo < khi) {
-    Stage st;
+    Stage<T> st;
     load(klo, st);
     store(klo, st, 0);
     __syncthreads();
@@ -230,14 +234,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       if (more) load(k0 + TK, st);
 #pragma unroll
       for (int kk = 0; kk < TK; kk += 2) {
-        const float a0 = As[buf][kk + lk][wm + lr];
-        const float a1 = As[buf][kk + lk][wm + 32 + lr];
-        const float b0 = Bs[buf][kk + lk][wn + lr];
-        const float b1 = Bs[buf][kk + lk][wn + 32 + lr];
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        float a[FD], b[FD];
+#pragma unroll
+        for (int i = 0; i < FD; ++i) a[i] = As[buf][kk + lk][wm + 32 * i + lr];
+#pragma unroll
+        for (int j = 0; j < FD; ++j) b[j] = Bs[buf][kk + lk][wn + 32 * j + lr];
+#pragma unroll
+        for (int i = 0; i < FD; ++i)
+#pragma unroll
+          for (int j = 0; j < FD; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
       }
       if (more) store(k0 + TK, st, buf ^ 1);
       __syncthreads();
@@ -248,9 +254,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   // epilogue: acc[i][j][r] is element (wm + 32i + 8(r/4) + 4 lk + r%4, wn + 32j + lr)
   const float alpha = g.alpha, beta = g.beta;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FD; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FD; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
@@ -306,12 +312,28 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
     return fail(KQ_ERR_SHAPE, "internal gemm: leading dimensions and K must be multiples of 4");
   if ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) & 15)
     return fail(KQ_ERR_ARG, "internal gemm: operands must be 16-byte aligned");
-  dim3 grid(unsigned(cdiv(g.N, TN)), unsigned(cdiv(g.M, TM)), unsigned(g.batch > 0 ? g.batch : 1));
+  const int64_t nb = g.batch > 0 ? g.batch : 1;
+  // 128-wide tiles unless they would give fewer than ~2 workgroups per CU
+  // (256 CUs); output-triangle flags halve the live tiles
+  int64_t live = cdiv(g.N, 128) * cdiv(g.M, 128) * nb;
+  if (g.flags & (G_OUT_LOWER | G_OUT_UPPER | G_OUT_SUPPER)) live /= 2;
+  if ((g.flags & G_C_ALIASES_A) && g.N > 128)
+    return fail(KQ_ERR_SHAPE, "internal gemm: an in-place product needs N <= 128");
+  const bool small = live < 512 && !((g.flags & G_C_ALIASES_A) && g.N > 64);
+  const int T = small ? 64 : 128;
+  dim3 grid(unsigned(cdiv(g.N, T)), unsigned(cdiv(g.M, T)), unsigned(nb));
   const bool ta = g.flags & G_TRANS_A, tb = g.flags & G_TRANS_B;
-  if (!ta && !tb) gemm_f32_kernel<false, false><<<grid, 256, 0, s>>>(g);
-  else if (!ta && tb) gemm_f32_kernel<false, true><<<grid, 256, 0, s>>>(g);
-  else if (ta && !tb) gemm_f32_kernel<true, false><<<grid, 256, 0, s>>>(g);
-  else gemm_f32_kernel<true, true><<<grid, 256, 0, s>>>(g);
+  if (small) {
+    if (!ta && !tb) gemm_f32_kernel<false, false, 64><<<grid, 256, 0, s>>>(g);
+    else if (!ta && tb) gemm_f32_kernel<false, true, 64><<<grid, 256, 0, s>>>(g);
+    else if (ta && !tb) gemm_f32_kernel<true, false, 64><<<grid, 256, 0, s>>>(g);
+    else gemm_f32_kernel<true, true, 64><<<grid, 256, 0, s>>>(g);
+  } else {
+    if (!ta && !tb) gemm_f32_kernel<false, false, 128><<<grid, 256, 0, s>>>(g);
+    else if (!ta && tb) gemm_f32_kernel<false, true, 128><<<grid, 256, 0, s>>>(g);
+    else if (ta && !tb) gemm_f32_kernel<true, false, 128><<<grid, 256, 0, s>>>(g);
+    else gemm_f32_kernel<true, true, 128><<<grid, 256, 0, s>>>(g);
+  }
   KQ_HIP(hipGetLastError());
   return KQ_OK;
 }

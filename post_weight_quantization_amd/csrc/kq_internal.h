@@ -66,6 +66,9 @@ enum GemmFlag : uint32_t {
   G_ORDER_NDESC = 1u << 12,  // column tiles in descending order
   G_ORDER_MDESC = 1u << 13,  // row tiles in descending order
   G_ORDER_DIAG = 1u << 14,   // by (column tile - row tile), descending
+  // C aliases A (in place): every tile must span all N columns so that it
+  // reads its rows of A before any tile writes them (requires N <= 128)
+  G_C_ALIASES_A = 1u << 15,
 };
 
 struct GemmArgs {
