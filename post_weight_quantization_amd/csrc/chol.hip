@@ -47,14 +47,13 @@ __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, cons
 // Factor the NB x NB diagonal block at (k0, k0) of A (ld n) in place (lower,
 // zeros written above the diagonal) and write its inverse to Dinv (NB x NB,
 // zeros above the diagonal). One workgroup of 4 waves; the block lives in LDS.
-//  * four 32-column panels; panel p is factored by wave 0 alone with rows
-//    lane and lane+64 in registers (column j is published to the other lanes
-//    through LDS, so no workgroup barrier sits inside the 32 column steps);
-//  * the rank-32 update of the trailing lower triangle runs on all 256
-//    threads with 4 x 4 register blocks;
-//  * the four 32 x 32 diagonal inverses are formed in parallel (one wave
-//    each, one column per lane by forward substitution), then the off-
-//    diagonal blocks X_ip = -X_ii sum_k L_ik X_kp, block row by block row.
+// Per 32-column panel:
+//  * wave 0 factors the 32 x 32 diagonal block and inverts it in registers
+//    (leaf_diag32), with no barrier or LDS access inside the 32 column steps;
+//  * all 256 threads solve the rows below as a product with the inverse
+//    (L21 = A21 L11^-T), then take the rank-32 update of the trailing lower
+//    triangle with 4 x 4 register blocks;
+// then the off-diagonal blocks of the inverse X_ip = -X_ii sum_k L_ik X_kp.
 constexpr int LS = NB + 4;  // LDS row stride (floats), keeps float4 alignment
 
 __device__ inline float lane_value(float v, int lane) {
@@ -66,52 +65,90 @@ __device__ inline void wave_lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-__device__ void leaf_panel(float* As, float* colbuf, int64_t k0, int* info, int P) {
-  const int C0 = 32 * P;
-  const int CS = C0 >> 6, CL = C0 & 63;  // register set / first lane of the diagonal block rows
+// Cholesky of the 32 x 32 block at (C0, C0) of As and its inverse, in
+// registers. Wave 0 only: lane r (and its copy r + 32) holds row r of the
+// block (x) and row r of Y, which starts as the identity. Step j eliminates
+// column j from the rows below with multipliers x_r[j] / piv_j (row j's
+// entries come from column j by symmetry) and applies the same row
+// operations to Y, so that at the end Y = L_u^-1 for A = L_u D L_u^T.
+// Then L = L_u D^(1/2): L[r][j] = x_r[j] / sqrt(piv_j), and
+// L^-1 = D^(-1/2) Y. Broadcasts are readlanes; nothing on the step's
+// dependent chain goes through LDS.
+__device__ void leaf_diag32(float* As, float* Xs, int64_t k0, int* info, int C0) {
   const int lane = threadIdx.x & 63;
-  float ra[32], rb[32];
+  const int r = lane & 31;
+  float x[32], y[32], dv[32];
+  const float* row = As + (C0 + r) * LS + C0;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    ra[k] = As[lane * LS + C0 + k];
-    rb[k] = As[(lane + 64) * LS + C0 + k];
+  for (int k = 0; k < 32; k += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(row + k);
+    x[k] = v.x;
+    x[k + 1] = v.y;
+    x[k + 2] = v.z;
+    x[k + 3] = v.w;
   }
+#pragma unroll
+  for (int k = 0; k < 32; ++k) y[k] = k == r ? 1.f : 0.f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
-    const int R = C0 + j;  // pivot row (compile-time after unrolling)
-    float piv = lane_value((R >> 6) ? rb[j] : ra[j], R & 63);
+    float piv = lane_value(x[j], j);
     if (!(piv > 0.f)) {  // non-positive or NaN pivot
-      if (lane == 0) atomicMin(info, int(k0 + R) + 1);
+      if (lane == 0) atomicMin(info, int(k0 + C0 + j) + 1);
       piv = 1.f;
     }
-    const float d = __builtin_amdgcn_sqrtf(piv);  // 1-ulp hardware square root
-    const float rinv = __builtin_amdgcn_rcpf(d);
-    ra[j] = lane > R ? ra[j] * rinv : (lane == R ? d : ra[j]);
-    rb[j] = lane + 64 > R ? rb[j] * rinv : (lane + 64 == R ? d : rb[j]);
-    // column j of the diagonal block, below the pivot, to every lane
-    const int kk = lane - CL;
-    if (kk >= 0 && kk < 32) colbuf[kk] = kk > j ? (CS ? rb[j] : ra[j]) : 0.f;
-    wave_lds_fence();
+    const float ip = __builtin_amdgcn_rcpf(piv);
+    const float mm = r > j ? x[j] * ip : 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (4 * q + 3 <= j) continue;  // every column of this chunk is finished
-      const float4 v = *reinterpret_cast<const float4*>(colbuf + 4 * q);
-      const float cv[4] = {v.x, v.y, v.z, v.w};
+    for (int k = j + 1; k < 32; ++k) x[k] = __builtin_fmaf(-mm, lane_value(x[j], k), x[k]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = 4 * q + u;
-        if (k <= j) continue;
-        ra[k] -= ra[j] * cv[u];
-        rb[k] -= rb[j] * cv[u];
+    for (int k = 0; k <= j; ++k) y[k] = __builtin_fmaf(-mm, lane_value(y[k], j), y[k]);
+    dv[j] = __builtin_amdgcn_sqrtf(piv);  // 1-ulp hardware square root
+  }
+  if (lane < 32) {
+    float* lrow = As + (C0 + r) * LS + C0;
+    float* xrow = Xs + (C0 + r) * LS + C0;
+    float dr = dv[0];
+#pragma unroll
+    for (int k = 1; k < 32; ++k) dr = r == k ? dv[k] : dr;
+    const float idr = __builtin_amdgcn_rcpf(dr);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      lrow[k] = k < r ? x[k] * __builtin_amdgcn_rcpf(dv[k]) : (k == r ? dr : 0.f);
+      xrow[k] = k <= r ? y[k] * idr : 0.f;
+    }
+  }
+}
+
+// Rows C0 + 32 .. NB - 1 of panel columns C0 .. C0 + 31:
+// L21 = A21 L11^-T, i.e. L21[r][c] = sum_k A21[r][k] X11[c][k] (X11 lower).
+// All 256 threads; results are held until every read is done.
+__device__ void leaf_trsm_below(float* As, const float* Xs, int C0) {
+  const int t = threadIdx.x;
+  const int r0 = C0 + 32;
+  const int nout = (NB - r0) * 32;  // at most 3072: 12 per thread
+  float res[12];
+#pragma unroll
+  for (int u = 0; u < 12; ++u) {
+    const int o = t + 256 * u;
+    float acc = 0.f;
+    if (o < nout) {
+      const int r = r0 + (o >> 5), cc = o & 31;
+      const float* a = As + r * LS + C0;
+      const float* xr = Xs + (C0 + cc) * LS + C0;
+#pragma unroll
+      for (int k = 0; k < 32; k += 4) {
+        const float4 av = *reinterpret_cast<const float4*>(a + k);
+        const float4 xv = *reinterpret_cast<const float4*>(xr + k);
+        acc += av.x * xv.x + av.y * xv.y + av.z * xv.z + av.w * xv.w;
       }
     }
-    wave_lds_fence();
+    res[u] = acc;
   }
-  // write back rows >= C0; zeros above the diagonal inside the diagonal block
+  __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    if (lane >= C0) As[lane * LS + C0 + k] = (lane - C0 < k) ? 0.f : ra[k];
-    if (lane + 64 >= C0) As[(lane + 64) * LS + C0 + k] = (lane + 64 - C0 < k) ? 0.f : rb[k];
+  for (int u = 0; u < 12; ++u) {
+    const int o = t + 256 * u;
+    if (o < nout) As[(r0 + (o >> 5)) * LS + C0 + (o & 31)] = res[u];
   }
 }
 
@@ -200,43 +237,19 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
   for (int e = t; e < NB * LS; e += 256) Xs[e] = 0.f;
   __syncthreads();
 
-  // ---- Cholesky, four panels
+  // ---- Cholesky and diagonal-block inverses, four panels
 #pragma unroll 1
   for (int p = 0; p < 4; ++p) {
-    if (w == 0) leaf_panel(As, colbuf, k0, info, p);
+    const int C0 = 32 * p;
+    if (w == 0) leaf_diag32(As, Xs, k0, info, C0);
     __syncthreads();
     if (p < 3) {
-      leaf_syrk(As, 32 * p, 32 * p + 32);
+      leaf_trsm_below(As, Xs, C0);
+      __syncthreads();
+      leaf_syrk(As, C0, C0 + 32);
       __syncthreads();
     }
   }
-
-  // ---- diagonal 32 x 32 inverses: wave w inverts block w, lane c < 32 owns column c
-  {
-    const int lane = t & 63;
-    const int b0 = 32 * w;
-    if (lane < 32) {
-      const int c = lane;
-      float x[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        float s = (i == c) ? 1.f : 0.f;
-        const float* Li = As + (b0 + i) * LS + b0;
-#pragma unroll
-        for (int k4 = 0; k4 < i; k4 += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(Li + k4);
-          s -= v.x * x[k4];
-          if (k4 + 1 < i) s -= v.y * x[k4 + 1];
-          if (k4 + 2 < i) s -= v.z * x[k4 + 2];
-          if (k4 + 3 < i) s -= v.w * x[k4 + 3];
-        }
-        x[i] = s / Li[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) Xs[(b0 + i) * LS + b0 + c] = x[i];
-    }
-  }
-  __syncthreads();
 
   // ---- off-diagonal blocks: X_ip = -X_ii sum_{k=p}^{i-1} L_ik X_kp
   for (int i = 1; i < 4; ++i) {
