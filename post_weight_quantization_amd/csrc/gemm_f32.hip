@@ -6,10 +6,10 @@
 // operands restrict each tile's K range and are masked at load, so the
 // algorithmic (triangle-aware) flop counts are what the kernel executes.
 //
-// Tiling: T x T output tile per workgroup of 4 waves (2 x 2), T = 128 (each
-// wave 64 x 64 as 2 x 2 v_mfma_f32_32x32x2_f32 accumulators) or T = 64 for
-// problems whose 128-tile grid would leave CUs idle (each wave one 32 x 32
-// block). K advances 16 per stage through double-buffered LDS stored k-major,
+// Tiling: T x T output tile per workgroup of 4 waves (2 x 2), T = 64 (each
+// wave one 32 x 32 v_mfma_f32_32x32x2_f32 accumulator) or T = 128 (each wave
+// 64 x 64 as 2 x 2 accumulators) where an in-place product needs one tile
+// across all N columns. K advances 16 per stage through double-buffered LDS stored k-major,
 // so the MFMA operand reads (32 consecutive m or n per k) are conflict-free.
 // Global loads are float4; all callers pass 16-byte aligned pointers and
 // leading dimensions that are multiples of 4.
@@ -313,13 +313,13 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   if ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) & 15)
     return fail(KQ_ERR_ARG, "internal gemm: operands must be 16-byte aligned");
   const int64_t nb = g.batch > 0 ? g.batch : 1;
-  // 128-wide tiles unless they would give fewer than ~2 workgroups per CU
-  // (256 CUs); output-triangle flags halve the live tiles
-  int64_t live = cdiv(g.N, 128) * cdiv(g.M, 128) * nb;
-  if (g.flags & (G_OUT_LOWER | G_OUT_UPPER | G_OUT_SUPPER)) live /= 2;
   if ((g.flags & G_C_ALIASES_A) && g.N > 128)
     return fail(KQ_ERR_SHAPE, "internal gemm: an in-place product needs N <= 128");
-  const bool small = live < 512 && !((g.flags & G_C_ALIASES_A) && g.N > 64);
+  // 64-wide tiles: at 5 waves per SIMD they hide latency better than the
+  // 128-wide tiles (2 waves per SIMD), also on large dense products, and
+  // shorten the longest tile of triangular products; 128-wide tiles only
+  // where an in-place product needs one tile across N
+  const bool small = !((g.flags & G_C_ALIASES_A) && g.N > 64);
   const int T = small ? 64 : 128;
   dim3 grid(unsigned(cdiv(g.N, T)), unsigned(cdiv(g.M, T)), unsigned(nb));
   const bool ta = g.flags & G_TRANS_A, tb = g.flags & G_TRANS_B;
