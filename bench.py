@@ -41,8 +41,8 @@ PEAK_HBM = 8.0e12       # bytes/s
 # workload (4096 x 4096, 131072 bf16 tokens), from FETCH_SIZE and WRITE_SIZE
 # counter passes scaled by the same counters on a copy of known size. Valid
 # only for the kernel source it was measured on (sha256 of cov.hip).
-COV_TRAFFIC = {"cov_sha256": "af322c357f642f95eddf4622698ffeb00b7610f5650d2bde56c1493293c7f329",
-               "bytes": 22844305848}
+COV_TRAFFIC = {"cov_sha256": "20c051834b13af674d4abfd46f9eace233eda7f7a2efc94e820ab564da66c9dc",
+               "bytes": 17112639603}
 
 
 def stage_costs(spec):
