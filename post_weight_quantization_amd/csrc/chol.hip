@@ -11,10 +11,10 @@
 //   1. writes A = J (H + delta I) J (lower triangle) into U's buffer, with
 //      delta = damp * mean(diag H) computed on the device;
 //   2. factors A = L L^T in place, right-looking with 128-column blocks: a
-//      single-workgroup leaf factors the diagonal block (32-column panels,
-//      each by one wave with rows in registers) and inverts it, the panel
-//      below is solved as a GEMM with that inverse, and the trailing lower
-//      triangle takes a rank-128 MFMA update;
+//      single-workgroup leaf factors the diagonal block and inverts it, the
+//      panel below is solved as a GEMM with that inverse (into a compact
+//      temporary, copied back), and the trailing lower triangle takes a
+//      rank-128 MFMA update from the compact copy;
 //   3. inverts L in place by bottom-up doubling with
 //      inv([[A,0],[B,C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]]: every level
 //      is two batched, triangle-aware fp32 MFMA GEMMs;
@@ -389,14 +389,16 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
     const int64_t m = n - k0 - NB;
     if (m <= 0) break;
     float* panel = A + (k0 + NB) * n + k0;
-    // panel <- panel * Dinv_k^T   (in place: each tile reads its rows before writing them)
-    GemmArgs gt = gemm_args(panel, n, Dinv + k * NB * NB, NB, panel, n, m, NB, NB, 1.f, 0.f,
-                            G_TRANS_B | G_C_ALIASES_A);
+    // L21 = panel * Dinv_k^T into the (still unused) inverse temporary, m x NB
+    // dense: out of place, so the product takes narrow tiles across N
+    GemmArgs gt = gemm_args(panel, n, Dinv + k * NB * NB, NB, T, NB, m, NB, NB, 1.f, 0.f, G_TRANS_B);
     KQ_TRY(gemm_f32(gt, s));
-    // trailing lower triangle -= panel panel^T
+    // trailing lower triangle -= L21 L21^T, then L21 back into place
     float* trail = A + (k0 + NB) * n + (k0 + NB);
-    GemmArgs gs = gemm_args(panel, n, panel, n, trail, n, m, m, NB, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
+    GemmArgs gs = gemm_args(T, NB, T, NB, trail, n, m, m, NB, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
     KQ_TRY(gemm_f32(gs, s));
+    KQ_HIP(hipMemcpy2DAsync(panel, size_t(n) * sizeof(float), T, NB * sizeof(float),
+                            NB * sizeof(float), size_t(m), hipMemcpyDeviceToDevice, s));
   }
 
   // invert L in place
