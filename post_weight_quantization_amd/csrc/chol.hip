@@ -50,10 +50,11 @@ __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, cons
 // Per 32-column panel:
 //  * wave 0 factors the 32 x 32 diagonal block and inverts it in registers
 //    (leaf_diag32), with no barrier or LDS access inside the 32 column steps;
-//  * all 256 threads solve the rows below as a product with the inverse
-//    (L21 = A21 L11^-T), then take the rank-32 update of the trailing lower
-//    triangle with 4 x 4 register blocks;
-// then the off-diagonal blocks of the inverse X_ip = -X_ii sum_k L_ik X_kp.
+//  * the waves solve the rows below as a product with the inverse
+//    (L21 = A21 L11^-T) and take the rank-32 update of the trailing lower
+//    triangle, in 32 x 32 blocks on the matrix cores;
+// then the off-diagonal blocks of the inverse X_ip = -X_ii sum_k L_ik X_kp,
+// one block column per wave, also on the matrix cores.
 constexpr int LS = NB + 4;  // LDS row stride (floats), keeps float4 alignment
 
 __device__ inline float lane_value(float v, int lane) {
@@ -119,94 +120,77 @@ __device__ void leaf_diag32(float* As, float* Xs, int64_t k0, int* info, int C0)
   }
 }
 
+// ---- 32 x 32 block products on the matrix cores (one wave each).
+// v_mfma_f32_32x32x2_f32: lane l supplies A[l % 32][k + l / 32] and
+// B[k + l / 32][l % 32]; accumulator element r of lane l is
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// acc += sgn * A op(B): A is 32 x K (rows at ld LS); TB: B holds B[c][k]
+// (op = transpose), else B[k][c].
+template <bool TB>
+__device__ inline void mma32(const float* A, const float* B, int K, float sgn, f32x16& acc) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll 4
+  for (int k = 0; k < K; k += 2) {
+    const float a = sgn * A[lr * LS + k + lk];
+    const float bv = TB ? B[lr * LS + k + lk] : B[(k + lk) * LS + lr];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, acc, 0, 0, 0);
+  }
+}
+
+__device__ inline void acc_load(const float* C, f32x16& acc) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = C[(8 * (r >> 2) + 4 * lk + (r & 3)) * LS + lr];
+}
+
+__device__ inline void acc_store(float* C, const f32x16& acc) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) C[(8 * (r >> 2) + 4 * lk + (r & 3)) * LS + lr] = acc[r];
+}
+
+__device__ inline void acc_zero(f32x16& acc) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+}
+
 // Rows C0 + 32 .. NB - 1 of panel columns C0 .. C0 + 31:
-// L21 = A21 L11^-T, i.e. L21[r][c] = sum_k A21[r][k] X11[c][k] (X11 lower).
-// All 256 threads; results are held until every read is done.
+// L21 = A21 L11^-T, i.e. L21[r][c] = sum_k A21[r][k] X11[c][k]. Wave w takes
+// block row w (in place: a wave reads only the rows it writes).
 __device__ void leaf_trsm_below(float* As, const float* Xs, int C0) {
-  const int t = threadIdx.x;
+  const int w = threadIdx.x >> 6;
   const int r0 = C0 + 32;
-  const int nout = (NB - r0) * 32;  // at most 3072: 12 per thread
-  float res[12];
-#pragma unroll
-  for (int u = 0; u < 12; ++u) {
-    const int o = t + 256 * u;
-    float acc = 0.f;
-    if (o < nout) {
-      const int r = r0 + (o >> 5), cc = o & 31;
-      const float* a = As + r * LS + C0;
-      const float* xr = Xs + (C0 + cc) * LS + C0;
-#pragma unroll
-      for (int k = 0; k < 32; k += 4) {
-        const float4 av = *reinterpret_cast<const float4*>(a + k);
-        const float4 xv = *reinterpret_cast<const float4*>(xr + k);
-        acc += av.x * xv.x + av.y * xv.y + av.z * xv.z + av.w * xv.w;
-      }
-    }
-    res[u] = acc;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 12; ++u) {
-    const int o = t + 256 * u;
-    if (o < nout) As[(r0 + (o >> 5)) * LS + C0 + (o & 31)] = res[u];
-  }
+  if (w >= (NB - r0) / 32) return;
+  f32x16 acc;
+  acc_zero(acc);
+  float* blk = As + (r0 + 32 * w) * LS + C0;
+  mma32<true>(blk, Xs + C0 * LS + C0, 32, 1.f, acc);
+  acc_store(blk, acc);
 }
 
-// As[r][c] -= sum_k As[r][c0+k] As[c][c0+k] (k < 32) for r >= c >= r0 (lower part only)
+// Trailing lower triangle, rows and columns >= r0: As[r][c] -= sum_k
+// As[r][c0 + k] As[c][c0 + k] (k < 32), in 32 x 32 blocks over the waves.
 __device__ void leaf_syrk(float* As, int c0, int r0) {
-  const int m4 = (NB - r0) / 4;
-  const int nblk = m4 * (m4 + 1) / 2;
-  for (int b = threadIdx.x; b < nblk; b += 256) {
-    int bi = int((sqrtf(8.f * float(b) + 1.f) - 1.f) * 0.5f);
-    while ((bi + 1) * (bi + 2) / 2 <= b) ++bi;
-    while (bi * (bi + 1) / 2 > b) --bi;
-    const int bj = b - bi * (bi + 1) / 2;
-    const int r = r0 + 4 * bi, c = r0 + 4 * bj;
-    float acc[4][4] = {};
-#pragma unroll
-    for (int k = 0; k < 32; k += 4) {
-      float4 x[4], y[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[u] = *reinterpret_cast<const float4*>(As + (r + u) * LS + c0 + k);
-        y[u] = *reinterpret_cast<const float4*>(As + (c + u) * LS + c0 + k);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          acc[u][v] += x[u].x * y[v].x + x[u].y * y[v].y + x[u].z * y[v].z + x[u].w * y[v].w;
+  const int w = threadIdx.x >> 6;
+  const int nb = (NB - r0) / 32;
+  for (int t = w, i = 0, j = 0, idx = 0; idx < nb * (nb + 1) / 2; ++idx) {
+    // block idx -> (i, j), j <= i, row by row
+    if (idx > 0) {
+      if (j < i) ++j;
+      else { ++i; j = 0; }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) As[(r + u) * LS + c + v] -= acc[u][v];
+    if (idx % 4 != t) continue;
+    f32x16 acc;
+    float* C = As + (r0 + 32 * i) * LS + r0 + 32 * j;
+    acc_load(C, acc);
+    mma32<true>(As + (r0 + 32 * i) * LS + c0, As + (r0 + 32 * j) * LS + c0, 32, -1.f, acc);
+    acc_store(C, acc);
   }
-}
-
-// C(32 x 32) = alpha * A(32 x K) B(K x 32), all in LDS (ld LS); 2 x 2 outputs per thread.
-__device__ void leaf_mm32(const float* A, const float* B, float* C, int K, float alpha) {
-  const int t = threadIdx.x;
-  const int r = 2 * (t >> 4), c = 2 * (t & 15);
-  float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
-  for (int k = 0; k < K; k += 4) {
-    const float4 x0 = *reinterpret_cast<const float4*>(A + r * LS + k);
-    const float4 x1 = *reinterpret_cast<const float4*>(A + (r + 1) * LS + k);
-    const float xs0[4] = {x0.x, x0.y, x0.z, x0.w};
-    const float xs1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float2 y = *reinterpret_cast<const float2*>(B + (k + u) * LS + c);
-      a00 += xs0[u] * y.x;
-      a01 += xs0[u] * y.y;
-      a10 += xs1[u] * y.x;
-      a11 += xs1[u] * y.y;
-    }
-  }
-  C[r * LS + c] = alpha * a00;
-  C[r * LS + c + 1] = alpha * a01;
-  C[(r + 1) * LS + c] = alpha * a10;
-  C[(r + 1) * LS + c + 1] = alpha * a11;
 }
 
 __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t k0, float* Dinv,
@@ -214,8 +198,6 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
   extern __shared__ __attribute__((aligned(16))) float sm[];
   float* As = sm;                    // NB x LS: the block, then L
   float* Xs = sm + NB * LS;          // NB x LS: the inverse
-  float* Ts = Xs + NB * LS;          // 32 x LS: temporary block
-  float* colbuf = Ts + 32 * LS;      // 32
   const int t = threadIdx.x;
   const int w = t >> 6;
   float* base = A + k0 * n + k0;
@@ -251,16 +233,23 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
     }
   }
 
-  // ---- off-diagonal blocks: X_ip = -X_ii sum_{k=p}^{i-1} L_ik X_kp
-  for (int i = 1; i < 4; ++i) {
-    for (int p = i - 1; p >= 0; --p) {
-      // Ts = L[i, p:i] X[p:i, p]
-      leaf_mm32(As + (32 * i) * LS + 32 * p, Xs + (32 * p) * LS + 32 * p, Ts, 32 * (i - p), 1.f);
-      __syncthreads();
-      leaf_mm32(Xs + (32 * i) * LS + 32 * i, Ts, Xs + (32 * i) * LS + 32 * p, 32, -1.f);
-      __syncthreads();
+  // ---- off-diagonal blocks: X_ip = -X_ii sum_{k=p}^{i-1} L_ik X_kp. Wave p
+  // owns block column p (i = p+1 .. 3 in order); the sum goes through the
+  // unused upper block (p, i) of Xs, zeroed again on the way out.
+  if (w < 3) {
+    const int p = w;
+    for (int i = p + 1; i < 4; ++i) {
+      f32x16 acc;
+      acc_zero(acc);
+      mma32<false>(As + (32 * i) * LS + 32 * p, Xs + (32 * p) * LS + 32 * p, 32 * (i - p), 1.f, acc);
+      float* Tb = Xs + (32 * p) * LS + 32 * i;
+      acc_store(Tb, acc);
+      acc_zero(acc);
+      mma32<false>(Xs + (32 * i) * LS + 32 * i, Tb, 32, -1.f, acc);
+      acc_store(Xs + (32 * i) * LS + 32 * p, acc);
     }
   }
+  __syncthreads();
 
   // ---- write L (lower, zeros above) and its inverse
   for (int e = t; e < NB * NB / 4; e += 256) {
@@ -277,7 +266,7 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
   }
 }
 
-constexpr size_t LEAF_LDS = sizeof(float) * (size_t(NB) * LS * 2 + 32 * LS + 32);
+constexpr size_t LEAF_LDS = sizeof(float) * (size_t(NB) * LS * 2);
 
 // Copy the inverted diagonal blocks into place (block b at (b*NB, b*NB)).
 __global__ void place_diag_kernel(const float* __restrict__ Dinv, int64_t nblk, float* A,
