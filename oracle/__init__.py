@@ -16,6 +16,7 @@ against closed forms, brute force or library routines. One result is
 "parity unpinned" beyond the oracle itself: the exact integer codes of the
 full-size workloads, since the pages print no worked example.
 """
+from . import deploy  # noqa: F401
 from .kronq import (  # noqa: F401
     allocate_bits,
     apply_hadamard_left,
