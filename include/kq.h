@@ -62,7 +62,8 @@ typedef enum {
   KQ_OP_CHOLESKY_INV = 3,
   KQ_OP_FORM_P = 4,
   KQ_OP_GPTAQ_QUANTIZE = 5,
-  KQ_OP_LAYER_OBJECTIVE = 6
+  KQ_OP_LAYER_OBJECTIVE = 6,
+  KQ_OP_APPLY_QUANTIZED = 7  /* n_tok argument of kq_workspace_size = batch */
 } kq_op;
 
 /* Grid and sweep configuration (KronQ summary, Method and experiments:
@@ -208,6 +209,43 @@ kq_status kq_allocate_bits(const double* s, const int64_t* n_params, int32_t L,
 kq_status kq_layer_objective(const float* W0, const float* What, const float* HX,
                              const float* D, const float* HG, int64_t d_out, int64_t d_in,
                              double* obj, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Inference with the quantized layer (KronQ explainer, gist.science,
+ * "Limitazioni": at inference only the orthogonal transforms remain, as in
+ * QuIP#). The sweep quantized W' = U S_G W S_X V^T; the layer in its
+ * original basis is W^ = S_G^-1 U^T W^' V S_X^-1 with W^' = scale (q - zero).
+ *
+ * Packing: each row of codes is a little-endian bit stream, code j in bits
+ * [bits j, bits j + bits) of consecutive 32-bit words; rows are padded to a
+ * multiple of 4 words (16 bytes). */
+
+/* Words per packed row for d_in codes of `bits` bits (host output). */
+kq_status kq_packed_row_words(int64_t d_in, int32_t bits, int64_t* words);
+
+/* codes (d_out x d_in uint8, each < 2^bits) -> packed (d_out x row words,
+ * uint32). bits in {2, 3, 4, 8}. Asynchronous. */
+kq_status kq_pack_codes(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
+                        uint32_t* packed, hipStream_t stream);
+
+/* y = S_G^-1 U^T (W^' (V (S_X^-1 x))) for a batch of vectors, the transforms
+ * applied to the vectors (the layer is never formed).
+ *   packed, bits        codes from kq_pack_codes
+ *   scale, zero         the grids of kq_gptaq_quantize (d_out x n_groups)
+ *   group               0 (one grid per row) or 128
+ *   s_x, s_g            the BiIP scalings (kq_biip outputs, d_in / d_out)
+ *   sign_in, sign_out   the Hadamard signs given to kq_biip, with its blocks
+ *                       blk_in, blk_out (0 = largest power of two dividing)
+ *   x                   batch x d_in fp32, row-major (not modified)
+ *   y                   batch x d_out fp32 output
+ * d_in must be a multiple of 32 (of 128 with groups). Workspace from
+ * kq_workspace_size(KQ_OP_APPLY_QUANTIZED, d_out, d_in, batch, ...).
+ * Asynchronous; fp32 arithmetic. */
+kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* scale,
+                             const float* zero, int32_t group, const float* s_x, const float* s_g,
+                             const int8_t* sign_in, const int8_t* sign_out, int64_t blk_in,
+                             int64_t blk_out, const float* x, int64_t batch, int64_t d_out,
+                             int64_t d_in, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -10,11 +10,14 @@ from ._native import KQError, LIB_PATH  # noqa: F401
 from .api import (  # noqa: F401
     kq_accumulate_cov,
     kq_allocate_bits,
+    kq_apply_quantized,
     kq_biip,
     kq_cholesky_inv,
     kq_form_p,
     kq_gptaq_quantize,
     kq_layer_objective,
+    kq_pack_codes,
+    kq_packed_row_words,
     kq_sensitivity,
     kq_set_kernel_events,
     kq_workspace_size,

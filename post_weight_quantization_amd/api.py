@@ -182,3 +182,34 @@ def kq_set_kernel_events(op: int, start=None, stop=None, stream=None):
             e.record(s)
     check(N.lib.kq_set_kernel_events(op, ctypes.c_void_p(start.cuda_event),
                                       ctypes.c_void_p(stop.cuda_event)))
+
+
+def kq_packed_row_words(d_in: int, bits: int) -> int:
+    out = ctypes.c_int64(0)
+    check(N.lib.kq_packed_row_words(d_in, bits, ctypes.byref(out)))
+    return out.value
+
+
+def kq_pack_codes(codes, bits: int, packed=None, stream=None):
+    """uint8 codes (d_out x d_in) -> packed 32-bit words, stored as int32 (d_out x row words)."""
+    _need_cuda(codes, packed)
+    d_out, d_in = codes.shape
+    if packed is None:
+        packed = torch.empty(d_out, kq_packed_row_words(d_in, bits), dtype=torch.int32, device=codes.device)
+    check(N.lib.kq_pack_codes(_ptr(codes), d_out, d_in, bits, _ptr(packed), _stream(stream)))
+    return packed
+
+
+def kq_apply_quantized(packed, bits: int, scale, zero, group: int, s_x, s_g, sign_in, sign_out, x,
+                       blk_in: int = 0, blk_out: int = 0, y=None, ws=None, stream=None):
+    """y = S_G^-1 U^T W^' V S_X^-1 x for x (batch x d_in fp32); returns y (batch x d_out)."""
+    _need_cuda(packed, scale, zero, s_x, s_g, sign_in, sign_out, x, y)
+    batch, d_in = x.shape
+    d_out = packed.shape[0]
+    if y is None:
+        y = torch.empty(batch, d_out, dtype=torch.float32, device=x.device)
+    ws = _ws(kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED, d_out, d_in, batch), x.device, ws)
+    check(N.lib.kq_apply_quantized(_ptr(packed), bits, _ptr(scale), _ptr(zero), group, _ptr(s_x),
+                                   _ptr(s_g), _ptr(sign_in), _ptr(sign_out), blk_in, blk_out, _ptr(x),
+                                   batch, d_out, d_in, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y

@@ -140,6 +140,10 @@ kq_status kq_workspace_size(kq_op op, int64_t d_out, int64_t d_in, int64_t n_tok
       if (d_out < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
       *bytes = objective_ws_bytes(d_out, d_in);
       return KQ_OK;
+    case KQ_OP_APPLY_QUANTIZED:
+      if (d_out < 1 || n_tok < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
+      *bytes = apply_ws_bytes(d_out, d_in, n_tok);
+      return KQ_OK;
   }
   return fail(KQ_ERR_ARG, "workspace_size: unknown op %d", int(op));
 }
@@ -304,6 +308,55 @@ kq_status kq_layer_objective(const float* W0, const float* What, const float* HX
   KQ_TRY(check_ws(ws, ws_bytes, objective_ws_bytes(d_out, d_in), "layer_objective"));
   Arena ar{static_cast<char*>(ws), ws_bytes, 0};
   return objective_run(W0, What, HX, D, HG, d_out, d_in, obj, ar, stream);
+}
+
+kq_status kq_packed_row_words(int64_t d_in, int32_t bits, int64_t* words) {
+  clear_error();
+  if (!words) return fail(KQ_ERR_ARG, "packed_row_words: words is NULL");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(KQ_ERR_ARG, "packed_row_words: bits must be 2, 3, 4 or 8");
+  if (d_in < 1) return fail(KQ_ERR_SHAPE, "packed_row_words: d_in must be >= 1");
+  *words = packed_row_words(d_in, bits);
+  return KQ_OK;
+}
+
+kq_status kq_pack_codes(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
+                        uint32_t* packed, hipStream_t stream) {
+  clear_error();
+  if (!codes || !packed) return fail(KQ_ERR_ARG, "pack_codes: NULL argument");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(KQ_ERR_ARG, "pack_codes: bits must be 2, 3, 4 or 8");
+  if (d_out < 1 || d_in < 1) return fail(KQ_ERR_SHAPE, "pack_codes: bad sizes");
+  if (!aligned16(packed)) return fail(KQ_ERR_ARG, "pack_codes: packed must be 16-byte aligned");
+  return pack_run(codes, d_out, d_in, bits, packed, stream);
+}
+
+kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* scale,
+                             const float* zero, int32_t group, const float* s_x, const float* s_g,
+                             const int8_t* sign_in, const int8_t* sign_out, int64_t blk_in,
+                             int64_t blk_out, const float* x, int64_t batch, int64_t d_out,
+                             int64_t d_in, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (!packed || !scale || !zero || !s_x || !s_g || !sign_in || !sign_out || !x || !y)
+    return fail(KQ_ERR_ARG, "apply_quantized: NULL argument");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(KQ_ERR_ARG, "apply_quantized: bits must be 2, 3, 4 or 8");
+  if (group != 0 && group != 128)
+    return fail(KQ_ERR_UNSUPPORTED, "apply_quantized: group must be 0 or 128");
+  if (d_out < 4 || d_out % 4 || batch < 1)
+    return fail(KQ_ERR_SHAPE, "apply_quantized: d_out must be a multiple of 4 and batch >= 1");
+  if (d_in < 32 || d_in % 32 || (group && d_in % group))
+    return fail(KQ_ERR_SHAPE, "apply_quantized: d_in must be a multiple of 32 (of the group size)");
+  int64_t bi = 0, bo = 0;
+  KQ_TRY(resolve_block(d_in, blk_in, &bi, "input"));
+  KQ_TRY(resolve_block(d_out, blk_out, &bo, "output"));
+  const void* ptrs[4] = {packed, x, y, s_x};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(KQ_ERR_ARG, "apply_quantized: packed, x, y, s_x must be 16-byte aligned");
+  KQ_TRY(check_ws(ws, ws_bytes, apply_ws_bytes(d_out, d_in, batch), "apply_quantized"));
+  Arena ar{static_cast<char*>(ws), ws_bytes, 0};
+  return apply_run(packed, bits, scale, zero, group, s_x, s_g, sign_in, sign_out, bi, bo, x, batch,
+                   d_out, d_in, y, ar, stream);
 }
 
 }  // extern "C"

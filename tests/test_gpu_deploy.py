@@ -1,0 +1,94 @@
+"""GPU parity of inference with the quantized layer (packing and the product
+y = S_G^-1 U^T W^' V S_X^-1 x) against oracle/deploy.py.
+
+Packing is integer work: bit-exact. The product runs in fp32 with the
+transforms applied to the vectors; against the fp64 reference it is held to
+1e-5 relative (Frobenius over the batch), the size of fp32 rounding over
+sums of d_in terms.
+"""
+import numpy as np
+import pytest
+
+from oracle import deploy
+from tests.gpu_util import dev, have_gpu, host, rel_fro
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+if have_gpu():
+    import torch
+
+    import post_weight_quantization_amd as kq
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("d_out,d_in", [(7, 33), (64, 4096), (3, 11008)])
+def test_pack_bit_exact(bits, d_out, d_in):
+    rng = np.random.default_rng(bits + d_in)
+    codes = rng.integers(0, 1 << bits, (d_out, d_in)).astype(np.uint8)
+    got = host(kq.kq_pack_codes(dev(codes), bits)).view(np.uint32)
+    np.testing.assert_array_equal(got, deploy.pack_codes(codes, bits))
+
+
+def _case(d_out, d_in, bits, group, rng):
+    ng = d_in // group if group else 1
+    codes = rng.integers(0, 1 << bits, (d_out, d_in)).astype(np.uint8)
+    scale = rng.uniform(0.005, 0.02, (d_out, ng)).astype(np.float32)
+    zero = rng.integers(0, 1 << bits, (d_out, ng)).astype(np.float32)
+    s_x = np.exp(rng.normal(0, 0.5, d_in)).astype(np.float32)
+    s_g = np.exp(rng.normal(0, 0.5, d_out)).astype(np.float32)
+    si = rng.choice([-1, 1], d_in).astype(np.int8)
+    so = rng.choice([-1, 1], d_out).astype(np.int8)
+    return codes, scale, zero, s_x, s_g, si, so
+
+
+def _run(codes, scale, zero, s_x, s_g, si, so, bits, group, x, bi=0, bo=0):
+    packed = kq.kq_pack_codes(dev(codes), bits)
+    y = kq.kq_apply_quantized(packed, bits, dev(scale), dev(zero), group, dev(s_x), dev(s_g), dev(si),
+                              dev(so), dev(x), bi, bo)
+    want = deploy.infer(x, deploy.pack_codes(codes, bits), bits, scale, zero, group, s_x, s_g, si, so,
+                        bi, bo)
+    return host(y), want
+
+
+@pytest.mark.parametrize("bits,group,bi,bo,batch", [
+    (2, 0, 0, 0, 1), (3, 128, 0, 0, 3), (4, 0, 128, 64, 5), (8, 128, 0, 32, 8), (2, 128, 256, 0, 4)])
+def test_apply_against_oracle(bits, group, bi, bo, batch):
+    rng = np.random.default_rng(bits * 7 + batch)
+    c = _case(256, 512, bits, group, rng)
+    x = rng.standard_normal((batch, 512)).astype(np.float32)
+    got, want = _run(*c, bits, group, x, bi, bo)
+    assert rel_fro(got, want) < 1e-5
+
+
+def test_apply_on_the_pipeline_output():
+    """Codes, grids and scalings straight from the GPU pipeline on the toy layer."""
+    from synth import layer_specs, make_layer
+    spec = layer_specs(0)[0]
+    L = make_layer(spec)
+    HX, D, HG = kq.kq_accumulate_cov(dev(L["x"]), dev(L["xq"]), dev(L["g"]), 1.0 / spec.n_tok, 0.0)
+    W = dev(L["W"])
+    s_x, s_g = kq.kq_biip(W, HX, D, HG, dev(L["sign_in"]), dev(L["sign_out"]))
+    U = kq.kq_cholesky_inv(HX, spec.damp)
+    codes, scale, zero = kq.kq_gptaq_quantize(W, U, D, spec.bits, spec.group)
+    x = np.random.default_rng(1).standard_normal((2, spec.d_in)).astype(np.float32)
+    y = kq.kq_apply_quantized(kq.kq_pack_codes(codes, spec.bits), spec.bits, scale, zero, 0, s_x, s_g,
+                              dev(L["sign_in"]), dev(L["sign_out"]), dev(x))
+    want = deploy.infer(x, deploy.pack_codes(host(codes), spec.bits), spec.bits, host(scale),
+                        host(zero), 0, host(s_x), host(s_g), L["sign_in"], L["sign_out"])
+    assert rel_fro(host(y), want) < 1e-5
+    # and the product with the de-transformed dequantized layer the sweep returned
+    dense = deploy.detransform(host(W), host(s_x), host(s_g), L["sign_in"], L["sign_out"])
+    assert rel_fro(host(y), x @ dense.T) < 1e-5
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("d_out,d_in,bits,group", [(4096, 4096, 2, 0), (11008, 4096, 3, 128),
+                                                   (8192, 28672, 2, 0)])
+def test_apply_full_size(d_out, d_in, bits, group):
+    rng = np.random.default_rng(d_in)
+    c = _case(d_out, d_in, bits, group, rng)
+    x = rng.standard_normal((4, d_in)).astype(np.float32)
+    got, want = _run(*c, bits, group, x)
+    err = rel_fro(got, want)
+    print(f"{d_out}x{d_in} {bits}-bit: rel {err:.3g}")
+    assert err < 1e-5

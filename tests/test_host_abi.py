@@ -73,6 +73,25 @@ def test_kernel_event_hook_validation():
     assert N.lib.kq_set_kernel_events(N.KQ_OP_ACCUMULATE_COV, None, None) == N.KQ_OK
 
 
+def test_inference_entry_points_validate_on_host():
+    from oracle import deploy
+    out = ctypes.c_int64()
+    for d_in, bits in ((4096, 2), (33, 3), (11008, 3), (1, 8)):
+        assert N.lib.kq_packed_row_words(d_in, bits, ctypes.byref(out)) == N.KQ_OK
+        assert out.value == deploy.packed_row_words(d_in, bits)
+    assert N.lib.kq_packed_row_words(64, 5, ctypes.byref(out)) == N.KQ_ERR_ARG
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+    args = lambda bits, group, d_out, d_in, ws: (fake, bits, fake, fake, group, fake, fake, fake, fake, 0,
+                                                 0, fake, 1, d_out, d_in, fake, fake, ws, None)
+    assert N.lib.kq_apply_quantized(*args(5, 0, 64, 64, 1 << 30)) == N.KQ_ERR_ARG
+    assert N.lib.kq_apply_quantized(*args(2, 64, 64, 128, 1 << 30)) == N.KQ_ERR_UNSUPPORTED
+    assert N.lib.kq_apply_quantized(*args(2, 0, 64, 48, 1 << 30)) == N.KQ_ERR_SHAPE
+    assert N.lib.kq_apply_quantized(*args(2, 0, 6, 64, 1 << 30)) == N.KQ_ERR_SHAPE
+    st = N.lib.kq_apply_quantized(*args(2, 0, 64, 64, 16))
+    assert st == N.KQ_ERR_WORKSPACE
+    assert N.lib.kq_pack_codes(None, 4, 4, 2, fake, None) == N.KQ_ERR_ARG
+
+
 def test_workspace_checked_before_launch():
     fake = ctypes.c_void_p(0x10000)
     cfg = N.kq_quant_cfg(2, 0, 128, 0)
@@ -83,7 +102,7 @@ def test_workspace_checked_before_launch():
     st, msg = _err(N.lib.kq_gptaq_quantize(fake, fake, fake, 256, 512, ctypes.byref(cfg), fake, fake,
                                            fake, fake, need.value - 1, None))
     assert st == N.KQ_ERR_WORKSPACE and str(need.value) in msg
-    for op in range(7):
+    for op in range(8):
         assert N.lib.kq_workspace_size(op, 1024, 4096, 8192, 0, ctypes.byref(cfg), ctypes.byref(need)) == 0
     assert N.lib.kq_workspace_size(99, 1, 1, 1, 0, None, ctypes.byref(need)) == N.KQ_ERR_ARG
 
