@@ -149,8 +149,75 @@ def run_gpu(spec, steps, warmup, data):
     except Exception as e:  # pragma: no cover - reporting only
         print(f"objective check failed: {e}", file=sys.stderr)
         obj_rtn = None
+    inf = run_inference(spec, codes, scale, zero, s_x, s_g, si, so)
     return dict(wall_s=wall, stage_ms=stage_ms, cov_kernel_ms=cov_kernel_ms, sens=sens, obj=obj,
-                obj_rtn=obj_rtn)
+                obj_rtn=obj_rtn, inference=inf)
+
+
+def time_apply(packed, bits, scale, zero, group, s_x, s_g, si, so, d_out, d_in, batch, reps=20):
+    """Mean time of one kq_apply_quantized call and of its product kernel (event
+    hook), over `reps` calls after warm-up; inputs resident on the device."""
+    import torch
+
+    import post_weight_quantization_amd as kq
+    from post_weight_quantization_amd import _native as N
+
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(batch)
+    x = torch.randn(batch, d_in, device="cuda", generator=g)
+    y = torch.empty(batch, d_out, device="cuda")
+    ws = torch.empty(kq.kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED, d_out, d_in, batch),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: kq.kq_apply_quantized(packed, bits, scale, zero, group, s_x, s_g, si, so, x, y=y, ws=ws)
+    for _ in range(3):
+        call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for k in range(reps):
+        ev[k][0].record(stream)
+        kq.kq_set_kernel_events(N.KQ_OP_APPLY_QUANTIZED, ev[k][1], ev[k][2], stream)
+        call()
+        ev[k][3].record(stream)
+    kq.kq_set_kernel_events(N.KQ_OP_APPLY_QUANTIZED)
+    torch.cuda.synchronize()
+    call_us = float(np.mean([e[0].elapsed_time(e[3]) for e in ev])) * 1e3
+    kern_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    return call_us, kern_us
+
+
+def run_inference(spec, codes, scale, zero, s_x, s_g, si, so):
+    """Inference with the quantized layer (packed codes, y = S_G^-1 U^T W^' V
+    S_X^-1 x): the layer this step quantized, and the 8192 x 28672 2-bit
+    down_proj shape of the 70B workload with random codes. Bytes per product
+    launch: packed codes + grids + the transformed input read + y1 written."""
+    import torch
+
+    import post_weight_quantization_amd as kq
+
+    out = {}
+    cases = [("layer", spec.d_out, spec.d_in, spec.bits, spec.group, codes, scale, zero, s_x, s_g, si, so)]
+    m, n, b = 8192, 28672, 2
+    g = torch.Generator(device="cuda").manual_seed(70)
+    cases.append(("down_proj_8192x28672", m, n, b, 0,
+                  torch.randint(0, 1 << b, (m, n), dtype=torch.uint8, device="cuda", generator=g),
+                  torch.rand(m, 1, device="cuda", generator=g) * 0.01 + 0.005,
+                  torch.randint(0, 1 << b, (m, 1), device="cuda", generator=g).float(),
+                  torch.rand(n, device="cuda", generator=g) + 0.5,
+                  torch.rand(m, device="cuda", generator=g) + 0.5,
+                  (torch.randint(0, 2, (n,), device="cuda", generator=g) * 2 - 1).to(torch.int8),
+                  (torch.randint(0, 2, (m,), device="cuda", generator=g) * 2 - 1).to(torch.int8)))
+    for name, d_out, d_in, bits, group, cd, sc, zr, sx, sg, sgi, sgo in cases:
+        packed = kq.kq_pack_codes(cd, bits)
+        ng = d_in // group if group else 1
+        rec = {"d_out": d_out, "d_in": d_in, "bits": bits, "group": group}
+        for batch in (1, 4):
+            call_us, kern_us = time_apply(packed, bits, sc, zr, group, sx, sg, sgi, sgo, d_out, d_in, batch)
+            nbytes = packed.numel() * 4 + 8 * d_out * ng + 4 * batch * (d_in + d_out)
+            rec[f"b{batch}"] = {"call_us": round(call_us, 2), "product_us": round(kern_us, 2),
+                                "product_gbs": round(nbytes / kern_us / 1e3, 1),
+                                "product_hbm_frac": round(nbytes / kern_us / 1e3 / (PEAK_HBM / 1e9), 4)}
+        out[name] = rec
+    return out
 
 
 def copy_calibration(mib):
@@ -272,6 +339,7 @@ def main():
         "sensitivity": g["sens"][2],
         "objective": g["obj"], "objective_rtn": g["obj_rtn"],
         "cpu_baseline": cpu,
+        "inference": g["inference"],
     }
     print(json.dumps(out))
 

@@ -88,11 +88,14 @@ const char* kq_version(void);
  * kernel is enqueued and `stop` right after, so the caller can time that one
  * kernel with hipEventElapsedTime on the stream it actually ran on. This is
  * the only state the library keeps between calls (per thread).
- *   op     KQ_OP_ACCUMULATE_COV only: the main kernel is the covariance
+ *   op     KQ_OP_ACCUMULATE_COV: the main kernel is the covariance
  *          kernel (bf16 inputs: the tile kernel that computes H_X, D and H_G
  *          together; the drift pre-pass and the split reduction lie outside
  *          the bracket). For fp32 inputs the bracket holds the three
  *          products and the drift pass.
+ *          KQ_OP_APPLY_QUANTIZED: the product with the packed codes (one
+ *          launch per 4 vectors of the batch; the two transforms lie
+ *          outside the bracket).
  *   start, stop  events created by the caller (who owns and destroys them);
  *          both NULL switches the hook off.
  * Errors: KQ_ERR_UNSUPPORTED for other ops, KQ_ERR_ARG if exactly one event

@@ -5,27 +5,73 @@
 // is the orthogonal transforms. The sweep quantizes W' = U S_G W S_X V^T, so
 //   y = W^ x = S_G^-1 U^T (W^' (V (S_X^-1 x))),
 // with U = blockdiag(H_b / sqrt b) diag(sign_out) and V likewise on the input
-// side. One call runs
-//   1. x2 = V S_X^-1 x: the row FWHT of the batch with sign_in / s_x folded
-//      into its load;
-//   2. sums of x2 over every 32-entry chunk (the zero-point term);
-//   3. y1 = W^' x2 from the packed codes: a lane takes a chunk of 32 codes of
-//      8 rows, with the chunk's x2 values in registers, decodes the codes
-//      with constant shifts and accumulates scale (sum q x - zero sum x) per
-//      chunk (a grid per row or per 128-column group); the lanes' partial
-//      sums meet in a wave reduction;
-//   4. y = S_G^-1 diag(sign_out) blockdiag(H_b / sqrt b) y1: the row FWHT of
-//      y1, then the output scaling.
+// side. One call is three launches:
+//   1. transform_in: x2 = V S_X^-1 x, a row FWHT in LDS with sign_in / s_x
+//      folded into the load, written out per 32-value chunk in the form the
+//      product reads (below);
+//   2. qmatvec: y1 = W^' x2 straight from the packed codes. The columns are
+//      cut into K tiles of 2048 (64 lanes x one 32-code chunk each). A
+//      workgroup owns a run of rows and its waves share out the K tiles; a
+//      lane keeps its chunk of x2 in registers for all of the rows and
+//      decodes each row's codes into sum_k q_k x_k. With 128-column groups
+//      the chunk's grid applies at once, scale (sum q x - zero sum x); with
+//      one grid per row it applies to the row's total, scale (sum_j q_j x_j
+//      - zero sum_j x_j), after the workgroup's sums meet. Per-row
+//      sums over the 64 lanes go through a transposing butterfly (8 rows x
+//      NB vectors leave the wave in 10 shuffles for NB = 1); the waves'
+//      sums meet in LDS and are added in wave order (no atomics);
+//   3. transform_out: FWHT of each output block of y1, then sign_out / s_g
+//      and 1 / sqrt(b).
+// Products: for 2-, 4- and 8-bit codes in integers. Each chunk of x2 is held
+// in fixed point against its own largest magnitude: with 2^(e-1) <=
+// max |x_k| < 2^e, m_k = rint(x_k 2^(22 - e)), |m_k| <= 2^22, and x_k =
+// m_k 2^(e - 22) up to half a unit of 2^(e - 22), below fp32's rounding of
+// the chunk's largest value. m_k is split into signed limbs, and a packed
+// word under a field mask lines its codes up with the limbs of one limb
+// word, so one dot instruction sums several products exactly in int32:
+//   2- and 4-bit codes: six 4-bit limbs (m = sum_l n_l 16^l, n_l in
+//     [-8, 7]), dot8 over 8 codes; 4-bit codes enter as q - 8 to fit a
+//     signed nibble. The limbs are taken from the top down, the sum shifted
+//     by 4 bits between them (|sum q m| < 2^30: exact);
+//   8-bit codes: three byte limbs (m = l0 + 2^8 l1 + 2^16 l2), dot4 over 4
+//     codes entered as q - 128, the limb sums combined in fp32.
+// That is 24 dot instructions per 32 codes and vector, against 2
+// conversions and fused multiply-adds per code in fp32. 3-bit codes
+// straddle words and use fp32 products (bit-field extract, conversion,
+// fused multiply-add).
 // Packing: code j of a row in bits [b j, b j + b) of a little-endian stream
 // of 32-bit words, rows padded to a multiple of 4 words.
 #include "kq_internal.h"
+#include "fwht_lds.h"
+
+#include <utility>
 
 namespace kq {
 
 namespace {
 
-constexpr int RPW = 8;  // rows per wave in the product
-constexpr int BT = 4;   // vectors per pass over the codes
+constexpr int LANES = 64;
+constexpr int CODES = 32;   // codes of a row per lane and K tile: one chunk
+constexpr int XW = 32;      // words per chunk and vector of the prepared input
+constexpr int G = 8;        // rows per group: G x NB values reduced together
+constexpr int SLOT = 64;    // rows x vectors per workgroup of the product
+constexpr int TCH = 8192;   // elements per LDS transform chunk
+constexpr int TCHP = TCH + TCH / 32;
+
+// Prepared chunk (XW words). Integer products: words 0-23 hold the limbs,
+// limb l of 2- and 4-bit codes in words 4 l .. 4 l + 3, of 8-bit codes in
+// words 8 l .. 8 l + 7. Limb word j of a limb holds in field f (nibble or
+// byte) the limb of the code that field f of the masked packed word j
+// holds: 2-bit codes, word j = 2 i + p <- packed word i shifted by 2 p,
+// nibble f = code 16 i + 2 f + p; 4-bit codes, nibble f of word j = code
+// 8 j + f; 8-bit codes, byte f of word j = code 4 j + f. Word 24 =
+// 2^(e - 22) and word 25 = sum m_k as floats. fp32 products: the 32 values.
+constexpr int W_UNIT = 24, W_MSUM = 25;
+
+// The integer products take codes q - offset: signed nibbles for 4-bit
+// codes, signed bytes for 8-bit codes.
+__device__ constexpr float code_offset(int bits) { return bits == 4 ? 8.f : bits == 8 ? 128.f : 0.f; }
+
 
 __global__ void pack_kernel(const uint8_t* __restrict__ codes, int64_t d_out, int64_t d_in, int bits,
                             int64_t row_words, uint32_t* __restrict__ packed) {
@@ -44,135 +90,492 @@ __global__ void pack_kernel(const uint8_t* __restrict__ codes, int64_t d_out, in
   packed[e] = v;
 }
 
-// fin = sign_in / s_x; fout = sign_out / s_g
-__global__ void factors_kernel(const int8_t* si, const float* s_x, int64_t d_in, const int8_t* so,
-                               const float* s_g, int64_t d_out, float* fin, float* fout) {
-  const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e < d_in) fin[e] = float(si[e]) / s_x[e];
-  if (e < d_out) fout[e] = float(so[e]) / s_g[e];
+inline int ilog2(int64_t v) {
+  int k = 0;
+  while ((int64_t(1) << (k + 1)) <= v) ++k;
+  return k;
 }
 
-// csum[b][c] = sum of x2[b][32c .. 32c + 31]
-__global__ void chunk_sum_kernel(const float* __restrict__ x2, int64_t d_in, int64_t nchunk,
-                                 int64_t batch, float* __restrict__ csum) {
-  const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e >= batch * nchunk) return;
-  const float4* p = reinterpret_cast<const float4*>(x2 + (e / nchunk) * d_in + (e % nchunk) * 32);
-  float s = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float4 v = p[k];
-    s += (v.x + v.y) + (v.z + v.w);
+// Transform chunk: the largest L with blk | L, L | n, L <= TCH.
+int64_t transform_len(int64_t n, int64_t blk) {
+  int64_t L = blk;
+  while (L * 2 <= TCH && n % (L * 2) == 0) L *= 2;
+  return L;
+}
+
+// x2 = gain * H_blk (x[b] sign_in / s_x) over a chunk of L = 2^lgL columns
+// of vector b, written as prepared chunks xq[b][c] (XW words each). One
+// workgroup per chunk of columns; blockDim is a multiple of 64 dividing L
+// (or 64 when L = 32).
+template <int BITS>
+__global__ __launch_bounds__(1024) void transform_in_kernel(const float* __restrict__ x, int64_t d_in,
+                                                            int lgL, int lgb,
+                                                            const int8_t* __restrict__ si,
+                                                            const float* __restrict__ s_x, float gain,
+                                                            uint32_t* __restrict__ xq) {
+  __shared__ float s[TCHP];
+  const int L = 1 << lgL;
+  const int64_t per_row = d_in >> lgL;
+  const int64_t b = blockIdx.x / per_row;
+  const int64_t c0 = int64_t(blockIdx.x % per_row) << lgL;
+  const float* src = x + b * d_in + c0;
+  for (int e = 4 * threadIdx.x; e < L; e += 4 * blockDim.x) {
+    const float4 v = *reinterpret_cast<const float4*>(src + e);
+    const float4 sx = *reinterpret_cast<const float4*>(s_x + c0 + e);
+    s[padi(e)] = v.x * float(si[c0 + e]) / sx.x;
+    s[padi(e + 1)] = v.y * float(si[c0 + e + 1]) / sx.y;
+    s[padi(e + 2)] = v.z * float(si[c0 + e + 2]) / sx.z;
+    s[padi(e + 3)] = v.w * float(si[c0 + e + 3]) / sx.w;
   }
-  csum[e] = s;
+  __syncthreads();
+  lds_fwht(s, L, 0, lgb);
+  const int64_t nchunk = d_in / CODES;
+  uint32_t* dst = xq + (b * nchunk + (c0 >> 5)) * XW;  // this chunk's first prepared chunk
+  if constexpr (BITS == 3) {
+    for (int e = threadIdx.x; e < L; e += blockDim.x) dst[e] = __float_as_uint(gain * s[padi(e)]);
+  } else {
+    constexpr bool NIB = BITS != 8;
+    constexpr int NL = NIB ? 6 : 3, LB = NIB ? 4 : 8;  // limbs, bits per limb
+    __shared__ int8_t lim[TCH * 6];
+    __shared__ float meta[TCH / CODES][2];
+    // one value per lane; the 32 lanes of a half-wave hold one chunk
+    for (int e = threadIdx.x; e < L; e += blockDim.x) {
+      const float v = gain * s[padi(e)];
+      float mx = fabsf(v);
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      int ex = 0;
+      if (mx > 0.f) frexpf(mx, &ex);  // mx = f 2^ex, 1/2 <= f < 1
+      const int m = int(rintf(ldexpf(v, 22 - ex)));
+      int r = m;
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        const int h = 1 << (LB - 1);
+        const int n = ((r + h) & (2 * h - 1)) - h;  // balanced digit
+        lim[e * 6 + l] = int8_t(n);
+        r = (r - n) >> LB;
+      }
+      int ms = m;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) ms += __shfl_xor(ms, o);
+      if ((e & (CODES - 1)) == 0) {
+        meta[e >> 5][0] = ldexpf(1.f, ex - 22);
+        meta[e >> 5][1] = float(ms);
+      }
+    }
+    __syncthreads();
+    // one output word per thread: chunk e / 32, word e % 32
+    for (int e = threadIdx.x; e < L; e += blockDim.x) {
+      const int ch = e >> 5, j = e & 31;
+      uint32_t word = 0u;
+      if (j < 24) {
+        const int l = NIB ? j >> 2 : j >> 3, wi = NIB ? j & 3 : j & 7;
+        constexpr int FIELDS = NIB ? 8 : 4;
+#pragma unroll
+        for (int f = 0; f < FIELDS; ++f) {
+          const int k = BITS == 2 ? 16 * (wi >> 1) + 2 * f + (wi & 1) : BITS == 4 ? 8 * wi + f : 4 * wi + f;
+          const uint32_t digit = uint32_t(int(lim[(32 * ch + k) * 6 + l])) & ((1u << LB) - 1);
+          word |= digit << (LB * f);
+        }
+      } else if (j == W_UNIT) {
+        word = __float_as_uint(meta[ch][0]);
+      } else if (j == W_MSUM) {
+        word = __float_as_uint(meta[ch][1]);
+      }
+      dst[e] = word;
+    }
+  }
 }
 
-__global__ void post_scale_kernel(const float* __restrict__ y2, const float* __restrict__ fout,
-                                  int64_t d_out, int64_t batch, float* __restrict__ y) {
-  const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e < batch * d_out) y[e] = y2[e] * fout[e % d_out];
+// y[b][r0 + e] = gain * sign_out / s_g * (H_blk y1[b])[r0 + e]
+__global__ __launch_bounds__(1024) void transform_out_kernel(const float* __restrict__ y1,
+                                                             int64_t d_out, int lgL, int lgb,
+                                                             const int8_t* __restrict__ so,
+                                                             const float* __restrict__ s_g, float gain,
+                                                             float* __restrict__ y) {
+  __shared__ float s[TCHP];
+  const int L = 1 << lgL;
+  const int64_t per_row = d_out >> lgL;
+  const int64_t b = blockIdx.x / per_row;
+  const int64_t r0 = int64_t(blockIdx.x % per_row) << lgL;
+  const float* src = y1 + b * d_out + r0;
+  for (int e = 4 * threadIdx.x; e < L; e += 4 * blockDim.x) {
+    const float4 v = *reinterpret_cast<const float4*>(src + e);
+    s[padi(e)] = v.x;
+    s[padi(e + 1)] = v.y;
+    s[padi(e + 2)] = v.z;
+    s[padi(e + 3)] = v.w;
+  }
+  __syncthreads();
+  lds_fwht(s, L, 0, lgb);
+  float* dst = y + b * d_out + r0;
+  for (int e = threadIdx.x; e < L; e += blockDim.x)
+    dst[e] = gain * s[padi(e)] * float(so[r0 + e]) / s_g[r0 + e];
 }
 
+// One step of the transposing butterfly over v[0 .. 2H): lanes with bit o
+// set keep the upper half, the others the lower, and each adds the half its
+// partner keeps. Constant indices only, so the values stay in registers.
+template <int N, int H, int... I>
+__device__ inline void fold_step(float (&v)[N], int lane, int o, std::integer_sequence<int, I...>) {
+  const bool up = lane & o;
+  ((v[I] = (up ? v[I + H] : v[I]) + __shfl_xor(up ? v[I] : v[I + H], o)), ...);
+}
+
+// Sums of N values (N a power of two <= 64) over the 64 lanes: transposing
+// steps at offsets 32, 16, ... leave lane L with value L >> (6 - log2 N)
+// summed over its 64 / N neighbours, plain steps finish the sum.
+template <int N, int K = 0>
+__device__ inline float fold_all(float (&v)[N], int lane) {
+  if constexpr ((N >> K) >= 2) {
+    fold_step<N, (N >> (K + 1))>(v, lane, 32 >> K, std::make_integer_sequence<int, (N >> (K + 1))>{});
+    return fold_all<N, K + 1>(v, lane);
+  } else {
+    float t = v[0];
+#pragma unroll
+    for (int o = 32 >> K; o > 0; o >>= 1) t += __shfl_xor(t, o);
+    return t;
+  }
+}
+
+// The codes of one row's chunk (p in bounds: lanes past the last chunk read
+// the last chunk, and their input chunk is zero)
 template <int BITS>
-__device__ inline uint32_t code_at(const uint32_t (&w)[BITS], int k) {
-  const int bit = BITS * k, i = bit >> 5, sh = bit & 31;
-  uint32_t v = w[i] >> sh;
-  if (sh + BITS > 32) v |= w[i + 1] << (32 - sh);
-  return v & ((1u << BITS) - 1);
+__device__ inline void load_codes(const uint32_t* p, uint32_t (&w)[BITS]) {
+  if constexpr (BITS == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else if constexpr (BITS == 4 || BITS == 8) {
+#pragma unroll
+    for (int h = 0; h < BITS / 4; ++h) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[h];
+      w[4 * h] = v.x;
+      w[4 * h + 1] = v.y;
+      w[4 * h + 2] = v.z;
+      w[4 * h + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) w[i] = p[i];
+  }
 }
 
-// y1[b0 + b][row] for b < nb (nb <= BT) over all rows; one wave per RPW rows
-template <int BITS>
-__global__ __launch_bounds__(256) void qmatvec_kernel(const uint32_t* __restrict__ packed,
-                                                      int64_t row_words, const float* __restrict__ scale,
-                                                      const float* __restrict__ zero, int ngroups,
-                                                      int gchunks, const float* __restrict__ x2,
-                                                      const float* __restrict__ csum, int64_t d_in,
-                                                      int64_t d_out, int b0, int nb,
-                                                      float* __restrict__ y1) {
+// Codes of one group of G rows for this lane's chunk: rows past `last`
+// repeat row `last` (in bounds; their values are not stored).
+template <int BITS, int G>
+__device__ inline void load_group(const uint32_t* gp, int rw, int last, uint32_t (&wc)[G][BITS]) {
+#pragma unroll
+  for (int r = 0; r < G; ++r) load_codes<BITS>(gp + min(r, last) * rw, wc[r]);
+}
+
+// sum_k q_k x_k of every row of a group and vector, pr[r][b]. The rows'
+// dependency chains are interleaved (row index innermost), so consecutive
+// instructions are independent.
+template <int BITS, int NB>
+__device__ inline void group_dot(const uint32_t (&wc)[G][BITS], const uint32_t (&xw)[NB][XW],
+                                 float (&pr)[G][NB]) {
+  if constexpr (BITS == 2 || BITS == 4) {
+    // nibble masks of the packed words (4-bit codes as q - 8) against the
+    // nibble limb words, top limb first, shifting the sums by 4 bits
+    // between limbs
+    uint32_t t[G][4];
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      if constexpr (BITS == 2) {
+        t[r][0] = wc[r][0] & 0x33333333u;
+        t[r][1] = (wc[r][0] >> 2) & 0x33333333u;
+        t[r][2] = wc[r][1] & 0x33333333u;
+        t[r][3] = (wc[r][1] >> 2) & 0x33333333u;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[r][i] = wc[r][i] ^ 0x88888888u;
+      }
+    }
+    int d[G][NB];
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) d[r][b] = 0;
+#pragma unroll
+    for (int l = 5; l >= 0; --l) {
+      if (l < 5) {
+#pragma unroll
+        for (int r = 0; r < G; ++r)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) d[r][b] <<= 4;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < G; ++r)
+            d[r][b] = __builtin_amdgcn_sdot8(int(t[r][j]), int(xw[b][4 * l + j]), d[r][b], false);
+    }
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) pr[r][b] = float(d[r][b]);
+  } else if constexpr (BITS == 8) {
+    // codes as signed bytes q - 128 against the byte limb words; the limb
+    // sums combine in fp32
+    int d[G][NB][3];
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) d[r][b][0] = d[r][b][1] = d[r][b][2] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int l = 0; l < 3; ++l)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < G; ++r)
+            d[r][b][l] = __builtin_amdgcn_sdot4(int(wc[r][i] ^ 0x80808080u), int(xw[b][8 * l + i]),
+                                                d[r][b][l], false);
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        pr[r][b] = float(d[r][b][0]) + 256.f * float(d[r][b][1]) + 65536.f * float(d[r][b][2]);
+  } else {
+    // 3-bit codes: bit-field extracts, conversions, fp32 fused multiply-adds
+    float acc[G][NB];
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+#pragma unroll
+    for (int k = 0; k < CODES; ++k) {
+      const int bit = 3 * k, i = bit >> 5, sh = bit & 31;
+      float q[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        uint32_t v = wc[r][i] >> sh;
+        if (sh + 3 > 32) v |= wc[r][i + 1] << (32 - sh);
+        q[r] = float(v & 7u);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float xk = __uint_as_float(xw[b][k]);
+#pragma unroll
+        for (int r = 0; r < G; ++r) acc[r][b] = __builtin_fmaf(q[r], xk, acc[r][b]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) pr[r][b] = acc[r][b];
+  }
+}
+
+// v[r * NB + b] for the group's rows: with one grid per row the unscaled
+// chunk product unit * sum_k q m (the grid applies to the row's total); with
+// groups of 128 columns scale unit (sum_k q m - zero sum_k m) for the chunk's
+// group (fp32 products: unit = 1, m = x).
+template <int BITS, int NB, bool GROUPED>
+__device__ inline void group_values(const uint32_t (&wc)[G][BITS], const float* scg,
+                                    const float* zrg, int ngroups, int64_t g, bool act, int last,
+                                    const uint32_t (&xw)[NB][XW], const float (&cs)[NB],
+                                    float (&v)[G * NB]) {
+  constexpr bool INT = BITS != 3;
+  float prg[G][NB];
+  group_dot<BITS, NB>(wc, xw, prg);
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    const float(&pr)[NB] = prg[r];
+    if constexpr (GROUPED) {
+      const int rr = min(r, last);
+      const float sc = act ? scg[rr * ngroups + g] : 0.f;
+      float zr = act ? zrg[rr * ngroups + g] : 0.f;
+      zr -= code_offset(BITS);  // the products used q - offset
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float u = INT ? sc * __uint_as_float(xw[b][W_UNIT]) : sc;
+        v[r * NB + b] = u * (pr[b] - zr * cs[b]);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) v[r * NB + b] = INT ? __uint_as_float(xw[b][W_UNIT]) * pr[b] : pr[b];
+    }
+  }
+}
+
+// Waves per workgroup of the product: 16 where the kernel fits 128 VGPRs
+// (one vector, 2-bit codes, one grid per row), else 8 (256 VGPRs).
+constexpr int max_waves(int bits, int nb, bool grouped) {
+  return nb == 1 && bits == 2 && !grouped ? 16 : 8;
+}
+
+// y1[b0 + b][rows] = W^'[rows] x2[b0 + b] for b < nb (nb <= NB), rows
+// blockIdx.x * rpw .. + rpw - 1 (rpw a multiple of G, rpw * NB <= SLOT).
+// Wave w of the workgroup takes K tiles w, w + waves, ...
+template <int BITS, int NB, bool GROUPED>
+__global__ __launch_bounds__(64 * max_waves(BITS, NB, GROUPED)) void qmatvec_kernel(
+    const uint32_t* __restrict__ packed, int rw, const float* __restrict__ scale,
+    const float* __restrict__ zero, int ngroups, const uint32_t* __restrict__ xq, int64_t nchunk,
+    int64_t d_out, int nkt, int rpw, int b0, int nb, float* __restrict__ y1) {
+  constexpr bool INT = BITS != 3;
+  constexpr int NV = G * NB;          // values per group
+  constexpr int LGV = NV == 8 ? 3 : NV == 16 ? 4 : 5;
+  __shared__ float red[max_waves(BITS, NB, GROUPED)][SLOT];
+  __shared__ float redx[max_waves(BITS, NB, GROUPED)][4];  // sum of x2, one grid per row
   const int lane = threadIdx.x & 63;
-  const int64_t r0 = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW;
-  if (r0 >= d_out) return;
-  const int64_t nchunk = d_in / 32;
-  float acc[RPW][BT];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int64_t rbeg = int64_t(blockIdx.x) * rpw;
+  const int nrows = int(min(int64_t(rpw), d_out - rbeg));
+  for (int i = lane; i < SLOT; i += LANES) red[w][i] = 0.f;  // this wave's slots only
+  if (lane < 4) redx[w][lane] = 0.f;
+  // after the butterfly lane L holds value L >> (6 - LGV) = row * NB + vector
+  const int vi = lane >> (6 - LGV), vr = vi / NB, vb = vi % NB;
 
-  for (int64_t c = lane; c < nchunk; c += 64) {
-    float xv[BT][32];
-    float cs[BT];
+  // The wave's work: K tiles w, w + nw, ... times the row groups, in that
+  // order. The codes of step it + 1 are loaded while step it is computed.
+  const int ngrp = (nrows + G - 1) / G;
+  const int steps = ((nkt - 1 - w) / nw + 1) * ngrp;
+  auto step_kt = [&](int it) { return w + (it / ngrp) * nw; };
+  auto step_gi = [&](int it) { return (it % ngrp) * G; };
+  auto issue = [&](int it, uint32_t (&dst)[G][BITS]) {
+    const int64_t c = min(int64_t(step_kt(it)) * LANES + lane, nchunk - 1);
+    const int gi = step_gi(it);
+    load_group<BITS, G>(packed + c * BITS + (rbeg + gi) * rw, rw, min(G, nrows - gi) - 1, dst);
+  };
+  // the next step's codes load during this step where the registers allow
+  constexpr bool PREFETCH = G * BITS <= 32 || (NB == 1 && G * BITS <= 64);
+  uint32_t xw[NB][XW];
+  float cs[NB];
+  int cur_kt = -1;
+  uint32_t wn[PREFETCH ? G : 1][BITS];
+  for (int it = 0; it < steps; ++it) {
+    const int kt = step_kt(it), gi = step_gi(it);
+    const int64_t c = int64_t(kt) * LANES + lane;
+    const bool act = c < nchunk;
+    if (kt != cur_kt) {
+      // a new K tile: this lane's chunk of the prepared input, loaded
+      // ahead of the step's codes
+      cur_kt = kt;
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const int bb = b < nb ? b0 + b : b0;  // unused slots repeat a valid vector
-      const float4* p = reinterpret_cast<const float4*>(x2 + bb * d_in + c * 32);
+      for (int b = 0; b < NB; ++b) {
+        const int bb = b < nb ? b0 + b : b0;  // unused slots repeat a valid vector
+        const uint4* p = reinterpret_cast<const uint4*>(xq + (bb * nchunk + min(c, nchunk - 1)) * XW);
+        constexpr int NQ = INT ? 7 : 8;  // integer chunks: words 0 .. 27
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float4 v = p[k];
-        xv[b][4 * k] = v.x;
-        xv[b][4 * k + 1] = v.y;
-        xv[b][4 * k + 2] = v.z;
-        xv[b][4 * k + 3] = v.w;
+        for (int q = 0; q < 8; ++q) {
+          const uint4 u = q < NQ ? p[q] : make_uint4(0u, 0u, 0u, 0u);
+          xw[b][4 * q] = act ? u.x : 0u;
+          xw[b][4 * q + 1] = act ? u.y : 0u;
+          xw[b][4 * q + 2] = act ? u.z : 0u;
+          xw[b][4 * q + 3] = act ? u.w : 0u;
+        }
       }
-      cs[b] = csum[bb * nchunk + c];
-    }
-    const int g = gchunks ? int(c / gchunks) : 0;
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int64_t row = min(r0 + r, d_out - 1);
-      const uint32_t* src = packed + row * row_words + c * BITS;
-      uint32_t w[BITS];
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) w[i] = src[i];
-      float part[BT];
-#pragma unroll
-      for (int b = 0; b < BT; ++b) part[b] = 0.f;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const float q = float(code_at<BITS>(w, k));
-#pragma unroll
-        for (int b = 0; b < BT; ++b) part[b] = __builtin_fmaf(q, xv[b][k], part[b]);
+      if constexpr (PREFETCH) {
+        if (it == 0) issue(0, wn);
       }
-      const float sc = scale[row * ngroups + g], zr = zero[row * ngroups + g];
 #pragma unroll
-      for (int b = 0; b < BT; ++b) acc[r][b] += sc * (part[b] - zr * cs[b]);
+      for (int b = 0; b < NB; ++b) {
+        if constexpr (INT) {
+          cs[b] = __uint_as_float(xw[b][W_MSUM]);
+        } else {
+          float sum = 0.f;
+#pragma unroll
+          for (int k = 0; k < CODES; k += 2)
+            sum += __uint_as_float(xw[b][k]) + __uint_as_float(xw[b][k + 1]);
+          cs[b] = sum;
+        }
+      }
+      if constexpr (!GROUPED) {
+        // the zero-point term of a row-wide grid needs sum_j x2_j
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          float t = INT ? __uint_as_float(xw[b][W_UNIT]) * cs[b] : cs[b];
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+          if (lane == 0) redx[w][b] += t;
+        }
+      }
     }
+    uint32_t wc[G][BITS];
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int r = 0; r < G; ++r)
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) wc[r][i] = wn[r][i];
+      if (it + 1 < steps) issue(it + 1, wn);
+    } else {
+      issue(it, wc);
+    }
+    const int last = min(G, nrows - gi) - 1;
+    const int64_t r0 = rbeg + gi;
+    const int64_t g = GROUPED ? c / (128 / CODES) : 0;
+    float v[NV];
+    group_values<BITS, NB, GROUPED>(wc, scale + r0 * ngroups, zero + r0 * ngroups, ngroups, g, act,
+                                    last, xw, cs, v);
+    const float tot = fold_all<NV>(v, lane);
+    if ((lane & ((64 >> LGV) - 1)) == 0 && gi + vr < nrows) red[w][(gi + vr) * NB + vb] += tot;
   }
-  // wave sums
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      float v = acc[r][b];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-      acc[r][b] = v;
-    }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      if (r0 + r >= d_out) continue;
-#pragma unroll
-      for (int b = 0; b < BT; ++b)
-        if (b < nb) y1[(b0 + b) * d_out + r0 + r] = acc[r][b];
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrows * NB; i += blockDim.x) {
+    const int r = i / NB, b = i % NB;
+    if (b < nb) {
+      float s = 0.f;
+      for (int u = 0; u < nw; ++u) s += red[u][i];
+      if constexpr (!GROUPED) {
+        float xs = 0.f;
+        for (int u = 0; u < nw; ++u) xs += redx[u][b];
+        const int64_t row = rbeg + r;
+        const float zr = zero[row] - code_offset(BITS);  // the products used q - offset
+        s = scale[row] * (s - zr * xs);
+      }
+      y1[(b0 + b) * d_out + rbeg + r] = s;
     }
   }
 }
 
+template <int BITS, int NB>
+void launch_qmatvec_nb(const uint32_t* packed, int64_t rw, const float* scale, const float* zero,
+                       int ngroups, bool grouped, const uint32_t* xq, int64_t nchunk, int64_t d_out,
+                       int b0, int nb, float* y1, hipStream_t s) {
+  const int nkt = int(cdiv(nchunk, LANES));
+  const int nw = std::min(nkt, max_waves(BITS, NB, grouped));
+  // rows per workgroup: the most (up to SLOT / NB) that leave >= 256
+  // workgroups, one per compute unit
+  int rpw = SLOT / NB;
+  while (rpw > G && cdiv(d_out, rpw) < 256) rpw >>= 1;
+  const unsigned blocks = unsigned(cdiv(d_out, rpw));
+  if (grouped)
+    qmatvec_kernel<BITS, NB, true><<<blocks, 64 * nw, 0, s>>>(packed, int(rw), scale, zero, ngroups, xq,
+                                                             nchunk, d_out, nkt, rpw, b0, nb, y1);
+  else
+    qmatvec_kernel<BITS, NB, false><<<blocks, 64 * nw, 0, s>>>(packed, int(rw), scale, zero, ngroups, xq,
+                                                              nchunk, d_out, nkt, rpw, b0, nb, y1);
+}
+
 template <int BITS>
-kq_status launch_qmatvec(const uint32_t* packed, int64_t row_words, const float* scale,
-                         const float* zero, int ngroups, int gchunks, const float* x2,
-                         const float* csum, int64_t d_in, int64_t d_out, int64_t batch, float* y1,
-                         hipStream_t s) {
-  const unsigned blocks = unsigned(cdiv(d_out, 4 * RPW));
-  for (int64_t b0 = 0; b0 < batch; b0 += BT) {
-    const int nb = int(std::min<int64_t>(BT, batch - b0));
-    qmatvec_kernel<BITS><<<blocks, 256, 0, s>>>(packed, row_words, scale, zero, ngroups, gchunks, x2,
-                                               csum, d_in, d_out, int(b0), nb, y1);
+kq_status run_bits(const uint32_t* packed, int64_t rw, const float* scale, const float* zero,
+                   int ngroups, bool grouped, const float* s_x, const int8_t* si, int64_t bi,
+                   const float* x, int64_t batch, int64_t d_out, int64_t d_in, uint32_t* xq,
+                   float* y1, hipStream_t s) {
+  const int64_t Li = transform_len(d_in, bi);
+  const unsigned tin = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Li / 4)));
+  transform_in_kernel<BITS><<<unsigned(batch * (d_in / Li)), tin, 0, s>>>(
+      x, d_in, ilog2(Li), ilog2(bi), si, s_x, float(1.0 / std::sqrt(double(bi))), xq);
+  KQ_HIP(hipGetLastError());
+  const int64_t nchunk = d_in / CODES;
+  KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED, 0, s));
+  for (int64_t b0 = 0; b0 < batch; b0 += 4) {
+    const int nb = int(std::min<int64_t>(4, batch - b0));
+    if (nb == 1)
+      launch_qmatvec_nb<BITS, 1>(packed, rw, scale, zero, ngroups, grouped, xq, nchunk, d_out, int(b0), 1, y1, s);
+    else if (nb == 2)
+      launch_qmatvec_nb<BITS, 2>(packed, rw, scale, zero, ngroups, grouped, xq, nchunk, d_out, int(b0), 2, y1, s);
+    else
+      launch_qmatvec_nb<BITS, 4>(packed, rw, scale, zero, ngroups, grouped, xq, nchunk, d_out, int(b0), nb, y1, s);
     KQ_HIP(hipGetLastError());
   }
-  return KQ_OK;
+  return mark_kernel(KQ_OP_APPLY_QUANTIZED, 1, s);
 }
 
 }  // namespace
@@ -193,11 +596,8 @@ kq_status pack_run(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, 
 
 size_t apply_ws_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
   Arena ar{nullptr, 0, 0};
-  ar.take<float>(size_t(batch) * d_in);        // x2
-  ar.take<float>(size_t(batch) * (d_in / 32));  // chunk sums
-  ar.take<float>(size_t(batch) * d_out);       // y1
-  ar.take<float>(d_in);                        // sign_in / s_x
-  ar.take<float>(d_out);                       // sign_out / s_g
+  ar.take<uint32_t>(size_t(batch) * (d_in / CODES) * XW);  // prepared input chunks
+  ar.take<float>(size_t(batch) * d_out);                   // y1
   return ar.used;
 }
 
@@ -205,31 +605,22 @@ kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const 
                     int group, const float* s_x, const float* s_g, const int8_t* si,
                     const int8_t* so, int64_t bi, int64_t bo, const float* x, int64_t batch,
                     int64_t d_out, int64_t d_in, float* y, Arena& ws, hipStream_t s) {
-  float* x2 = ws.take<float>(size_t(batch) * d_in);
-  float* csum = ws.take<float>(size_t(batch) * (d_in / 32));
+  uint32_t* xq = ws.take<uint32_t>(size_t(batch) * (d_in / CODES) * XW);
   float* y1 = ws.take<float>(size_t(batch) * d_out);
-  float* fin = ws.take<float>(d_in);
-  float* fout = ws.take<float>(d_out);
-  if (!x2 || !csum || !y1 || !fin || !fout) return fail(KQ_ERR_WORKSPACE, "apply_quantized: workspace too small");
-  const int64_t mx = std::max(d_in, d_out);
-  factors_kernel<<<unsigned(cdiv(mx, 256)), 256, 0, s>>>(si, s_x, d_in, so, s_g, d_out, fin, fout);
-  KQ_HIP(hipGetLastError());
-  KQ_HIP(hipMemcpyAsync(x2, x, size_t(batch) * d_in * sizeof(float), hipMemcpyDeviceToDevice, s));
-  KQ_TRY(fwht_rows(x2, batch, d_in, bi, nullptr, fin, float(1.0 / std::sqrt(double(bi))), s));
-  const int64_t nchunk = d_in / 32;
-  chunk_sum_kernel<<<unsigned(cdiv(batch * nchunk, 256)), 256, 0, s>>>(x2, d_in, nchunk, batch, csum);
-  KQ_HIP(hipGetLastError());
+  if (!xq || !y1) return fail(KQ_ERR_WORKSPACE, "apply_quantized: workspace too small");
   const int ngroups = group ? int(d_in / group) : 1;
-  const int gchunks = group ? group / 32 : 0;
+  const bool grouped = group != 0;
   const int64_t rw = packed_row_words(d_in, bits);
   switch (bits) {
-    case 2: KQ_TRY(launch_qmatvec<2>(packed, rw, scale, zero, ngroups, gchunks, x2, csum, d_in, d_out, batch, y1, s)); break;
-    case 3: KQ_TRY(launch_qmatvec<3>(packed, rw, scale, zero, ngroups, gchunks, x2, csum, d_in, d_out, batch, y1, s)); break;
-    case 4: KQ_TRY(launch_qmatvec<4>(packed, rw, scale, zero, ngroups, gchunks, x2, csum, d_in, d_out, batch, y1, s)); break;
-    default: KQ_TRY(launch_qmatvec<8>(packed, rw, scale, zero, ngroups, gchunks, x2, csum, d_in, d_out, batch, y1, s)); break;
+    case 2: KQ_TRY(run_bits<2>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
+    case 3: KQ_TRY(run_bits<3>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
+    case 4: KQ_TRY(run_bits<4>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
+    default: KQ_TRY(run_bits<8>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
   }
-  KQ_TRY(fwht_rows(y1, batch, d_out, bo, nullptr, nullptr, float(1.0 / std::sqrt(double(bo))), s));
-  post_scale_kernel<<<unsigned(cdiv(batch * d_out, 256)), 256, 0, s>>>(y1, fout, d_out, batch, y);
+  const int64_t Lo = transform_len(d_out, bo);
+  const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));
+  transform_out_kernel<<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(
+      y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), y);
   KQ_HIP(hipGetLastError());
   return KQ_OK;
 }

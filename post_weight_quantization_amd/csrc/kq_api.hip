@@ -31,12 +31,13 @@ kq_status hip_fail(hipError_t e, const char* where) {
 void clear_error() { g_err[0] = 0; }
 
 namespace {
-thread_local hipEvent_t g_cov_ev[2] = {nullptr, nullptr};
+// per op: events recorded around the op's main kernel
+thread_local hipEvent_t g_kernel_ev[8][2] = {};
 }
 
 kq_status mark_kernel(kq_op op, int edge, hipStream_t s) {
-  if (op != KQ_OP_ACCUMULATE_COV || g_cov_ev[edge] == nullptr) return KQ_OK;
-  KQ_HIP(hipEventRecord(g_cov_ev[edge], s));
+  if (op < 0 || op >= 8 || g_kernel_ev[op][edge] == nullptr) return KQ_OK;
+  KQ_HIP(hipEventRecord(g_kernel_ev[op][edge], s));
   return KQ_OK;
 }
 
@@ -90,12 +91,13 @@ const char* kq_version(void) { return "kq 0.1 gfx950"; }
 
 kq_status kq_set_kernel_events(kq_op op, hipEvent_t start, hipEvent_t stop) {
   clear_error();
-  if (op != KQ_OP_ACCUMULATE_COV)
-    return fail(KQ_ERR_UNSUPPORTED, "set_kernel_events: only KQ_OP_ACCUMULATE_COV has a timed kernel");
+  if (op != KQ_OP_ACCUMULATE_COV && op != KQ_OP_APPLY_QUANTIZED)
+    return fail(KQ_ERR_UNSUPPORTED,
+                "set_kernel_events: only KQ_OP_ACCUMULATE_COV and KQ_OP_APPLY_QUANTIZED have a timed kernel");
   if ((start == nullptr) != (stop == nullptr))
     return fail(KQ_ERR_ARG, "set_kernel_events: pass both events or neither");
-  g_cov_ev[0] = start;
-  g_cov_ev[1] = stop;
+  g_kernel_ev[op][0] = start;
+  g_kernel_ev[op][1] = stop;
   return KQ_OK;
 }
 

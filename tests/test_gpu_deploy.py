@@ -1,10 +1,13 @@
 """GPU parity of inference with the quantized layer (packing and the product
 y = S_G^-1 U^T W^' V S_X^-1 x) against oracle/deploy.py.
 
-Packing is integer work: bit-exact. The product runs in fp32 with the
-transforms applied to the vectors; against the fp64 reference it is held to
-1e-5 relative (Frobenius over the batch), the size of fp32 rounding over
-sums of d_in terms.
+Packing is integer work: bit-exact. The product applies the transforms to
+the vectors in fp32; 2-, 4- and 8-bit codes multiply a 23-bit fixed-point
+form of each 32-value chunk of the transformed input in integer dot
+products (each value off by at most 2^-23 of the chunk's largest, about
+fp32's own rounding of that value), 3-bit codes multiply in fp32. Against
+the fp64 reference it is held to 1e-5 relative (Frobenius over the batch),
+the size of fp32 rounding over sums of d_in terms.
 """
 import numpy as np
 import pytest
@@ -79,6 +82,38 @@ def test_apply_on_the_pipeline_output():
     # and the product with the de-transformed dequantized layer the sweep returned
     dense = deploy.detransform(host(W), host(s_x), host(s_g), L["sign_in"], L["sign_out"])
     assert rel_fro(host(y), x @ dense.T) < 1e-5
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("group,batch", [(0, 1), (128, 2), (0, 3), (128, 6)])
+def test_apply_ragged(bits, group, batch):
+    # 260 rows: the last row group of a wave is partial; 2176 columns = 68
+    # chunks of 32: two K tiles of 64 lanes, the second with 4 active lanes;
+    # batches 1, 2, 3 and 6 take every vector-count variant (6 = 4 + 2)
+    rng = np.random.default_rng(1000 * bits + 10 * batch + group)
+    c = _case(260, 2176, bits, group, rng)
+    x = rng.standard_normal((batch, 2176)).astype(np.float32)
+    got, want = _run(*c, bits, group, x)
+    assert rel_fro(got, want) < 1e-5
+
+
+@pytest.mark.parametrize("bits", [2, 3, 8])
+def test_apply_dynamic_range(bits):
+    # Hadamard blocks of 32 keep every 32-column chunk of the transformed
+    # input at its own magnitude: chunks from 1e-6 to 1e6, and all-zero
+    # chunks, so each chunk's own exponent in the integer products matters
+    rng = np.random.default_rng(77 + bits)
+    d_out, d_in, batch = 128, 4096, 3
+    c = _case(d_out, d_in, bits, 0, rng)
+    mag = 10.0 ** rng.uniform(-6, 6, (batch, d_in // 32))
+    mag[:, ::7] = 0.0
+    x = (rng.standard_normal((batch, d_in)) * np.repeat(mag, 32, axis=1)).astype(np.float32)
+    got, want = _run(*c, bits, 0, x, bi=32, bo=0)
+    assert rel_fro(got, want) < 1e-5
+    # rows are dominated by the largest chunks: check a small-input vector too
+    x2 = (rng.standard_normal((1, d_in)) * 1e-30).astype(np.float32)
+    got2, want2 = _run(*c, bits, 0, x2, bi=32, bo=0)
+    assert rel_fro(got2, want2) < 1e-5
 
 
 @pytest.mark.slow
