@@ -150,8 +150,48 @@ def run_gpu(spec, steps, warmup, data):
         print(f"objective check failed: {e}", file=sys.stderr)
         obj_rtn = None
     inf = run_inference(spec, codes, scale, zero, s_x, s_g, si, so)
+    cap = run_streaming(spec, X, Xq, G, HX, D, HG, ws)
     return dict(wall_s=wall, stage_ms=stage_ms, cov_kernel_ms=cov_kernel_ms, sens=sens, obj=obj,
-                obj_rtn=obj_rtn, inference=inf)
+                obj_rtn=obj_rtn, inference=inf, streaming=cap)
+
+
+def run_streaming(spec, X, Xq, G, HX, D, HG, ws, chunk=16384, reps=3):
+    """Covariances of the same tokens streamed in chunks (the way a capture
+    of calibration batches feeds them: beta = 0, then 1) against one call."""
+    import torch
+
+    import post_weight_quantization_amd as kq
+
+    from post_weight_quantization_amd import _native as N
+
+    n = spec.n_tok
+    if n % chunk:
+        return None
+    stream = torch.cuda.current_stream()
+    dt = N.KQ_F32 if spec.dtype == "f32" else N.KQ_BF16
+    need = max(kq.kq_workspace_size(N.KQ_OP_ACCUMULATE_COV, spec.d_out, spec.d_in, c, dt) for c in (n, chunk))
+    if ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=ws.device)
+
+    def once(c):
+        for k in range(0, n, c):
+            kq.kq_accumulate_cov(X[k:k + c], Xq[k:k + c], G[k:k + c], 1.0 / n, 0.0 if k == 0 else 1.0,
+                                 HX, D, HG, ws=ws)
+
+    res = {}
+    for c in (n, chunk):
+        once(c)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            once(c)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        res[c] = ev[0].elapsed_time(ev[1]) / reps
+    return {"tokens": n, "chunk_tokens": chunk, "chunks": n // chunk,
+            "chunked_ms": round(res[chunk], 3), "single_call_ms": round(res[n], 3),
+            "chunked_mtok_s": round(n / res[chunk] / 1e3, 2)}
 
 
 def time_apply(packed, bits, scale, zero, group, s_x, s_g, si, so, d_out, d_in, batch, reps=20):
@@ -340,6 +380,7 @@ def main():
         "objective": g["obj"], "objective_rtn": g["obj_rtn"],
         "cpu_baseline": cpu,
         "inference": g["inference"],
+        "streaming_covariances": g["streaming"],
     }
     print(json.dumps(out))
 

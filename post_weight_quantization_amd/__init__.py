@@ -2,10 +2,13 @@
 
 The computation lives in libkq.so (HIP kernels behind the C ABI of
 include/kq.h). ``api`` is a thin torch binding with the same entry-point
-names; ``layer`` chains the entry points for one layer. Importing this
+names; ``layer`` chains the entry points for one layer; ``capture`` feeds
+the covariance entry point from a torch model's forward and backward hooks.
+Importing this
 package raises if the library has not been built.
 """
-from . import layer  # noqa: F401
+from . import capture, layer  # noqa: F401
+from .capture import CovarianceCapture  # noqa: F401
 from ._native import KQError, LIB_PATH  # noqa: F401
 from .api import (  # noqa: F401
     kq_accumulate_cov,
