@@ -22,6 +22,10 @@
 //      sums meet in LDS and are added in wave order (no atomics);
 //   3. transform_out: FWHT of each output block of y1, then sign_out / s_g
 //      and 1 / sqrt(b).
+// 2-bit codes with one grid per row (d_in a multiple of 512: the workloads'
+// setting) take the matrix-core path further down: the codes are fp4
+// operands of v_mfma_scale_f32_16x16x128_f8f6f4 as they stand and the input
+// enters as fp8 digits with E8M0 block scales. The rest:
 // Products: for 2-, 4- and 8-bit codes in integers. Each chunk of x2 is held
 // in fixed point against its own largest magnitude: with 2^(e-1) <=
 // max |x_k| < 2^e, m_k = rint(x_k 2^(22 - e)), |m_k| <= 2^22, and x_k =
@@ -578,6 +582,268 @@ kq_status run_bits(const uint32_t* packed, int64_t rw, const float* scale, const
   return mark_kernel(KQ_OP_APPLY_QUANTIZED, 1, s);
 }
 
+
+// ---------------------------------------------------------------------------
+// Matrix-core path for 2-bit codes with one grid per row (d_in a multiple of
+// 512): v_mfma_scale_f32_16x16x128_f8f6f4, A = codes as fp4 (e2m1), B = the
+// transformed input as fp8 (e4m3) digits with E8M0 block scales.
+//
+// Operand layout of the instruction (16 x 16 x 128; lane l, G = l / 16):
+//   A: row l % 16, K 32 G + j in nibble j of its first four registers;
+//   B: column l % 16, K 16 G + (j % 16) + 64 (j / 16) in byte j;
+//   scale byte of lane l (selected by op_sel): K block G (32 values) of its
+//   row (A) or column (B); C: lane l holds rows 4 G + i, column l % 16.
+// The e2m1 encodings 0-3 are the values 0, 0.5, 1, 1.5: a 2-bit code q is
+// the fp4 value q / 2 as it stands, so the decode is two nibble masks per
+// packed word (0x33333333 after shifts of 0 and 2).
+// Codes: over a super-step of 512 columns a lane (row r, G) reads codes
+// 64 G .. 64 G + 63 and 256 + 64 G .. 256 + 64 G + 63 (two 16-byte loads;
+// each load instruction covers 64 contiguous bytes of 16 rows), and step
+// q = 2 h + o takes the 32 codes from 256 h + 64 G + 32 o; nibble j holds
+// code p(j) = 2 i + (j / 8 odd) + 16 (j >= 16) of them, i = j % 8.
+// Input: each 32-value chunk in fixed point against its own exponent e
+// (m = rint(x 2^(22 - e)), as in the integer path), m = sum_l n_l 16^l with
+// six digits n_l in [-8, 7], exact in e4m3. Column n = 6 v + l of B holds
+// digit l of vector v; its block scale is 2^(4 l + e - 21) (the 2 undoes the
+// halved codes). The instruction's sum is then sum_k q_k x_k, to fp32
+// accumulation (measured error <= 2^-23 of the sum of |terms|).
+constexpr int MX_SS = 512;         // columns per super-step
+constexpr int MX_DIG = 6;          // digits per value
+constexpr int MX_BYTES = 4 * 4 * MX_DIG * 32;  // digit bytes per super-step and vector
+constexpr int MX_SCALES = 4 * MX_DIG;          // scale words per super-step and vector
+
+// e4m3 encodings of the integers -8 .. 7 (index n + 8)
+__device__ __constant__ uint8_t kE4M3Int[16] = {0xD0, 0xCE, 0xCC, 0xCA, 0xC8, 0xC4, 0xC0, 0xB8,
+                                                0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E};
+
+// x2 = gain * H_blk (x[b] sign_in / s_x) over L columns, written as B digits
+// xb[b][S][q][g][l][32 bytes], scale words xs[b][S][G][l] (byte q) and the
+// chunk's sum of x2 in xsum[b][blockIdx % per_row].
+__global__ __launch_bounds__(1024) void transform_in_mx_kernel(
+    const float* __restrict__ x, int64_t d_in, int lgL, int lgb, const int8_t* __restrict__ si,
+    const float* __restrict__ s_x, float gain, uint8_t* __restrict__ xb, uint32_t* __restrict__ xs,
+    float* __restrict__ xsum) {
+  __shared__ float s[TCHP];
+  __shared__ __align__(16) uint8_t dig[TCH * MX_DIG];  // digit bytes in output order
+  __shared__ uint32_t scl[TCH / 32 * MX_DIG];
+  __shared__ float part[32];
+  const int L = 1 << lgL;
+  const int64_t per_row = d_in >> lgL;
+  const int64_t b = blockIdx.x / per_row;
+  const int64_t c0 = int64_t(blockIdx.x % per_row) << lgL;
+  const float* src = x + b * d_in + c0;
+  for (int e = 4 * threadIdx.x; e < L; e += 4 * blockDim.x) {
+    const float4 v = *reinterpret_cast<const float4*>(src + e);
+    const float4 sx = *reinterpret_cast<const float4*>(s_x + c0 + e);
+    s[padi(e)] = v.x * float(si[c0 + e]) / sx.x;
+    s[padi(e + 1)] = v.y * float(si[c0 + e + 1]) / sx.y;
+    s[padi(e + 2)] = v.z * float(si[c0 + e + 2]) / sx.z;
+    s[padi(e + 3)] = v.w * float(si[c0 + e + 3]) / sx.w;
+  }
+  for (int i = threadIdx.x; i < L / 32 * MX_DIG; i += blockDim.x) scl[i] = 0u;
+  __syncthreads();
+  lds_fwht(s, L, 0, lgb);
+  float tsum = 0.f;
+  // one value per lane; the 32 lanes of a half-wave hold one chunk
+  for (int e = threadIdx.x; e < L; e += blockDim.x) {
+    const float v = gain * s[padi(e)];
+    tsum += v;
+    float mx = fabsf(v);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    int ex = 0;
+    if (mx > 0.f) frexpf(mx, &ex);  // mx = f 2^ex, 1/2 <= f < 1
+    // chunks whose smallest digit scale would fall below E8M0's range hold
+    // values under 2^-148: taken as zero
+    const bool keep = mx > 0.f && ex - 21 >= -127;
+    const int m = keep ? int(rintf(ldexpf(v, 22 - ex))) : 0;
+    // position of this code in the operand layout
+    const int u = e & (MX_SS - 1), S = e / MX_SS;
+    const int G = (u >> 6) & 3, q = 2 * (u >> 8) + ((u >> 5) & 1), p = u & 31;
+    const int j = 8 * (2 * (p >> 4) + (p & 1)) + ((p & 15) >> 1);
+    const int k = 32 * G + j;
+    const int g = (k & 63) >> 4, jb = (k & 15) + 16 * (k >> 6);
+    int r = m;
+#pragma unroll
+    for (int l = 0; l < MX_DIG; ++l) {
+      const int n = ((r + 8) & 15) - 8;  // balanced base-16 digit
+      r = (r - n) >> 4;
+      dig[(((S * 4 + q) * 4 + g) * MX_DIG + l) * 32 + jb] = kE4M3Int[n + 8];
+    }
+    if ((e & 31) == 0) {
+#pragma unroll
+      for (int l = 0; l < MX_DIG; ++l) {
+        const uint32_t sc = keep ? uint32_t(127 + 4 * l + ex - 21) : 0u;
+        atomicOr(&scl[(S * 4 + G) * MX_DIG + l], sc << (8 * q));
+      }
+    }
+  }
+  // workgroup sum of x2 (fixed order: lanes, then waves)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = tsum;
+  __syncthreads();
+  const int64_t nss = d_in / MX_SS, S0 = c0 / MX_SS;
+  uint8_t* dstb = xb + (b * nss + S0) * MX_BYTES;
+  for (int i = 16 * threadIdx.x; i < L / MX_SS * MX_BYTES; i += 16 * blockDim.x)
+    *reinterpret_cast<uint4*>(dstb + i) = *reinterpret_cast<const uint4*>(dig + i);
+  uint32_t* dsts = xs + (b * nss + S0) * MX_SCALES;
+  for (int i = threadIdx.x; i < L / MX_SS * MX_SCALES; i += blockDim.x) dsts[i] = scl[i];
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < int(blockDim.x >> 6); ++w) t += part[w];
+    xsum[b * per_row + blockIdx.x % per_row] = t;
+  }
+}
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+// y1[b0 + v][rows] = scale (W^' x2 - zero sum x2) for v < NV, rows
+// blockIdx.x * rpw .. + rpw - 1 (a multiple of 16). K ranges of RK
+// super-steps; wave w takes ranges w, w + waves, ... and holds a range's B
+// operands in registers while it streams the rows.
+template <int NV, int RK>
+__global__ __launch_bounds__(1024) void qmatvec_mx_kernel(
+    const uint32_t* __restrict__ packed, int rw, const float* __restrict__ scale,
+    const float* __restrict__ zero, const uint8_t* __restrict__ xb, const uint32_t* __restrict__ xs,
+    const float* __restrict__ xsum, int nparts, int64_t nss, int64_t d_out, int nkr, int rpw, int b0,
+    int64_t batch, float* __restrict__ y1) {
+  __shared__ float red[16][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int64_t rbeg = int64_t(blockIdx.x) * rpw;
+  const int nrows = int(min(int64_t(rpw), d_out - rbeg));
+  for (int i = lane; i < 64; i += 64) red[w][i] = 0.f;
+  const int n = lane & 15, G = lane >> 4;
+  const bool bcol = n < MX_DIG * NV;  // columns past the vectors' digits stay zero
+  const int vcol = bcol ? n / MX_DIG : 0, lcol = n % MX_DIG;
+  // The wave's items: its K ranges (w, w + nw, ...) times the 16-row tiles,
+  // ranges outer. The codes of item it + 1 load while item it computes; a
+  // range's B operands load when the range starts.
+  const int ntile = (nrows + 15) / 16;
+  const int items = ((nkr - 1 - w) / nw + 1) * ntile;
+  auto load_a = [&](int it, uint4 (&dst)[RK][2]) {
+    const int kr = w + (it / ntile) * nw, t0 = (it % ntile) * 16;
+    const int64_t row = rbeg + min(t0 + n, nrows - 1);  // past the end: the last row, not stored
+#pragma unroll
+    for (int t = 0; t < RK; ++t) {
+      const int64_t S = min(int64_t(kr) * RK + t, nss - 1);  // past the end: unused
+      const uint4* ap = reinterpret_cast<const uint4*>(packed + row * rw + S * (MX_SS / 16) + G * 4);
+      dst[t][0] = ap[0];  // codes 64 G .. 64 G + 63 of the super-step
+      dst[t][1] = ap[4];  // codes 256 + 64 G .. 256 + 64 G + 63
+    }
+  };
+  v8i_t bop[RK][4];
+  uint32_t bsc[RK];
+  uint4 an[RK][2];
+  load_a(0, an);
+  int cur_kr = -1;
+  for (int it = 0; it < items; ++it) {
+    const int kr = w + (it / ntile) * nw, t0 = (it % ntile) * 16;
+    if (kr != cur_kr) {
+      cur_kr = kr;
+#pragma unroll
+      for (int t = 0; t < RK; ++t) {
+        const int64_t S = int64_t(kr) * RK + t;
+        const bool ok = bcol && S < nss;
+        const uint8_t* bp = xb + ((b0 + vcol) * nss + (ok ? S : 0)) * MX_BYTES;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4* p = reinterpret_cast<const uint4*>(bp + ((q * 4 + G) * MX_DIG + lcol) * 32);
+          const uint4 lo = ok ? p[0] : make_uint4(0u, 0u, 0u, 0u);
+          const uint4 hi = ok ? p[1] : make_uint4(0u, 0u, 0u, 0u);
+          bop[t][q] = v8i_t{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        }
+        bsc[t] = ok ? xs[((b0 + vcol) * nss + S) * MX_SCALES + G * MX_DIG + lcol] : 0u;
+      }
+    }
+    uint4 ac[RK][2];
+#pragma unroll
+    for (int t = 0; t < RK; ++t) {
+      ac[t][0] = an[t][0];
+      ac[t][1] = an[t][1];
+    }
+    if (it + 1 < items) load_a(it + 1, an);
+    v4f_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < RK; ++t) {
+      if (int64_t(kr) * RK + t >= nss) break;
+      const uint32_t wd[8] = {ac[t][0].x, ac[t][0].y, ac[t][0].z, ac[t][0].w,
+                              ac[t][1].x, ac[t][1].y, ac[t][1].z, ac[t][1].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x0 = wd[2 * q], x1 = wd[2 * q + 1];
+        const v8i_t aop = {int(x0 & 0x33333333u), int((x0 >> 2) & 0x33333333u),
+                           int(x1 & 0x33333333u), int((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+        if (q == 0) acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][0], acc, 4, 0, 0, 0x7f7f7f7f, 0, int(bsc[t]));
+        if (q == 1) acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][1], acc, 4, 0, 0, 0x7f7f7f7f, 1, int(bsc[t]));
+        if (q == 2) acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][2], acc, 4, 0, 0, 0x7f7f7f7f, 2, int(bsc[t]));
+        if (q == 3) acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][3], acc, 4, 0, 0, 0x7f7f7f7f, 3, int(bsc[t]));
+      }
+    }
+    // acc[i] = C[4 G + i][n]: add the digit columns of each vector
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float t = (bcol && vcol == v) ? acc[i] : 0.f;
+        t += __shfl_xor(t, 8);
+        t += __shfl_xor(t, 4);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 1);
+        const int r = t0 + 4 * G + i;
+        if (n == 0 && r < nrows) red[w][r * NV + v] += t;
+      }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrows * NV; i += blockDim.x) {
+    const int r = i / NV, v = i % NV;
+    float acc = 0.f;
+    for (int u = 0; u < nw; ++u) acc += red[u][i];
+    float xs_sum = 0.f;
+    for (int pp = 0; pp < nparts; ++pp) xs_sum += xsum[(b0 + v) * nparts + pp];
+    const int64_t row = rbeg + r;
+    y1[(b0 + v) * d_out + row] = scale[row] * (acc - zero[row] * xs_sum);
+  }
+}
+
+template <int NV>
+void launch_qmatvec_mx(const uint32_t* packed, int64_t rw, const float* scale, const float* zero,
+                       const uint8_t* xb, const uint32_t* xs, const float* xsum, int nparts,
+                       int64_t nss, int64_t d_out, int b0, int64_t batch, float* y1, hipStream_t s) {
+  constexpr int RK = 2;
+  const int nkr = int(cdiv(nss, RK));
+  // waves per workgroup: the largest divisor of the range count up to 16
+  int nw = std::min(nkr, 16);
+  while (nkr % nw) --nw;
+  // rows per workgroup: 32 (two 16-row tiles) unless that leaves < 256 workgroups
+  const int rpw = cdiv(d_out, 32) >= 256 ? 32 : 16;
+  qmatvec_mx_kernel<NV, RK><<<unsigned(cdiv(d_out, rpw)), 64 * nw, 0, s>>>(
+      packed, int(rw), scale, zero, xb, xs, xsum, nparts, nss, d_out, nkr, rpw, b0, batch, y1);
+}
+
+kq_status run_mx(const uint32_t* packed, int64_t rw, const float* scale, const float* zero,
+                 const float* s_x, const int8_t* si, int64_t bi, const float* x, int64_t batch,
+                 int64_t d_out, int64_t d_in, uint8_t* xb, uint32_t* xs, float* xsum, float* y1,
+                 hipStream_t s) {
+  const int64_t Li = transform_len(d_in, bi);
+  const int64_t nss = d_in / MX_SS, nparts = d_in / Li;
+  transform_in_mx_kernel<<<unsigned(batch * nparts), unsigned(std::min<int64_t>(1024, Li / 4)), 0, s>>>(
+      x, d_in, ilog2(Li), ilog2(bi), si, s_x, float(1.0 / std::sqrt(double(bi))), xb, xs, xsum);
+  KQ_HIP(hipGetLastError());
+  KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED, 0, s));
+  for (int64_t b0 = 0; b0 < batch; b0 += 2) {
+    if (batch - b0 >= 2)
+      launch_qmatvec_mx<2>(packed, rw, scale, zero, xb, xs, xsum, int(nparts), nss, d_out, int(b0), batch, y1, s);
+    else
+      launch_qmatvec_mx<1>(packed, rw, scale, zero, xb, xs, xsum, int(nparts), nss, d_out, int(b0), batch, y1, s);
+    KQ_HIP(hipGetLastError());
+  }
+  return mark_kernel(KQ_OP_APPLY_QUANTIZED, 1, s);
+}
+
 }  // namespace
 
 int64_t packed_row_words(int64_t d_in, int bits) {
@@ -594,10 +860,21 @@ kq_status pack_run(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, 
   return KQ_OK;
 }
 
+// The matrix-core path (2-bit codes, one grid per row, d_in % 512 == 0)
+bool use_mx(int bits, int group, int64_t d_in) { return bits == 2 && group == 0 && d_in % MX_SS == 0; }
+
 size_t apply_ws_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
-  Arena ar{nullptr, 0, 0};
-  ar.take<uint32_t>(size_t(batch) * (d_in / CODES) * XW);  // prepared input chunks
-  ar.take<float>(size_t(batch) * d_out);                   // y1
+  // the larger of the two prepared-input forms, then y1
+  Arena a1{nullptr, 0, 0};
+  a1.take<uint32_t>(size_t(batch) * (d_in / CODES) * XW);  // prepared input chunks
+  Arena a2{nullptr, 0, 0};
+  if (d_in % MX_SS == 0) {
+    a2.take<uint8_t>(size_t(batch) * (d_in / MX_SS) * MX_BYTES);     // B digits
+    a2.take<uint32_t>(size_t(batch) * (d_in / MX_SS) * MX_SCALES);  // B scales
+    a2.take<float>(size_t(batch) * (d_in / MX_SS));                 // sums of x2
+  }
+  Arena ar{nullptr, 0, std::max(a1.used, a2.used)};
+  ar.take<float>(size_t(batch) * d_out);  // y1
   return ar.used;
 }
 
@@ -605,17 +882,28 @@ kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const 
                     int group, const float* s_x, const float* s_g, const int8_t* si,
                     const int8_t* so, int64_t bi, int64_t bo, const float* x, int64_t batch,
                     int64_t d_out, int64_t d_in, float* y, Arena& ws, hipStream_t s) {
-  uint32_t* xq = ws.take<uint32_t>(size_t(batch) * (d_in / CODES) * XW);
+  const int64_t rw = packed_row_words(d_in, bits);
+  const size_t front = apply_ws_bytes(d_out, d_in, batch) - size_t(batch) * d_out * sizeof(float);
+  char* base = ws.take<char>(front);
   float* y1 = ws.take<float>(size_t(batch) * d_out);
-  if (!xq || !y1) return fail(KQ_ERR_WORKSPACE, "apply_quantized: workspace too small");
+  if (!base || !y1) return fail(KQ_ERR_WORKSPACE, "apply_quantized: workspace too small");
+  if (use_mx(bits, group, d_in)) {
+    Arena fa{base, front, 0};
+    uint8_t* xb = fa.take<uint8_t>(size_t(batch) * (d_in / MX_SS) * MX_BYTES);
+    uint32_t* xs = fa.take<uint32_t>(size_t(batch) * (d_in / MX_SS) * MX_SCALES);
+    float* xsum = fa.take<float>(size_t(batch) * (d_in / MX_SS));
+    if (!xb || !xs || !xsum) return fail(KQ_ERR_WORKSPACE, "apply_quantized: workspace too small");
+    KQ_TRY(run_mx(packed, rw, scale, zero, s_x, si, bi, x, batch, d_out, d_in, xb, xs, xsum, y1, s));
+  } else {
+  uint32_t* xq = reinterpret_cast<uint32_t*>(base);
   const int ngroups = group ? int(d_in / group) : 1;
   const bool grouped = group != 0;
-  const int64_t rw = packed_row_words(d_in, bits);
   switch (bits) {
     case 2: KQ_TRY(run_bits<2>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
     case 3: KQ_TRY(run_bits<3>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
     case 4: KQ_TRY(run_bits<4>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
     default: KQ_TRY(run_bits<8>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
+  }
   }
   const int64_t Lo = transform_len(d_out, bo);
   const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));
