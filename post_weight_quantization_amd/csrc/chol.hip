@@ -23,6 +23,7 @@
 #include "kq_internal.h"
 
 #include <climits>
+#include <utility>
 
 namespace kq {
 
@@ -66,22 +67,61 @@ __device__ inline void wave_lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Cholesky of the 32 x 32 block at (C0, C0) of As and its inverse, in
-// registers. Wave 0 only: lane r (and its copy r + 32) holds row r of the
-// block (x) and row r of Y, which starts as the identity. Step j eliminates
-// column j from the rows below with multipliers x_r[j] / piv_j (row j's
-// entries come from column j by symmetry) and applies the same row
-// operations to Y, so that at the end Y = L_u^-1 for A = L_u D L_u^T.
-// Then L = L_u D^(1/2): L[r][j] = x_r[j] / sqrt(piv_j), and
-// L^-1 = D^(-1/2) Y. Broadcasts are readlanes; nothing on the step's
-// dependent chain goes through LDS.
-__device__ void leaf_diag32(float* As, float* Xs, int64_t k0, int* info, int C0) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 31;
-  float x[32], y[32], dv[32];
-  const float* row = As + (C0 + r) * LS + C0;
+// Broadcast of lane J of each 16-lane row (DPP row_newbcast) to that row.
+template <int J>
+__device__ inline float bc16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + J,
+                                                            0xF, 0xF, true));
+}
+
+// x[J + 1 + K] += nmm * (entry (J + 1 + K, J): lane J + 1 + K's x[J], the
+// symmetric mirror of row J's entry), nmm = minus the row's multiplier
+template <int J, int... K>
+__device__ inline void chol16_upd_x(float (&x)[16], float nmm, std::integer_sequence<int, K...>) {
+  ((x[J + 1 + K] = __builtin_fmaf(bc16<J + 1 + K>(x[J]), nmm, x[J + 1 + K])), ...);
+}
+
+// y[K] += nmm * (row J of Y: lane J's y[K]), K <= J
+template <int J, int... K>
+__device__ inline void chol16_upd_y(float (&y)[16], float nmm, std::integer_sequence<int, K...>) {
+  ((y[K] = __builtin_fmaf(bc16<J>(y[K]), nmm, y[K])), ...);
+}
+
+// Step J of the 16 x 16 elimination: the pivot is lane J's x[J]; the rows
+// below take multipliers x_r[J] / piv, and the same row operations apply to
+// Y. Only the lower triangle of the block is ever read.
+template <int J>
+struct Chol16 {
+  __device__ static void run(float (&x)[16], float (&y)[16], float (&dv)[16], int r, int col0,
+                             int* info) {
+    float piv = bc16<J>(x[J]);
+    if (!(piv > 0.f)) {  // non-positive or NaN pivot
+      if ((threadIdx.x & 63) == 0) atomicMin(info, col0 + J + 1);
+      piv = 1.f;
+    }
+    const float nmm = r > J ? -(x[J] * __builtin_amdgcn_rcpf(piv)) : 0.f;  // minus the multiplier
+    chol16_upd_x<J>(x, nmm, std::make_integer_sequence<int, 15 - J>{});
+    chol16_upd_y<J>(y, nmm, std::make_integer_sequence<int, J + 1>{});
+    dv[J] = __builtin_amdgcn_sqrtf(piv);  // 1-ulp hardware square root
+    Chol16<J + 1>::run(x, y, dv, r, col0, info);
+  }
+};
+template <>
+struct Chol16<16> {
+  __device__ static void run(float (&)[16], float (&)[16], float (&)[16], int, int, int*) {}
+};
+
+// Cholesky and inverse of the 16 x 16 block at (R0, R0) of As (row stride
+// LS), one row per lane (lane r % 16 holds row r; the four 16-lane rows of
+// the wave hold copies): A = L_u D L_u^T by elimination with Y = L_u^-1,
+// then L[r][k] = x_r[k] / sqrt(piv_k) and L^-1 = D^(-1/2) Y. Lanes below 16
+// write L (zeros above the diagonal) to As and L^-1 to Xs.
+__device__ inline void chol16_block(float* As, float* Xs, int R0, int col0, int* info) {
+  const int r = threadIdx.x & 15;
+  float x[16], y[16], dv[16];
+  const float* row = As + (R0 + r) * LS + R0;
 #pragma unroll
-  for (int k = 0; k < 32; k += 4) {
+  for (int k = 0; k < 16; k += 4) {
     const float4 v = *reinterpret_cast<const float4*>(row + k);
     x[k] = v.x;
     x[k + 1] = v.y;
@@ -89,33 +129,113 @@ __device__ void leaf_diag32(float* As, float* Xs, int64_t k0, int* info, int C0)
     x[k + 3] = v.w;
   }
 #pragma unroll
-  for (int k = 0; k < 32; ++k) y[k] = k == r ? 1.f : 0.f;
+  for (int k = 0; k < 16; ++k) y[k] = k == r ? 1.f : 0.f;
+  Chol16<0>::run(x, y, dv, r, col0, info);
+  float dr = dv[0];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    float piv = lane_value(x[j], j);
-    if (!(piv > 0.f)) {  // non-positive or NaN pivot
-      if (lane == 0) atomicMin(info, int(k0 + C0 + j) + 1);
-      piv = 1.f;
-    }
-    const float ip = __builtin_amdgcn_rcpf(piv);
-    const float mm = r > j ? x[j] * ip : 0.f;
+  for (int k = 1; k < 16; ++k) dr = r == k ? dv[k] : dr;
+  const float idr = __builtin_amdgcn_rcpf(dr);
+  if ((threadIdx.x & 63) < 16) {
+    float* lrow = As + (R0 + r) * LS + R0;
+    float* xrow = Xs + (R0 + r) * LS + R0;
 #pragma unroll
-    for (int k = j + 1; k < 32; ++k) x[k] = __builtin_fmaf(-mm, lane_value(x[j], k), x[k]);
-#pragma unroll
-    for (int k = 0; k <= j; ++k) y[k] = __builtin_fmaf(-mm, lane_value(y[k], j), y[k]);
-    dv[j] = __builtin_amdgcn_sqrtf(piv);  // 1-ulp hardware square root
-  }
-  if (lane < 32) {
-    float* lrow = As + (C0 + r) * LS + C0;
-    float* xrow = Xs + (C0 + r) * LS + C0;
-    float dr = dv[0];
-#pragma unroll
-    for (int k = 1; k < 32; ++k) dr = r == k ? dv[k] : dr;
-    const float idr = __builtin_amdgcn_rcpf(dr);
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < 16; ++k) {
       lrow[k] = k < r ? x[k] * __builtin_amdgcn_rcpf(dv[k]) : (k == r ? dr : 0.f);
       xrow[k] = k <= r ? y[k] * idr : 0.f;
+    }
+  }
+}
+
+// Cholesky of the 32 x 32 block at (C0, C0) of As and its inverse (wave 0):
+// two 16 x 16 factors with 16 x 16 products between them,
+//   L11 X11 = chol(A11), L21 = A21 X11^T, A22 -= L21 L21^T,
+//   L22 X22 = chol(A22), X21 = -X22 (L21 X11).
+// The products take lane l = (r, column group): row r = l % 16, columns
+// 4 (l / 16) .. + 3, reading their operands from LDS.
+__device__ void leaf_diag32(float* As, float* Xs, int64_t k0, int* info, int C0) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c0 = 4 * (lane >> 4);
+  const int col0 = int(k0) + C0;
+  chol16_block(As, Xs, C0, col0, info);
+  wave_lds_fence();
+  // L21[r][c] = sum_{k <= c} A21[r][k] X11[c][k]
+  float a[16];
+  {
+    const float* arow = As + (C0 + 16 + r) * LS + C0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a[k] = arow[k];
+  }
+  float l21[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float* xr = Xs + (C0 + c0 + q) * LS + C0;
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t = __builtin_fmaf(a[k], xr[k], t);  // X11 is zero above its diagonal
+    l21[q] = t;
+  }
+  wave_lds_fence();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) As[(C0 + 16 + r) * LS + C0 + c0 + q] = l21[q];
+  wave_lds_fence();
+  // A22[r][c] -= sum_k L21[r][k] L21[c][k] (lower triangle used)
+  {
+    float lr[16];
+    const float* lrow = As + (C0 + 16 + r) * LS + C0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lr[k] = lrow[k];
+    float upd[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* lc = As + (C0 + 16 + c0 + q) * LS + C0;
+      float t = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) t = __builtin_fmaf(lr[k], lc[k], t);
+      upd[q] = t;
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) As[(C0 + 16 + r) * LS + C0 + 16 + c0 + q] -= upd[q];
+  }
+  wave_lds_fence();
+  chol16_block(As, Xs, C0 + 16, col0 + 16, info);
+  wave_lds_fence();
+  // T = L21 X11 (T[r][c] = sum_{k >= c} L21[r][k] X11[k][c]), then X21 = -X22 T
+  {
+    float lr[16];
+    const float* lrow = As + (C0 + 16 + r) * LS + C0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lr[k] = lrow[k];
+    float t4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float t = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) t = __builtin_fmaf(lr[k], Xs[(C0 + k) * LS + C0 + c0 + q], t);
+      t4[q] = t;
+    }
+    // T goes to the unused upper-right block of Xs (rows 0..15, columns 16..31)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Xs[(C0 + r) * LS + C0 + 16 + c0 + q] = t4[q];
+    wave_lds_fence();
+    float xr[16];
+    const float* x22 = Xs + (C0 + 16 + r) * LS + C0 + 16;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) xr[k] = x22[k];  // zero above the diagonal
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float t = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) t = __builtin_fmaf(xr[k], Xs[(C0 + k) * LS + C0 + 16 + c0 + q], t);
+      o[q] = -t;
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      Xs[(C0 + 16 + r) * LS + C0 + c0 + q] = o[q];
+      Xs[(C0 + r) * LS + C0 + 16 + c0 + q] = 0.f;  // upper-right of X back to zero
+      As[(C0 + r) * LS + C0 + 16 + c0 + q] = 0.f;  // and of L
     }
   }
 }
