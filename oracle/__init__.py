@@ -12,11 +12,13 @@ gist.science) and cites the passage it follows. Where the pages leave a step
 open, the reading taken is stated next to the code.
 
 Parity pins: each function here is checked by ``tests/test_oracle_pins.py``
+(``tests/test_oracle_yaqa.py`` for the rounding with output-side feedback)
 against closed forms, brute force or library routines. One result is
 "parity unpinned" beyond the oracle itself: the exact integer codes of the
 full-size workloads, since the pages print no worked example.
 """
 from . import deploy  # noqa: F401
+from . import yaqa  # noqa: F401
 from .kronq import (  # noqa: F401
     allocate_bits,
     apply_hadamard_left,
