@@ -63,7 +63,8 @@ typedef enum {
   KQ_OP_FORM_P = 4,
   KQ_OP_GPTAQ_QUANTIZE = 5,
   KQ_OP_LAYER_OBJECTIVE = 6,
-  KQ_OP_APPLY_QUANTIZED = 7  /* n_tok argument of kq_workspace_size = batch */
+  KQ_OP_APPLY_QUANTIZED = 7, /* n_tok argument of kq_workspace_size = batch */
+  KQ_OP_YAQA_QUANTIZE = 8
 } kq_op;
 
 /* Grid and sweep configuration (KronQ summary, Method and experiments:
@@ -193,6 +194,36 @@ kq_status kq_gptaq_quantize(float* W, const float* U, const float* D,
                             int64_t d_out, int64_t d_in, const kq_quant_cfg* cfg,
                             uint8_t* codes, float* scale, float* zero,
                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Rounding with output-side feedback: the generalized LDLQ of YAQA (notes on
+ * YAQA, arXiv 2505.22988, section "key designs", item 4, Eq. 5/6: for a
+ * Kronecker sketch H_O (x) H_I the codes are the fixed point of
+ * W = Q(W* + L_O'^T Dl L_I' + L_O'^T Dl + Dl L_I'), Dl = W* - W, L' = L - I
+ * with L the unit-triangular LDL factor; item 1: it settles within
+ * d_out + d_in - 1 steps), on KronQ's sketch H_G' (x) H_X'. In terms of the
+ * inverse factors the rounded input of entry (i, j) is
+ *   z_ij = W*_ij - sum_{k<=i, l<=j, (k,l)!=(i,j)} U_out[k][i] e_kl U_in[l][j],
+ *   e_kl = (z_kl - w^_kl) / (U_out[k][k] U_in[l][l]),
+ *   q = clamp(rint(z / scale) + zero, 0, 2^bits - 1),  w^ = scale (q - zero);
+ * with U_out = I this is the column sweep of kq_gptaq_quantize.
+ *   W        d_out x d_in; on entry the processed weights W0', on exit W^'.
+ *   U_in     kq_cholesky_inv of H_X' (d_in x d_in, upper).
+ *   U_out    kq_cholesky_inv of H_G' (d_out x d_out, upper).
+ *   D        the processed drift term or NULL; with D the target is the GPTAQ
+ *            fold W* = W0' + W0' P, P = triu_1(D U_in^T) U_in (as in
+ *            kq_gptaq_quantize), else W* = W0'.
+ *   cfg      bits 2..8; group must be 0 (one grid per output channel, from
+ *            W0' as in kq_gptaq_quantize: group grids depend on the moment a
+ *            row reaches a group, which this order does not fix, so they
+ *            return KQ_ERR_UNSUPPORTED); block must be 128 (unused).
+ *   codes    d_out x d_in uint8;  scale, zero: d_out fp32.
+ * Any d_out, d_in >= 1. Workspace from
+ * kq_workspace_size(KQ_OP_YAQA_QUANTIZE, d_out, d_in, ...) (sized for a
+ * non-NULL D). Asynchronous; fp32 arithmetic. */
+kq_status kq_yaqa_quantize(float* W, const float* U_in, const float* U_out, const float* D,
+                           int64_t d_out, int64_t d_in, const kq_quant_cfg* cfg,
+                           uint8_t* codes, float* scale, float* zero,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Mixed-precision allocation (KronQ summary, Method: sublayers with larger
  * s get wider codes). Host only, deterministic. Visits the L sublayers in

@@ -175,3 +175,36 @@ def kron_objective(dW, H_in, H_out) -> float:
     row-major vec: the proxy objective of [YQ] "损失函数 / 训练策略"."""
     dW = np.asarray(dW, dtype=np.float64)
     return float(np.sum((dW @ np.asarray(H_in, np.float64) @ dW.T) * np.asarray(H_out, np.float64)))
+
+
+def residuals_of(Wt, What, U_in, U_out):
+    """Rounding residuals eps = z - w^ implied by a finished result.
+
+    From the definition of z (round_two_sided), W* - W^ = U_out^T e U_in
+    exactly (the sum over k <= i, l <= j including (i, j) itself), so
+    e = U_out^-T (W* - W^) U_in^-1 by two triangular solves and
+    eps_ij = e_ij U_out[i,i] U_in[j,j]. A result is the rounding of its own
+    fed-back inputs exactly when every eps lies within half a grid step
+    (beyond it only toward a clamped end of the grid): a check that holds at
+    any size without rerunning the rounding.
+    """
+    from scipy.linalg import solve_triangular
+
+    Dl = np.asarray(Wt, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    U_in = np.asarray(U_in, dtype=np.float64)
+    U_out = np.asarray(U_out, dtype=np.float64)
+    X = solve_triangular(U_out, Dl, trans="T", lower=False)        # U_out^T X = Dl
+    e = solve_triangular(U_in, X.T, trans="T", lower=False).T      # e U_in = X
+    return e * np.diag(U_out)[:, None] * np.diag(U_in)[None, :]
+
+
+def rounding_violation(eps, codes, scale, bits: int):
+    """Largest excess of |eps| over half a grid step, in grid steps (<= 0 for
+    a valid rounding): interior codes need |eps| <= step / 2, code 0 needs
+    eps <= step / 2 and the top code eps >= -step / 2."""
+    sc = np.asarray(scale, dtype=np.float64).reshape(-1)[:, None]
+    r = np.asarray(eps, dtype=np.float64) / sc
+    q = np.asarray(codes)
+    top = 2 ** bits - 1
+    over = np.where(q == 0, r - 0.5, np.where(q == top, -r - 0.5, np.abs(r) - 0.5))
+    return float(over.max())

@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     kq_cholesky_inv,
     kq_form_p,
     kq_gptaq_quantize,
+    kq_yaqa_quantize,
     kq_layer_objective,
     kq_pack_codes,
     kq_packed_row_words,

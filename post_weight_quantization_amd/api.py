@@ -149,6 +149,27 @@ def kq_gptaq_quantize(W, U, D, bits: int, group: int = 0, block: int = 128, code
     return codes, scale, zero
 
 
+def kq_yaqa_quantize(W, U_in, U_out, D, bits: int, codes=None, scale=None, zero=None, ws=None,
+                     stream=None):
+    """In place W0' -> W^' with feedback along rows (U_in) and columns
+    (U_out); returns (codes, scale, zero), one grid per output channel."""
+    _need_cuda(W, U_in, U_out, D, codes, scale, zero)
+    d_out, d_in = W.shape
+    dev = W.device
+    cfg = N.kq_quant_cfg(bits, 0, 128, 0)
+    if codes is None:
+        codes = torch.empty(d_out, d_in, dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(d_out, 1, dtype=torch.float32, device=dev)
+    if zero is None:
+        zero = torch.empty(d_out, 1, dtype=torch.float32, device=dev)
+    ws = _ws(kq_workspace_size(N.KQ_OP_YAQA_QUANTIZE, d_out, d_in, cfg=cfg), dev, ws)
+    check(N.lib.kq_yaqa_quantize(_ptr(W), _ptr(U_in), _ptr(U_out), _ptr(D), d_out, d_in,
+                                 ctypes.byref(cfg), _ptr(codes), _ptr(scale), _ptr(zero), _ptr(ws),
+                                 ws.numel(), _stream(stream)))
+    return codes, scale, zero
+
+
 def kq_allocate_bits(s, n_params, widths=(2, 3, 4), avg_budget: float = 2.5):
     L = len(s)
     sa = (ctypes.c_double * L)(*[float(v) for v in s])

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
 
 SOURCES = ["kq_api.hip", "gemm_f32.hip", "cov.hip", "biip.hip", "chol.hip", "gptaq.hip",
-           "objective.hip", "deploy.hip"]
+           "objective.hip", "deploy.hip", "yaqa.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

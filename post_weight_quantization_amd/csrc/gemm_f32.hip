@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   if ((fl & G_OUT_UPPER) && m0 > n0 + TN - 1) return;
   if ((fl & G_OUT_SUPPER) && m0 >= n0 + TN - 1) return;
 
-  const int64_t ko = z * g.kofs;  // global k = local k + ko (for masks)
+  const int64_t ko = g.kbase + z * g.kofs;  // global k = local k + ko (for masks)
   int64_t klo = 0, khi = g.K;
   if (fl & G_A_UPPER) klo = max(klo, m0 - ko);
   if (fl & G_A_SUPPER) klo = max(klo, m0 + 1 - ko);
@@ -84,6 +84,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   if (fl & G_B_UPPER) khi = min(khi, n0 + TN - ko);
   if (fl & G_B_LOWER) klo = max(klo, n0 - ko);
   klo = max<int64_t>(0, klo) & ~int64_t(3);  // keep float4 alignment of k
+  // an empty K range leaves an accumulated output as it is
+  if (klo >= khi && g.beta == 1.f && Cin == C) return;
 
   __shared__ float As[2][TK][LDSP];
   __shared__ float Bs[2][TK][LDSP];

@@ -277,6 +277,14 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
 
 }  // namespace
 
+kq_status grid_rows(const float* W, int64_t rows, int64_t cols, float maxq, float* scale,
+                    float* zero, hipStream_t s) {
+  if (rows <= 0) return KQ_OK;
+  grid_rows_kernel<<<unsigned(cdiv(rows, 4)), 256, 0, s>>>(W, rows, cols, maxq, scale, zero);
+  KQ_HIP(hipGetLastError());
+  return KQ_OK;
+}
+
 size_t formp_ws_bytes(int64_t n) { return 0; }
 
 kq_status formp_run(const float* D, const float* U, int64_t n, float* P, Arena& ws, hipStream_t s) {

@@ -146,6 +146,10 @@ kq_status kq_workspace_size(kq_op op, int64_t d_out, int64_t d_in, int64_t n_tok
       if (d_out < 1 || n_tok < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
       *bytes = apply_ws_bytes(d_out, d_in, n_tok);
       return KQ_OK;
+    case KQ_OP_YAQA_QUANTIZE:
+      if (d_out < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
+      *bytes = yaqa_ws_bytes(d_out, d_in, true);
+      return KQ_OK;
   }
   return fail(KQ_ERR_ARG, "workspace_size: unknown op %d", int(op));
 }
@@ -258,6 +262,30 @@ kq_status kq_gptaq_quantize(float* W, const float* U, const float* D, int64_t d_
   KQ_TRY(check_ws(ws, ws_bytes, gptaq_ws_bytes(d_out, d_in, cfg->group, D != nullptr), "gptaq_quantize"));
   Arena ar{static_cast<char*>(ws), ws_bytes, 0};
   return gptaq_run(W, U, D, d_out, d_in, cfg->bits, cfg->group, codes, scale, zero, ar, stream);
+}
+
+kq_status kq_yaqa_quantize(float* W, const float* U_in, const float* U_out, const float* D,
+                           int64_t d_out, int64_t d_in, const kq_quant_cfg* cfg, uint8_t* codes,
+                           float* scale, float* zero, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  clear_error();
+  if (!W || !U_in || !U_out || !codes || !scale || !zero)
+    return fail(KQ_ERR_ARG, "yaqa_quantize: NULL argument");
+  if (d_out < 1 || d_in < 1) return fail(KQ_ERR_SHAPE, "yaqa_quantize: d_out and d_in must be >= 1");
+  if (!cfg) return fail(KQ_ERR_ARG, "yaqa_quantize: cfg is NULL");
+  if (cfg->bits < 1 || cfg->bits > 8) return fail(KQ_ERR_ARG, "yaqa_quantize: bits must be in [1, 8]");
+  if (cfg->group != 0)
+    return fail(KQ_ERR_UNSUPPORTED, "yaqa_quantize: group must be 0 (one grid per output channel)");
+  if (cfg->block != 128) return fail(KQ_ERR_UNSUPPORTED, "yaqa_quantize: block must be 128");
+  if (cfg->flags != 0) return fail(KQ_ERR_ARG, "yaqa_quantize: flags must be 0");
+  if (d_out > (int64_t(1) << 24) || d_in > (int64_t(1) << 24))
+    return fail(KQ_ERR_SHAPE, "yaqa_quantize: dimensions above 2^24 are not supported");
+  const void* ptrs[4] = {W, U_in, U_out, D};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(KQ_ERR_ARG, "yaqa_quantize: buffers must be 16-byte aligned");
+  KQ_TRY(check_ws(ws, ws_bytes, yaqa_ws_bytes(d_out, d_in, D != nullptr), "yaqa_quantize"));
+  Arena ar{static_cast<char*>(ws), ws_bytes, 0};
+  return yaqa_run(W, U_in, U_out, D, d_out, d_in, cfg->bits, codes, scale, zero, ar, stream);
 }
 
 kq_status kq_allocate_bits(const double* s, const int64_t* n_params, int32_t L, const int32_t* widths,

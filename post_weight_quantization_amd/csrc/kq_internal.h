@@ -80,6 +80,7 @@ struct GemmArgs {
   int64_t lda, ldb, ldc;
   int64_t strideA, strideB, strideC;  // per batch (blockIdx.z)
   int64_t kofs;                       // per-batch offset added to k for the triangle masks
+  int64_t kbase;                      // offset added to k for the triangle masks of every batch
   int batch;
   float alpha, beta;
   uint32_t flags;
@@ -123,6 +124,15 @@ size_t gptaq_ws_bytes(int64_t d_out, int64_t d_in, int group, bool has_d);
 kq_status gptaq_run(float* W, const float* U, const float* D, int64_t d_out, int64_t d_in,
                     int bits, int group, uint8_t* codes, float* scale, float* zero, Arena& ws,
                     hipStream_t s);
+
+// ------------------------------------------------- rounding with output feedback
+size_t yaqa_ws_bytes(int64_t d_out, int64_t d_in, bool has_d);
+kq_status yaqa_run(float* W, const float* U_in, const float* U_out, const float* D, int64_t d_out,
+                   int64_t d_in, int bits, uint8_t* codes, float* scale, float* zero, Arena& ws,
+                   hipStream_t s);
+// per-row grid of the sweeps (rows x cols, row stride cols, cols % 4 == 0)
+kq_status grid_rows(const float* W, int64_t rows, int64_t cols, float maxq, float* scale,
+                    float* zero, hipStream_t s);
 
 // ------------------------------------------------------------- objective
 size_t objective_ws_bytes(int64_t d_out, int64_t d_in);

@@ -119,3 +119,26 @@ def test_allocate_bits_matches_oracle():
         assert api.kq_allocate_bits(s, n, (2, 3, 4), avg) == oracle.allocate_bits(s, n, (2, 3, 4), avg)
     with pytest.raises(N.KQError):
         api.kq_allocate_bits([1.0], [10], (2, 3, 4), 1.5)
+
+
+def test_yaqa_validation():
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+    cfg = N.kq_quant_cfg(2, 0, 128, 0)
+    st, msg = _err(N.lib.kq_yaqa_quantize(None, fake, fake, None, 4, 64, ctypes.byref(cfg), fake,
+                                          fake, fake, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_ARG and "NULL" in msg
+    st, msg = _err(N.lib.kq_yaqa_quantize(fake, fake, fake, None, 0, 64, ctypes.byref(cfg), fake,
+                                          fake, fake, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_SHAPE
+    grouped = N.kq_quant_cfg(2, 128, 128, 0)
+    st, msg = _err(N.lib.kq_yaqa_quantize(fake, fake, fake, None, 4, 128, ctypes.byref(grouped), fake,
+                                          fake, fake, fake, 1 << 30, None))
+    assert st == N.KQ_ERR_UNSUPPORTED and "group" in msg
+    need = ctypes.c_size_t()
+    assert N.lib.kq_workspace_size(N.KQ_OP_YAQA_QUANTIZE, 100, 200, 0, 0, ctypes.byref(cfg),
+                                   ctypes.byref(need)) == 0
+    # three padded 128 x 256 work matrices, padded U_in and U_out, padded D, P and T
+    assert need.value >= 4 * (3 * 128 * 256 + 3 * 256 * 256 + 128 * 128)
+    st, msg = _err(N.lib.kq_yaqa_quantize(fake, fake, fake, fake, 100, 200, ctypes.byref(cfg), fake,
+                                          fake, fake, fake, need.value - 1, None))
+    assert st == N.KQ_ERR_WORKSPACE

@@ -143,3 +143,26 @@ def test_output_feedback_lowers_the_kronecker_objective():
         two.append(yaqa.kron_objective(W0 - a["what"], HI, HO))
         one.append(yaqa.kron_objective(W0 - b["what"], HI, HO))
     assert np.mean(two) < np.mean(one)
+
+
+@pytest.mark.parametrize("with_p", [False, True])
+def test_residuals_recovered_from_the_result(with_p):
+    """The any-size check: the residuals solved back from (W*, W^) are the
+    ones the rounding produced, and they lie within half a grid step; a
+    result rounded with the output feedback left out fails the check."""
+    rng = np.random.default_rng(41 + with_p)
+    m, n, bits = 20, 36, 2
+    W0, HI, HO, UI, UO, sc, zr = _layer(m, n, rng, bits)
+    P = None
+    Wt = W0
+    if with_p:
+        D = 1e-3 * rng.standard_normal((n, n))
+        P = kronq.form_p(D, UI)
+        Wt = W0 + W0 @ P
+    res = yaqa.quantize_two_sided(W0, UI, UO, bits, P=P)
+    eps = yaqa.residuals_of(Wt, res["what"], UI, UO)
+    np.testing.assert_allclose(eps, res["eps"], rtol=0, atol=1e-10)
+    assert yaqa.rounding_violation(eps, res["codes"], res["scale"], bits) <= 1e-9
+    one = yaqa.quantize_two_sided(W0, UI, np.eye(m), bits, P=P)
+    eps1 = yaqa.residuals_of(Wt, one["what"], UI, UO)
+    assert yaqa.rounding_violation(eps1, one["codes"], one["scale"], bits) > 0.05
