@@ -219,7 +219,8 @@ kq_status kq_gptaq_quantize(float* W, const float* U, const float* D,
  *   codes    d_out x d_in uint8;  scale, zero: d_out fp32.
  * Any d_out, d_in >= 1. Workspace from
  * kq_workspace_size(KQ_OP_YAQA_QUANTIZE, d_out, d_in, ...) (sized for a
- * non-NULL D). Asynchronous; fp32 arithmetic. */
+ * non-NULL D). Synchronizes the stream (the call overlaps work on a second
+ * stream of its own, which it releases before returning); fp32 arithmetic. */
 kq_status kq_yaqa_quantize(float* W, const float* U_in, const float* U_out, const float* D,
                            int64_t d_out, int64_t d_in, const kq_quant_cfg* cfg,
                            uint8_t* codes, float* scale, float* zero,

@@ -75,6 +75,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   if ((fl & G_OUT_LOWER) && n0 > m0 + TM - 1) return;
   if ((fl & G_OUT_UPPER) && m0 > n0 + TN - 1) return;
   if ((fl & G_OUT_SUPPER) && m0 >= n0 + TN - 1) return;
+  if ((fl & G_OUT_NSTART) && n0 < g.ostart + z * g.ostart_ofs) return;
+  if ((fl & G_OUT_MSTART) && m0 < g.ostart + z * g.ostart_ofs) return;
 
   const int64_t ko = g.kbase + z * g.kofs;  // global k = local k + ko (for masks)
   int64_t klo = 0, khi = g.K;

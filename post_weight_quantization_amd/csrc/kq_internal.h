@@ -69,6 +69,10 @@ enum GemmFlag : uint32_t {
   // C aliases A (in place): every tile must span all N columns so that it
   // reads its rows of A before any tile writes them (requires N <= 128)
   G_C_ALIASES_A = 1u << 15,
+  // skip output tiles that start before column (G_OUT_NSTART) or row
+  // (G_OUT_MSTART) ostart + batch * ostart_ofs (a multiple of the tile)
+  G_OUT_NSTART = 1u << 16,
+  G_OUT_MSTART = 1u << 17,
 };
 
 struct GemmArgs {
@@ -81,6 +85,7 @@ struct GemmArgs {
   int64_t strideA, strideB, strideC;  // per batch (blockIdx.z)
   int64_t kofs;                       // per-batch offset added to k for the triangle masks
   int64_t kbase;                      // offset added to k for the triangle masks of every batch
+  int64_t ostart, ostart_ofs;         // first output column / row (G_OUT_NSTART / G_OUT_MSTART)
   int batch;
   float alpha, beta;
   uint32_t flags;

@@ -14,28 +14,27 @@
 // each column. Every order that visits (k,l) before (i,j) whenever k <= i and
 // l <= j gives the same codes.
 //
-// Order used here: a wavefront over TS x TS tiles. The tiles (I, J) with
+// Order used here: a wavefront over 64 x 64 tiles. The tiles (I, J) with
 // I + J = s form one launch, one workgroup per tile, and inside a tile the
 // entries run as a skewed wavefront (row i reaches column j at step i + j).
 // What a tile needs from outside arrives through two accumulators in HBM:
 //   M[I,J] = sum_{L<=J} e_{I,L} U_I[L,J]            (row feedback)
 //   Wk     = W* - sum_{K<I} U_O[K,I]^T M[K,J]          (column feedback)
-// so a tile starts from Z0 = Wk_IJ - U_O[I,I]^T Mpart_IJ, Mpart holding the
-// column blocks L < J. After each step two batched fp32 MFMA GEMMs carry its
-// results on: M[I, :] += e_IJ U_I[J, :] (U_I upper: only blocks >= J change,
-// and block J becomes the complete M_IJ), then
-// Wk[:, J] -= U_O[I, :]^T M_IJ (only row blocks >= I change).
+// A tile starts from Z0 = Wk_IJ - U_O[I,I]^T Mpart_IJ, Mpart holding the
+// column blocks L < J. The feedback of its two neighbours finished one step
+// earlier (left: e_{I,J-1} U_I[J-1,J]; above: U_O[I-1,I]^T M_{I-1,J}) the tile
+// computes itself as MFMA products in LDS; everything farther away arrives
+// through batched fp32 MFMA GEMMs on a second stream, which carry the results
+// of step s to the tiles of steps >= s + 2 while the tiles of step s + 1 run:
+// M[I, blocks >= J+2] += e_IJ U_I[J, .] and Wk[blocks >= I+2, J] -= U_O[I, .]^T M_IJ.
 //
-// Inside a tile, thread (row i, 16-column segment) keeps v = Z0 - (column
-// feedback received) and t = sum_{l<j} e_il U_I[l,j] for its 16 columns, so
-// z = v - U_O[i,i] t. At each step the entry on the front of each row is
-// rounded; its e goes to its row (t += e U_I[j, :]) and its
-// T = t + (z - w^) / U_O[i,i] (= sum_{l<=j} e_il U_I[l,j]) down its column
-// (v -= U_O[i, r] T for rows r below). Both travel through LDS, double
-// buffered by step parity, with one barrier per step. The column
-// coefficients U_O[sp - c][i] of a thread's 16 columns form a sliding window
-// that takes one LDS read per step: with the step loop unrolled by 16 the
-// window slot of each column is a compile-time index.
+// Inside a tile, the four lanes of a quad hold one row (16 columns each) as
+// v = Z0 - (column feedback received) and t = sum_{l<j} e_il U_I[l,j], so
+// z = v - U_O[i,i] t. Row i reaches column j at step 2 i + j: the rounded
+// front entry's e goes along its row (t += e U_I[j, :]) by DPP within the
+// quad, and its T = t + (z - w^) / U_O[i,i] (= sum_{l<=j} e_il U_I[l,j]) down
+// its column (v -= U_O[i, r] T for rows r below) through LDS, read after the
+// step's barrier and applied one step later, before the row below needs it.
 #include "kq_internal.h"
 
 #include <algorithm>
@@ -52,11 +51,13 @@ constexpr int YCP = YT + 16;      // padded code row (bytes)
 
 static_assert(YNSEG * YT == 256, "one tile row per YNSEG threads, 256 threads");
 
-constexpr size_t YAQA_LDS = sizeof(float) * (4 * YT * YP + YT + 4 * YT) + YT * YCP;
+constexpr size_t YAQA_LDS = sizeof(float) * (6 * YT * YP + YT + 4 * YT) + YT * YCP;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct YaqaStep {
   const float* Wk;  // m_p x n_p working input (column feedback applied)
-  const float* Mp;  // m_p x n_p row-feedback accumulator
+  float* Mp;        // m_p x n_p row-feedback accumulator; a finished tile holds its complete M
   float* E;         // m_p x n_p scaled errors
   int64_t ld;       // n_p
   const float* UI;  // n_p x n_p (row stride ldI)
@@ -71,13 +72,43 @@ struct YaqaStep {
   int s, I_lo;
 };
 
+// acc += op(A) B with K = YT for this wave's 32 x 32 block at (wm, wn), both
+// operands in LDS: A(m, k) = Ap[m][k] if AT else Ap[k][m]; B(k, n) = Bp[k][n].
+// acc[r] of lane (lr, lk) is element (wm + 8 (r / 4) + 4 lk + r % 4, wn + lr).
+template <bool AT>
+__device__ inline void mfma_k64(const float (*Ap)[YP], const float (*Bp)[YP], f32x16& acc, int wm,
+                                int wn, int lr, int lk) {
+#pragma unroll
+  for (int kk = 0; kk < YT; kk += 2) {
+    const float av = AT ? Ap[wm + lr][kk + lk] : Ap[kk + lk][wm + lr];
+    const float bv = Bp[kk + lk][wn + lr];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+}
+
+__device__ inline void load_block(float (*dst)[YP], const float* src, int64_t lds, int t) {
+  for (int e4 = t; e4 < YT * YT / 4; e4 += 256) {
+    const int r = e4 / (YT / 4), c = (e4 % (YT / 4)) * 4;
+    *reinterpret_cast<float4*>(&dst[r][c]) = *reinterpret_cast<const float4*>(src + r * lds + c);
+  }
+}
+
+// One tile (I, J) of the wavefront. Besides the far feedback already in Wk
+// and Mp it takes the near feedback of its two finished neighbours itself:
+//   P2 = e_{I,J-1} U_I[J-1, J]           (completes Mpart_IJ)
+//   P1 = U_O[I-1, I]^T M_{I-1, J}        (M of the tile above, complete)
+//   Z0 = Wk_IJ - P1 - U_O[I, I]^T (Mpart_IJ + P2)
+// as fp32 MFMA products over K = 64 in LDS, then sweeps the tile and writes
+// e, W^, the codes and its complete M = Mpart + P2 + e_IJ U_I[J, J].
 __global__ __launch_bounds__(256) void yaqa_tile_kernel(YaqaStep a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   float(*UIs)[YP] = reinterpret_cast<float(*)[YP]>(sm);               // U_I[l][c], 0 for c < l
   float(*UOt)[YP] = reinterpret_cast<float(*)[YP]>(sm + YT * YP);     // U_O[k][i] at [i][k], 0 for k > i
-  float(*Ms)[YP] = reinterpret_cast<float(*)[YP]>(sm + 2 * YT * YP);  // Mpart, then staged W^
+  float(*Ms)[YP] = reinterpret_cast<float(*)[YP]>(sm + 2 * YT * YP);  // Mpart (+ P2)
   float(*Es)[YP] = reinterpret_cast<float(*)[YP]>(sm + 3 * YT * YP);  // staged e
-  float* uiinv = sm + 4 * YT * YP;                                    // 1 / U_I[j][j]
+  float(*A1)[YP] = reinterpret_cast<float(*)[YP]>(sm + 4 * YT * YP);  // operands, then staged T
+  float(*B1)[YP] = reinterpret_cast<float(*)[YP]>(sm + 5 * YT * YP);  // operands, Z, then staged W^
+  float* uiinv = sm + 6 * YT * YP;                                    // 1 / U_I[j][j]
   float* erow = uiinv + YT;                                           // [2][YT]
   float* tcol = erow + 2 * YT;                                        // [2][YT]
   uint8_t(*Cs)[YCP] = reinterpret_cast<uint8_t(*)[YCP]>(tcol + 2 * YT);
@@ -86,6 +117,9 @@ __global__ __launch_bounds__(256) void yaqa_tile_kernel(YaqaStep a) {
   const int I = a.I_lo + int(blockIdx.x);
   const int J = a.s - I;
   const int64_t r0 = int64_t(I) * YT, c0 = int64_t(J) * YT;
+  const int lane = t & 63, w = t >> 6;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
 
   for (int e4 = t; e4 < YT * YT / 4; e4 += 256) {
     const int r = e4 / (YT / 4), c = (e4 % (YT / 4)) * 4;
@@ -100,12 +134,39 @@ __global__ __launch_bounds__(256) void yaqa_tile_kernel(YaqaStep a) {
     UOt[c + 1][r] = c + 1 >= r ? uo.y : 0.f;
     UOt[c + 2][r] = c + 2 >= r ? uo.z : 0.f;
     UOt[c + 3][r] = c + 3 >= r ? uo.w : 0.f;
-    *reinterpret_cast<float4*>(&Ms[r][c]) =
-        *reinterpret_cast<const float4*>(a.Mp + (r0 + r) * a.ld + c0 + c);
+  }
+  load_block(Ms, a.Mp + r0 * a.ld + c0, a.ld, t);
+  if (J > 0) {
+    load_block(A1, a.E + r0 * a.ld + c0 - YT, a.ld, t);       // e_{I,J-1} as [m][k]
+    load_block(B1, a.UI + (c0 - YT) * a.ldI + c0, a.ldI, t);  // U_I[J-1, J] as [k][n]
   }
   if (t < 4 * YT) erow[t] = 0.f;  // erow and tcol (contiguous)
   __syncthreads();
   if (t < YT) uiinv[t] = 1.f / UIs[t][t];
+
+  if (J > 0) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    mfma_k64<true>(A1, B1, acc, wm, wn, lr, lk);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ms[wm + 8 * (r >> 2) + 4 * lk + (r & 3)][wn + lr] += acc[r];
+    __syncthreads();
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  if (I > 0) {
+    load_block(A1, a.UO + (r0 - YT) * a.ldO + r0, a.ldO, t);  // U_O[I-1, I] as [k][m]
+    load_block(B1, a.Mp + (r0 - YT) * a.ld + c0, a.ld, t);    // M_{I-1, J}
+    __syncthreads();
+    mfma_k64<false>(A1, B1, acc, wm, wn, lr, lk);
+  }
+  mfma_k64<true>(UOt, Ms, acc, wm, wn, lr, lk);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) B1[wm + 8 * (r >> 2) + 4 * lk + (r & 3)][wn + lr] = acc[r];
+  __syncthreads();
 
   const int i = t / YNSEG;
   const int cb = (t % YNSEG) * YSEG;
@@ -119,105 +180,159 @@ __global__ __launch_bounds__(256) void yaqa_tile_kernel(YaqaStep a) {
   const float uo = UOt[i][i];
   const float iuo = 1.f / uo;
 
-  // Z0 = Wk_IJ - U_O[I,I]^T Mpart_IJ for this thread's columns; U_O[k][i] = 0
-  // for k > i, so the wave stops at its last row
-  float v[YSEG], tt[YSEG], win[YSEG];
+  float v[YSEG], tt[YSEG], tcp[YSEG], uic[YSEG], win[8];
   {
     const float* wp = a.Wk + grow * a.ld + c0 + cb;
 #pragma unroll
     for (int j = 0; j < YSEG; j += 4) {
       const float4 x = *reinterpret_cast<const float4*>(wp + j);
-      v[j] = x.x;
-      v[j + 1] = x.y;
-      v[j + 2] = x.z;
-      v[j + 3] = x.w;
-    }
-    const int kend = (t / 64 + 1) * (64 / YNSEG);
-    for (int k = 0; k < kend; ++k) {
-      const float co = UOt[i][k];
-#pragma unroll
-      for (int j = 0; j < YSEG; j += 4) {
-        const float4 m = *reinterpret_cast<const float4*>(&Ms[k][cb + j]);
-        v[j] -= co * m.x;
-        v[j + 1] -= co * m.y;
-        v[j + 2] -= co * m.z;
-        v[j + 3] -= co * m.w;
-      }
+      const float4 z = *reinterpret_cast<const float4*>(&B1[i][cb + j]);
+      v[j] = x.x - z.x;
+      v[j + 1] = x.y - z.y;
+      v[j + 2] = x.z - z.z;
+      v[j + 3] = x.w - z.w;
     }
 #pragma unroll
     for (int j = 0; j < YSEG; ++j) {
       tt[j] = 0.f;
-      win[j] = 0.f;
+      tcp[j] = 0.f;
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) win[k] = 0.f;
   }
-  __syncthreads();  // Ms is free for the staged W^
+  // U_I row and 1 / U_I[j][j] of this row's front at the first step
+  float uinv;
+  {
+    const int j0 = -2 * i;
+    const int jc = j0 >= 0 && j0 < YT ? j0 : 0;
+#pragma unroll
+    for (int j = 0; j < YSEG; j += 4) {
+      const float4 u = *reinterpret_cast<const float4*>(&UIs[jc][cb + j]);
+      uic[j] = u.x;
+      uic[j + 1] = u.y;
+      uic[j + 2] = u.z;
+      uic[j + 3] = u.w;
+    }
+    uinv = uiinv[jc];
+  }
+  __syncthreads();  // A1 and B1 are free for the staged T and W^
 
-  constexpr int NSTEP = 2 * YT - 1;
+  // Row i reaches column j at step 2 i + j. Along a row the chain stays in
+  // registers (the front's e reaches the row's four lanes by DPP quad sums);
+  // the column feedback T of step sp is read from LDS after the step's
+  // barrier and applied during step sp + 1, one step before the row below
+  // reaches that column. The window win[k % 8] = U_O[k][i] holds the
+  // coefficients of the last eight producer rows; with the step loop
+  // unrolled by 16 (and sp0 a multiple of 16) every slot index below is a
+  // compile-time constant.
+  constexpr int NSTEP = 2 * (YT - 1) + YT;
 #pragma unroll 1
-  for (int sp0 = 0; sp0 < NSTEP; sp0 += YSEG) {
+  for (int sp0 = 0; sp0 < NSTEP; sp0 += 16) {
 #pragma unroll
-    for (int p = 0; p < YSEG; ++p) {
+    for (int p = 0; p < 16; ++p) {
       const int sp = sp0 + p;
-      float* eb = erow + (p & 1) * YT;
       float* tb = tcol + (p & 1) * YT;
-      const int j0 = sp - i;
+      const int j0 = sp - 2 * i;
       const int jj = j0 - cb;
+      float ev = 0.f;
       if (jj >= 0 && jj < YSEG) {
-        float vz = v[0], ta = tt[0];
+        // the front entry of this row: a 4-level tree of bitwise selects
+        // (written as masks: a select tree on the index is turned back into
+        // an indexed private array, which would live in scratch memory)
+        auto pick = [](float lo, float hi, int m) {
+          return __int_as_float((__float_as_int(lo) & ~m) | (__float_as_int(hi) & m));
+        };
+        const int m0 = -(jj & 1), m1 = -((jj >> 1) & 1), m2 = -((jj >> 2) & 1), m3 = -((jj >> 3) & 1);
+        float x8[8], t8[8];
 #pragma unroll
-        for (int k = 1; k < YSEG; ++k) {
-          vz = jj == k ? v[k] : vz;
-          ta = jj == k ? tt[k] : ta;
+        for (int k = 0; k < 8; ++k) {
+          x8[k] = pick(v[2 * k], v[2 * k + 1], m0);
+          t8[k] = pick(tt[2 * k], tt[2 * k + 1], m0);
         }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x8[k] = pick(x8[2 * k], x8[2 * k + 1], m1);
+          t8[k] = pick(t8[2 * k], t8[2 * k + 1], m1);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          x8[k] = pick(x8[2 * k], x8[2 * k + 1], m2);
+          t8[k] = pick(t8[2 * k], t8[2 * k + 1], m2);
+        }
+        const float vz = pick(x8[0], x8[1], m3);
+        const float ta = pick(t8[0], t8[1], m3);
         const float z = vz - uo * ta;
         const float q = __builtin_amdgcn_fmed3f(rintf(z * isc) + zr, 0.f, a.maxq);
         const float wq = sc * (q - zr);
         const float eps = z - wq;
-        const float e = eps * iuo * uiinv[j0];
-        eb[i] = e;
-        tb[j0] = ta + eps * iuo;
-        Ms[i][j0] = wq;
-        Es[i][j0] = e;
+        ev = eps * iuo * uinv;
+        const float tv = ta + eps * iuo;
+        tb[j0] = tv;
+        A1[i][j0] = tv;
+        B1[i][j0] = wq;
+        Es[i][j0] = ev;
         Cs[i][j0] = uint8_t(q);
       }
+      // e of the row's front to its four lanes (the others hold 0)
+      ev += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ev), 0xB1, 0xF, 0xF, true));
+      ev += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ev), 0x4E, 0xF, 0xF, true));
+#pragma unroll
+      for (int j = 0; j < YSEG; ++j) tt[j] += ev * uic[j];
+      // column feedback produced at step sp - 1: column cb + j from row
+      // (sp - 1 - cb - j) / 2, present only for one parity of j
+#pragma unroll
+      for (int j = 0; j < YSEG; ++j)
+        if (((p - 1 - j) & 1) == 0) v[j] -= win[((p - 1 - j) >> 1) & 7] * tcp[j];
       __syncthreads();
-      {
-        const int k = sp - cb;  // newest window entry U_O[k][i]
-        const bool in = k >= 0 && k < YT;
-        const float x = UOt[i][in ? k : 0];
-        win[p] = in ? x : 0.f;
-      }
-      const bool act = j0 >= 0 && j0 < YT;
-      const float e = act ? eb[i] : 0.f;
-      const int jr = act ? j0 : 0;
+      // for step sp + 1: this step's T, the newest window entry, the next
+      // U_I row and 1 / U_I[j][j] of the front
 #pragma unroll
       for (int j = 0; j < YSEG; j += 4) {
-        const float4 u = *reinterpret_cast<const float4*>(&UIs[jr][cb + j]);
-        tt[j] += e * u.x;
-        tt[j + 1] += e * u.y;
-        tt[j + 2] += e * u.z;
-        tt[j + 3] += e * u.w;
         const float4 tc = *reinterpret_cast<const float4*>(tb + cb + j);
-        v[j] -= win[(p - j) & (YSEG - 1)] * tc.x;
-        v[j + 1] -= win[(p - j - 1) & (YSEG - 1)] * tc.y;
-        v[j + 2] -= win[(p - j - 2) & (YSEG - 1)] * tc.z;
-        v[j + 3] -= win[(p - j - 3) & (YSEG - 1)] * tc.w;
+        tcp[j] = tc.x;
+        tcp[j + 1] = tc.y;
+        tcp[j + 2] = tc.z;
+        tcp[j + 3] = tc.w;
+      }
+      {
+        const int k = (sp - cb) >> 1;  // newest producer row of a column of this lane
+        const bool in = k >= 0 && k < YT;
+        const float x = UOt[i][in ? k : 0];
+        win[(p >> 1) & 7] = in ? x : 0.f;
+      }
+      {
+        const int jn = j0 + 1;
+        const int jc = jn >= 0 && jn < YT ? jn : 0;
+#pragma unroll
+        for (int j = 0; j < YSEG; j += 4) {
+          const float4 u = *reinterpret_cast<const float4*>(&UIs[jc][cb + j]);
+          uic[j] = u.x;
+          uic[j + 1] = u.y;
+          uic[j + 2] = u.z;
+          uic[j + 3] = u.w;
+        }
+        uinv = uiinv[jc];
       }
     }
   }
   __syncthreads();
 
-  // results: e into the padded E, W^ and codes into the real outputs
+  // results: e and the complete M into the padded buffers, W^ and codes into
+  // the real outputs
   for (int e4 = t; e4 < YT * YT / 4; e4 += 256) {
     const int r = e4 / (YT / 4), c = (e4 % (YT / 4)) * 4;
     *reinterpret_cast<float4*>(a.E + (r0 + r) * a.ld + c0 + c) =
         *reinterpret_cast<const float4*>(&Es[r][c]);
+    const float4 m = *reinterpret_cast<const float4*>(&Ms[r][c]);
+    const float4 tv = *reinterpret_cast<const float4*>(&A1[r][c]);
+    *reinterpret_cast<float4*>(a.Mp + (r0 + r) * a.ld + c0 + c) =
+        make_float4(m.x + tv.x, m.y + tv.y, m.z + tv.z, m.w + tv.w);
   }
   for (int e = t; e < YT * YT; e += 256) {
     const int r = e / YT, c = e % YT;
     const int64_t gr = r0 + r, gc = c0 + c;
     if (gr < a.d_out && gc < a.d_in) {
-      a.What[gr * a.d_in + gc] = Ms[r][c];
+      a.What[gr * a.d_in + gc] = B1[r][c];
       a.codes[gr * a.d_in + gc] = Cs[r][c];
     }
   }
@@ -248,6 +363,32 @@ kq_status pad_copy(const float* src, int64_t rows, int64_t cols, float* dst, int
 }
 
 inline int64_t pad_to(int64_t x) { return cdiv(x, YT) * YT; }
+
+// A second stream (default priority) and two rings of events for the
+// overlap of the far feedback with the next wavefront step; released when
+// the call returns, after the caller's stream has been synchronized.
+struct Side {
+  static constexpr int NE = 4;
+  hipStream_t st = nullptr;
+  hipEvent_t tiles[NE] = {};
+  hipEvent_t done[NE] = {};
+  kq_status open() {
+    KQ_HIP(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    for (int k = 0; k < NE; ++k) {
+      KQ_HIP(hipEventCreateWithFlags(&tiles[k], hipEventDisableTiming));
+      KQ_HIP(hipEventCreateWithFlags(&done[k], hipEventDisableTiming));
+    }
+    return KQ_OK;
+  }
+  ~Side() {
+    if (st) hipStreamSynchronize(st);
+    for (int k = 0; k < NE; ++k) {
+      if (tiles[k]) hipEventDestroy(tiles[k]);
+      if (done[k]) hipEventDestroy(done[k]);
+    }
+    if (st) hipStreamDestroy(st);
+  }
+};
 
 }  // namespace
 
@@ -331,38 +472,50 @@ kq_status yaqa_run(float* W, const float* U_in, const float* U_out, const float*
   st.maxq = float((1 << bits) - 1);
   KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(yaqa_tile_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(YAQA_LDS)));
-  for (int sidx = 0; sidx <= mt + nt - 2; ++sidx) {
+
+  // The far feedback of step s (targets two or more tiles away) runs on a
+  // second stream while the tiles of step s + 1 run; step s + 2 waits for it.
+  Side side;
+  KQ_TRY(side.open());
+  const int nsteps = mt + nt - 1;
+  for (int sidx = 0; sidx < nsteps; ++sidx) {
     const int I_lo = std::max(0, sidx - nt + 1), I_hi = std::min(sidx, mt - 1);
     const int cnt = I_hi - I_lo + 1;
     const int J_hi = sidx - I_lo;
+    if (sidx >= 2) KQ_HIP(hipStreamWaitEvent(s, side.done[(sidx - 2) % Side::NE], 0));
     st.s = sidx;
     st.I_lo = I_lo;
     yaqa_tile_kernel<<<unsigned(cnt), 256, YAQA_LDS, s>>>(st);
     KQ_HIP(hipGetLastError());
-    // M[I, :] += e_IJ U_I[J, :]   (op(B) zero for global k > n: U_I upper)
+    KQ_HIP(hipEventRecord(side.tiles[sidx % Side::NE], s));
+    KQ_HIP(hipStreamWaitEvent(side.st, side.tiles[sidx % Side::NE], 0));
+    // M[I, blocks >= J + 2] += e_IJ U_I[J, same]
     GemmArgs gr = gemm_args(E + int64_t(I_lo) * YT * np + int64_t(J_hi) * YT, np,
                             UI + int64_t(J_hi) * YT * np, np, Mp + int64_t(I_lo) * YT * np, np, YT,
-                            np, YT, 1.f, 1.f, G_B_UPPER);
+                            np, YT, 1.f, 1.f, G_OUT_NSTART);
     gr.batch = cnt;
     gr.strideA = int64_t(YT) * np - YT;
     gr.strideB = -int64_t(YT) * np;
     gr.strideC = int64_t(YT) * np;
-    gr.kbase = int64_t(J_hi) * YT;
-    gr.kofs = -YT;
-    KQ_TRY(gemm_f32(gr, s));
-    // Wk[:, J] -= U_O[I, :]^T M_IJ   (op(A)[m][k] = U_O[I*YT + k][m], zero for global k > m)
+    gr.ostart = int64_t(J_hi + 2) * YT;
+    gr.ostart_ofs = -YT;
+    if (sidx - I_hi + 2 < nt) KQ_TRY(gemm_f32(gr, side.st));  // the smallest J has targets
+    // Wk[blocks >= I + 2, J] -= U_O[I, same]^T M_IJ
     GemmArgs gc = gemm_args(UO + int64_t(I_lo) * YT * mp, mp,
                             Mp + int64_t(I_lo) * YT * np + int64_t(J_hi) * YT, np,
                             Wk + int64_t(J_hi) * YT, np, mp, YT, YT, -1.f, 1.f,
-                            G_TRANS_A | G_A_LOWER);
+                            G_TRANS_A | G_OUT_MSTART);
     gc.batch = cnt;
     gc.strideA = int64_t(YT) * mp;
     gc.strideB = int64_t(YT) * np - YT;
     gc.strideC = -int64_t(YT);
-    gc.kbase = int64_t(I_lo) * YT;
-    gc.kofs = YT;
-    KQ_TRY(gemm_f32(gc, s));
+    gc.ostart = int64_t(I_lo + 2) * YT;
+    gc.ostart_ofs = YT;
+    if (I_lo + 2 < mt) KQ_TRY(gemm_f32(gc, side.st));  // the smallest I has targets
+    KQ_HIP(hipEventRecord(side.done[sidx % Side::NE], side.st));
   }
+  KQ_HIP(hipStreamWaitEvent(s, side.done[(nsteps - 1) % Side::NE], 0));
+  KQ_HIP(hipStreamSynchronize(s));
   return KQ_OK;
 }
 
