@@ -51,7 +51,7 @@ constexpr int YCP = YT + 16;      // padded code row (bytes)
 
 static_assert(YNSEG * YT == 256, "one tile row per YNSEG threads, 256 threads");
 
-constexpr size_t YAQA_LDS = sizeof(float) * (6 * YT * YP + YT + 4 * YT) + YT * YCP;
+constexpr size_t YAQA_LDS = sizeof(float) * (8 * YT * YP + YT + 4 * YT) + YT * YCP;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -100,15 +100,18 @@ __device__ inline void load_block(float (*dst)[YP], const float* src, int64_t ld
 //   Z0 = Wk_IJ - P1 - U_O[I, I]^T (Mpart_IJ + P2)
 // as fp32 MFMA products over K = 64 in LDS, then sweeps the tile and writes
 // e, W^, the codes and its complete M = Mpart + P2 + e_IJ U_I[J, J].
-__global__ __launch_bounds__(256) void yaqa_tile_kernel(YaqaStep a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void yaqa_tile_kernel(
+    YaqaStep a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   float(*UIs)[YP] = reinterpret_cast<float(*)[YP]>(sm);               // U_I[l][c], 0 for c < l
   float(*UOt)[YP] = reinterpret_cast<float(*)[YP]>(sm + YT * YP);     // U_O[k][i] at [i][k], 0 for k > i
   float(*Ms)[YP] = reinterpret_cast<float(*)[YP]>(sm + 2 * YT * YP);  // Mpart (+ P2)
   float(*Es)[YP] = reinterpret_cast<float(*)[YP]>(sm + 3 * YT * YP);  // staged e
-  float(*A1)[YP] = reinterpret_cast<float(*)[YP]>(sm + 4 * YT * YP);  // operands, then staged T
-  float(*B1)[YP] = reinterpret_cast<float(*)[YP]>(sm + 5 * YT * YP);  // operands, Z, then staged W^
-  float* uiinv = sm + 6 * YT * YP;                                    // 1 / U_I[j][j]
+  float(*A1)[YP] = reinterpret_cast<float(*)[YP]>(sm + 4 * YT * YP);  // e_{I,J-1}, then staged T
+  float(*B1)[YP] = reinterpret_cast<float(*)[YP]>(sm + 5 * YT * YP);  // U_I[J-1,J], then staged W^
+  float(*A2)[YP] = reinterpret_cast<float(*)[YP]>(sm + 6 * YT * YP);  // U_O[I-1,I]
+  float(*B2)[YP] = reinterpret_cast<float(*)[YP]>(sm + 7 * YT * YP);  // M_{I-1,J}, then Z
+  float* uiinv = sm + 8 * YT * YP;                                    // 1 / U_I[j][j]
   float* erow = uiinv + YT;                                           // [2][YT]
   float* tcol = erow + 2 * YT;                                        // [2][YT]
   uint8_t(*Cs)[YCP] = reinterpret_cast<uint8_t(*)[YCP]>(tcol + 2 * YT);
@@ -120,57 +123,76 @@ __global__ __launch_bounds__(256) void yaqa_tile_kernel(YaqaStep a) {
   const int lane = t & 63, w = t >> 6;
   const int lr = lane & 31, lk = lane >> 5;
   const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
+  const int i = t / YNSEG;
+  const int cb = (t % YNSEG) * YSEG;
+  const int64_t grow = r0 + i;
 
-  for (int e4 = t; e4 < YT * YT / 4; e4 += 256) {
+  // every operand block in flight at once: the diagonal blocks of U_I and
+  // U_O, Mpart, this thread's Wk, and the two neighbours' operands
+  constexpr int NB = YT * YT / 4 / 256;  // float4 per thread and block
+  float4 gUI[NB], gUO[NB], gM[NB], gEL[NB], gUIo[NB], gUOo[NB], gMa[NB], wk[YSEG / 4];
+  const int64_t cl = J > 0 ? c0 - YT : c0, ru = I > 0 ? r0 - YT : r0;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int e4 = t + 256 * k;
     const int r = e4 / (YT / 4), c = (e4 % (YT / 4)) * 4;
-    float4 ui = *reinterpret_cast<const float4*>(a.UI + (c0 + r) * a.ldI + c0 + c);
+    gUI[k] = *reinterpret_cast<const float4*>(a.UI + (c0 + r) * a.ldI + c0 + c);
+    gUO[k] = *reinterpret_cast<const float4*>(a.UO + (r0 + r) * a.ldO + r0 + c);
+    gM[k] = *reinterpret_cast<const float4*>(a.Mp + (r0 + r) * a.ld + c0 + c);
+    // without a left or upper neighbour these read the tile's own blocks
+    // (in bounds, unused)
+    gEL[k] = *reinterpret_cast<const float4*>(a.E + (r0 + r) * a.ld + cl + c);
+    gUIo[k] = *reinterpret_cast<const float4*>(a.UI + (cl + r) * a.ldI + c0 + c);
+    gUOo[k] = *reinterpret_cast<const float4*>(a.UO + (ru + r) * a.ldO + r0 + c);
+    gMa[k] = *reinterpret_cast<const float4*>(a.Mp + (ru + r) * a.ld + c0 + c);
+  }
+#pragma unroll
+  for (int j = 0; j < YSEG / 4; ++j)
+    wk[j] = *reinterpret_cast<const float4*>(a.Wk + grow * a.ld + c0 + cb + 4 * j);
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int e4 = t + 256 * k;
+    const int r = e4 / (YT / 4), c = (e4 % (YT / 4)) * 4;
+    float4 ui = gUI[k];
     ui.x = c >= r ? ui.x : 0.f;
     ui.y = c + 1 >= r ? ui.y : 0.f;
     ui.z = c + 2 >= r ? ui.z : 0.f;
     ui.w = c + 3 >= r ? ui.w : 0.f;
     *reinterpret_cast<float4*>(&UIs[r][c]) = ui;
-    const float4 uo = *reinterpret_cast<const float4*>(a.UO + (r0 + r) * a.ldO + r0 + c);
+    const float4 uo = gUO[k];
     UOt[c][r] = c >= r ? uo.x : 0.f;
     UOt[c + 1][r] = c + 1 >= r ? uo.y : 0.f;
     UOt[c + 2][r] = c + 2 >= r ? uo.z : 0.f;
     UOt[c + 3][r] = c + 3 >= r ? uo.w : 0.f;
-  }
-  load_block(Ms, a.Mp + r0 * a.ld + c0, a.ld, t);
-  if (J > 0) {
-    load_block(A1, a.E + r0 * a.ld + c0 - YT, a.ld, t);       // e_{I,J-1} as [m][k]
-    load_block(B1, a.UI + (c0 - YT) * a.ldI + c0, a.ldI, t);  // U_I[J-1, J] as [k][n]
+    *reinterpret_cast<float4*>(&Ms[r][c]) = gM[k];
+    *reinterpret_cast<float4*>(&A1[r][c]) = gEL[k];   // e_{I,J-1} as [m][k]
+    *reinterpret_cast<float4*>(&B1[r][c]) = gUIo[k];  // U_I[J-1, J] as [k][n]
+    *reinterpret_cast<float4*>(&A2[r][c]) = gUOo[k];  // U_O[I-1, I] as [k][m]
+    *reinterpret_cast<float4*>(&B2[r][c]) = gMa[k];   // M_{I-1, J}
   }
   if (t < 4 * YT) erow[t] = 0.f;  // erow and tcol (contiguous)
   __syncthreads();
   if (t < YT) uiinv[t] = 1.f / UIs[t][t];
 
+  // P2 into Mpart; P1 + U_O[I,I]^T (Mpart + P2) into acc
+  f32x16 acc, acc2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc[r] = 0.f;
+    acc2[r] = 0.f;
+  }
+  if (J > 0) mfma_k64<true>(A1, B1, acc2, wm, wn, lr, lk);
+  if (I > 0) mfma_k64<false>(A2, B2, acc, wm, wn, lr, lk);
   if (J > 0) {
-    f32x16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    mfma_k64<true>(A1, B1, acc, wm, wn, lr, lk);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Ms[wm + 8 * (r >> 2) + 4 * lk + (r & 3)][wn + lr] += acc[r];
-    __syncthreads();
+    for (int r = 0; r < 16; ++r) Ms[wm + 8 * (r >> 2) + 4 * lk + (r & 3)][wn + lr] += acc2[r];
   }
-  f32x16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  if (I > 0) {
-    load_block(A1, a.UO + (r0 - YT) * a.ldO + r0, a.ldO, t);  // U_O[I-1, I] as [k][m]
-    load_block(B1, a.Mp + (r0 - YT) * a.ld + c0, a.ld, t);    // M_{I-1, J}
-    __syncthreads();
-    mfma_k64<false>(A1, B1, acc, wm, wn, lr, lk);
-  }
-  mfma_k64<true>(UOt, Ms, acc, wm, wn, lr, lk);
   __syncthreads();
+  mfma_k64<true>(UOt, Ms, acc, wm, wn, lr, lk);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) B1[wm + 8 * (r >> 2) + 4 * lk + (r & 3)][wn + lr] = acc[r];
+  for (int r = 0; r < 16; ++r) B2[wm + 8 * (r >> 2) + 4 * lk + (r & 3)][wn + lr] = acc[r];
   __syncthreads();
 
-  const int i = t / YNSEG;
-  const int cb = (t % YNSEG) * YSEG;
-  const int64_t grow = r0 + i;
   float sc = 1.f, zr = 0.f;  // padded rows: any finite grid
   if (grow < a.d_out) {
     sc = a.scale[grow];
@@ -182,11 +204,10 @@ __global__ __launch_bounds__(256) void yaqa_tile_kernel(YaqaStep a) {
 
   float v[YSEG], tt[YSEG], tcp[YSEG], uic[YSEG], win[8];
   {
-    const float* wp = a.Wk + grow * a.ld + c0 + cb;
 #pragma unroll
     for (int j = 0; j < YSEG; j += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(wp + j);
-      const float4 z = *reinterpret_cast<const float4*>(&B1[i][cb + j]);
+      const float4 x = wk[j / 4];
+      const float4 z = *reinterpret_cast<const float4*>(&B2[i][cb + j]);
       v[j] = x.x - z.x;
       v[j + 1] = x.y - z.y;
       v[j + 2] = x.z - z.z;
