@@ -150,9 +150,52 @@ def run_gpu(spec, steps, warmup, data):
         print(f"objective check failed: {e}", file=sys.stderr)
         obj_rtn = None
     inf = run_inference(spec, codes, scale, zero, s_x, s_g, si, so)
+    fb = run_output_feedback(spec, W0p, HX, D, HG, U, obj) if W0p is not None and not spec.group else None
     cap = run_streaming(spec, X, Xq, G, HX, D, HG, ws)
     return dict(wall_s=wall, stage_ms=stage_ms, cov_kernel_ms=cov_kernel_ms, sens=sens, obj=obj,
-                obj_rtn=obj_rtn, inference=inf, streaming=cap)
+                obj_rtn=obj_rtn, inference=inf, streaming=cap, output_feedback=fb)
+
+
+def run_output_feedback(spec, W0p, HX, D, HG, U, obj_gptaq, reps=3):
+    """The rounding with output-side feedback (generalized LDLQ on H_G' x H_X')
+    on the same processed layer: U_out from H_G', the GPTAQ fold as target.
+    Time per call (the call synchronizes), its algorithmic flops, and the
+    layer objective beside the one-sided sweep's."""
+    import torch
+
+    import post_weight_quantization_amd as kq
+    from post_weight_quantization_amd import _native as N
+
+    m, n = spec.d_out, spec.d_in
+    stream = torch.cuda.current_stream()
+    cfg = N.kq_quant_cfg(spec.bits, 0, 128, 0)
+    ws = torch.empty(max(kq.kq_workspace_size(N.KQ_OP_YAQA_QUANTIZE, m, n, cfg=cfg),
+                         kq.kq_workspace_size(N.KQ_OP_CHOLESKY_INV, m, m)), dtype=torch.uint8,
+                     device=W0p.device)
+    Uo = torch.empty(m, m, dtype=torch.float32, device=W0p.device)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    kq.kq_cholesky_inv(HG, spec.damp, Uo, ws=ws)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    chol_ms = ev[0].elapsed_time(ev[1])
+    W = W0p.clone()
+    kq.kq_yaqa_quantize(W, U, Uo, D, spec.bits, ws=ws)  # warm-up
+    ts = []
+    for _ in range(reps):
+        W.copy_(W0p)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        kq.kq_yaqa_quantize(W, U, Uo, D, spec.bits, ws=ws)
+        ts.append(time.perf_counter() - t0)
+    ms = 1e3 * float(np.median(ts))
+    obj = kq.kq_layer_objective(W0p, W, HX, D, HG)
+    # row feedback m n^2, column feedback m^2 n, P formation 2 n^3 / 3, fold m n^2 (2 flops per FMA)
+    flops = m * n * n + m * m * n + 2 * n ** 3 / 3 + m * n * n
+    return {"ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 2),
+            "frac_fp32_mfma": round(flops / (ms * 1e-3) / PEAK_FP32_MFMA, 3),
+            "u_out_factor_ms": round(chol_ms, 3),
+            "objective": obj, "objective_one_sided": obj_gptaq}
 
 
 def run_streaming(spec, X, Xq, G, HX, D, HG, ws, chunk=16384, reps=3):
@@ -381,6 +424,7 @@ def main():
         "cpu_baseline": cpu,
         "inference": g["inference"],
         "streaming_covariances": g["streaming"],
+        "output_feedback": g["output_feedback"],
     }
     print(json.dumps(out))
 
