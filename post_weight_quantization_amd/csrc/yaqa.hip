@@ -385,32 +385,6 @@ kq_status pad_copy(const float* src, int64_t rows, int64_t cols, float* dst, int
 
 inline int64_t pad_to(int64_t x) { return cdiv(x, YT) * YT; }
 
-// A second stream (default priority) and two rings of events for the
-// overlap of the far feedback with the next wavefront step; released when
-// the call returns, after the caller's stream has been synchronized.
-struct Side {
-  static constexpr int NE = 4;
-  hipStream_t st = nullptr;
-  hipEvent_t tiles[NE] = {};
-  hipEvent_t done[NE] = {};
-  kq_status open() {
-    KQ_HIP(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
-    for (int k = 0; k < NE; ++k) {
-      KQ_HIP(hipEventCreateWithFlags(&tiles[k], hipEventDisableTiming));
-      KQ_HIP(hipEventCreateWithFlags(&done[k], hipEventDisableTiming));
-    }
-    return KQ_OK;
-  }
-  ~Side() {
-    if (st) hipStreamSynchronize(st);
-    for (int k = 0; k < NE; ++k) {
-      if (tiles[k]) hipEventDestroy(tiles[k]);
-      if (done[k]) hipEventDestroy(done[k]);
-    }
-    if (st) hipStreamDestroy(st);
-  }
-};
-
 }  // namespace
 
 size_t yaqa_ws_bytes(int64_t d_out, int64_t d_in, bool has_d) {
@@ -496,20 +470,20 @@ kq_status yaqa_run(float* W, const float* U_in, const float* U_out, const float*
 
   // The far feedback of step s (targets two or more tiles away) runs on a
   // second stream while the tiles of step s + 1 run; step s + 2 waits for it.
-  Side side;
+  SideStream side;
   KQ_TRY(side.open());
   const int nsteps = mt + nt - 1;
   for (int sidx = 0; sidx < nsteps; ++sidx) {
     const int I_lo = std::max(0, sidx - nt + 1), I_hi = std::min(sidx, mt - 1);
     const int cnt = I_hi - I_lo + 1;
     const int J_hi = sidx - I_lo;
-    if (sidx >= 2) KQ_HIP(hipStreamWaitEvent(s, side.done[(sidx - 2) % Side::NE], 0));
+    if (sidx >= 2) KQ_HIP(hipStreamWaitEvent(s, side.done[(sidx - 2) % SideStream::NE], 0));
     st.s = sidx;
     st.I_lo = I_lo;
     yaqa_tile_kernel<<<unsigned(cnt), 256, YAQA_LDS, s>>>(st);
     KQ_HIP(hipGetLastError());
-    KQ_HIP(hipEventRecord(side.tiles[sidx % Side::NE], s));
-    KQ_HIP(hipStreamWaitEvent(side.st, side.tiles[sidx % Side::NE], 0));
+    KQ_HIP(hipEventRecord(side.tiles[sidx % SideStream::NE], s));
+    KQ_HIP(hipStreamWaitEvent(side.st, side.tiles[sidx % SideStream::NE], 0));
     // M[I, blocks >= J + 2] += e_IJ U_I[J, same]
     GemmArgs gr = gemm_args(E + int64_t(I_lo) * YT * np + int64_t(J_hi) * YT, np,
                             UI + int64_t(J_hi) * YT * np, np, Mp + int64_t(I_lo) * YT * np, np, YT,
@@ -533,9 +507,9 @@ kq_status yaqa_run(float* W, const float* U_in, const float* U_out, const float*
     gc.ostart = int64_t(I_lo + 2) * YT;
     gc.ostart_ofs = YT;
     if (I_lo + 2 < mt) KQ_TRY(gemm_f32(gc, side.st));  // the smallest I has targets
-    KQ_HIP(hipEventRecord(side.done[sidx % Side::NE], side.st));
+    KQ_HIP(hipEventRecord(side.done[sidx % SideStream::NE], side.st));
   }
-  KQ_HIP(hipStreamWaitEvent(s, side.done[(nsteps - 1) % Side::NE], 0));
+  KQ_HIP(hipStreamWaitEvent(s, side.done[(nsteps - 1) % SideStream::NE], 0));
   KQ_HIP(hipStreamSynchronize(s));
   return KQ_OK;
 }
