@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 
+import numpy as np
 import torch
 
 from . import _native as N
@@ -32,6 +33,16 @@ def _need_cuda(*ts):
                 raise ValueError("tensors must be on the GPU")
             if not t.is_contiguous():
                 raise ValueError("tensors must be contiguous")
+
+
+def _expect(t, shape, dtype, name):
+    """Shape and dtype of a tensor handed to the library (it sees raw pointers)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) and t.numel() != int(np.prod(shape)):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
 
 
 def kq_workspace_size(op: int, d_out: int, d_in: int, n_tok: int = 0, dtype: int = N.KQ_BF16,
@@ -155,6 +166,14 @@ def kq_yaqa_quantize(W, U_in, U_out, D, bits: int, codes=None, scale=None, zero=
     (U_out); returns (codes, scale, zero), one grid per output channel."""
     _need_cuda(W, U_in, U_out, D, codes, scale, zero)
     d_out, d_in = W.shape
+    f32 = torch.float32
+    _expect(W, (d_out, d_in), f32, "W")
+    _expect(U_in, (d_in, d_in), f32, "U_in")
+    _expect(U_out, (d_out, d_out), f32, "U_out")
+    _expect(D, (d_in, d_in), f32, "D")
+    _expect(codes, (d_out, d_in), torch.uint8, "codes")
+    _expect(scale, (d_out, 1), f32, "scale")
+    _expect(zero, (d_out, 1), f32, "zero")
     dev = W.device
     cfg = N.kq_quant_cfg(bits, 0, 128, 0)
     if codes is None:

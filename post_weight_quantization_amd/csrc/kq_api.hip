@@ -147,7 +147,7 @@ kq_status kq_workspace_size(kq_op op, int64_t d_out, int64_t d_in, int64_t n_tok
       *bytes = apply_ws_bytes(d_out, d_in, n_tok);
       return KQ_OK;
     case KQ_OP_YAQA_QUANTIZE:
-      if (d_out < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
+      if (d_out < 1 || d_in < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
       *bytes = yaqa_ws_bytes(d_out, d_in, true);
       return KQ_OK;
   }
