@@ -16,7 +16,8 @@
 //
 // Order used here: a wavefront over 64 x 64 tiles. The tiles (I, J) with
 // I + J = s form one launch, one workgroup per tile, and inside a tile the
-// entries run as a skewed wavefront (row i reaches column j at step i + j).
+// entries run as a skewed wavefront (row i reaches column j at step 2 i + j,
+// below).
 // What a tile needs from outside arrives through two accumulators in HBM:
 //   M[I,J] = sum_{L<=J} e_{I,L} U_I[L,J]            (row feedback)
 //   Wk     = W* - sum_{K<I} U_O[K,I]^T M[K,J]          (column feedback)
@@ -83,13 +84,6 @@ __device__ inline void mfma_k64(const float (*Ap)[YP], const float (*Bp)[YP], f3
     const float av = AT ? Ap[wm + lr][kk + lk] : Ap[kk + lk][wm + lr];
     const float bv = Bp[kk + lk][wn + lr];
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
-  }
-}
-
-__device__ inline void load_block(float (*dst)[YP], const float* src, int64_t lds, int t) {
-  for (int e4 = t; e4 < YT * YT / 4; e4 += 256) {
-    const int r = e4 / (YT / 4), c = (e4 % (YT / 4)) * 4;
-    *reinterpret_cast<float4*>(&dst[r][c]) = *reinterpret_cast<const float4*>(src + r * lds + c);
   }
 }
 
