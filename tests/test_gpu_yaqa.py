@@ -120,11 +120,12 @@ def test_yaqa_on_the_toy_layer():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("d_out,d_in,with_d", [(4096, 4096, True), (1000, 4100, False)])
+@pytest.mark.parametrize("d_out,d_in,with_d", [(4096, 4096, True), (1000, 4100, False),
+                                                (8192, 8192, True)])
 def test_yaqa_full_size_residuals(d_out, d_in, with_d):
-    """The bench layer's shape (2-bit, one grid per channel) and a ragged
-    one: every residual solved back from the result lies within half a grid
-    step (1e-4 of a step of slack for fp32)."""
+    """The bench layer's shape (2-bit, one grid per channel), a ragged one and
+    the 70B q_proj shape: every residual solved back from the result lies
+    within half a grid step (1e-4 of a step of slack for fp32)."""
     rng = np.random.default_rng(d_out + d_in)
     print(f"[yaqa full] {d_out}x{d_in} D={with_d}: factors", flush=True)
     UI = oracle.inv_factor(spd(rng, d_in, 1e3), 0.01).astype(np.float32)
