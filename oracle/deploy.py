@@ -102,3 +102,67 @@ def infer(x, packed, bits: int, scale, zero, group: int, s_x, s_g, sign_in, sign
     y1 = Wq @ x2                                                     # d_out x B
     y2 = np.asarray(sign_out, np.float64)[:, None] * apply_hadamard_left(y1, np.ones(d_out), bo)
     return (y2 / np.asarray(s_g, np.float64)[:, None]).T
+
+
+# ---------------------------------------------------------------------------
+# Weights and activations both quantized (the W2A4 setting).
+#
+# [GS] KronQ explainer, "Quantizzazione di Pesi e Attivazioni": for the
+# weight-and-activation results the activations follow the QuaRot recipe.
+# The pages give no more than that. Readings taken here:
+#   * the activation is quantized where the rotation leaves it, i.e. the
+#     rotated input x2 = V S_X^-1 x that the quantized rows W^' act on
+#     (the rotation spreads outliers before rounding);
+#   * one grid per vector (per token), symmetric, round to nearest (ties to
+#     even), s = clip * max_k |x2_k| / (2^(b-1) - 1), q = clamp(rint(x2 / s),
+#     -2^(b-1), 2^(b-1) - 1); the clipping ratio is the caller's; an all-zero
+#     vector has s = 0 and q = 0;
+#   * the integer decision is taken in fp32 (x2 rounded to fp32, then the
+#     max, the product with clip, the division by 2^(b-1) - 1 and the division
+#     x2 / s each rounded to fp32), the precision of the kernels.
+
+
+def quantize_activations(x2, bits: int = 4, clip: float = 1.0, forced=None):
+    """Per-vector symmetric RTN of x2 (B x d_in). Returns dict(q int8, s fp32
+    per vector, t = x2 / s in fp32: the values that were rounded).
+
+    forced: codes to use instead of the rounding (each must be within 1e-4 of
+    a rounding boundary of t where it differs; the caller checks that)."""
+    x = np.atleast_2d(np.asarray(x2, np.float64)).astype(np.float32)
+    qmax = (1 << (bits - 1)) - 1
+    mx = np.max(np.abs(x), axis=1)
+    s = (np.float32(clip) * mx).astype(np.float32) / np.float32(qmax)
+    s = s.astype(np.float32)
+    t = np.zeros_like(x)
+    nz = s > 0
+    t[nz] = x[nz] / s[nz, None]
+    q = np.clip(np.rint(t), -qmax - 1, qmax).astype(np.int8)
+    if forced is not None:
+        q = np.asarray(forced, np.int8).reshape(q.shape)
+    return {"q": q, "s": s, "t": t}
+
+
+def rotate_input(x, s_x, sign_in, blk_in: int = 0) -> np.ndarray:
+    """x2 = V S_X^-1 x for a batch (B x d_in), in fp64."""
+    x = np.atleast_2d(np.asarray(x, np.float64))
+    bi = blk_in or hadamard_block(x.shape[1])
+    x1 = x / np.asarray(s_x, np.float64)[None, :]
+    return apply_hadamard_left(x1.T, sign_in, bi).T
+
+
+def infer_a4(x, packed, bits: int, scale, zero, group: int, s_x, s_g, sign_in, sign_out,
+             blk_in: int = 0, blk_out: int = 0, act_bits: int = 4, clip: float = 1.0,
+             forced_act=None) -> dict:
+    """y = S_G^-1 U^T (W^' (s q)) with (q, s) the per-vector quantization of
+    x2 = V S_X^-1 x, step by step (fp64 apart from the fp32 decision).
+    Returns dict(y, q, s, t)."""
+    x2 = rotate_input(x, s_x, sign_in, blk_in)
+    qa = quantize_activations(x2, act_bits, clip, forced_act)
+    d_in = x2.shape[1]
+    d_out = np.asarray(packed).shape[0]
+    bo = blk_out or hadamard_block(d_out)
+    xa = qa["s"].astype(np.float64)[:, None] * qa["q"].astype(np.float64)   # B x d_in
+    Wq = dequantize(unpack_codes(packed, bits, d_in), scale, zero, group)
+    y1 = Wq @ xa.T                                                            # d_out x B
+    y2 = np.asarray(sign_out, np.float64)[:, None] * apply_hadamard_left(y1, np.ones(d_out), bo)
+    return {"y": (y2 / np.asarray(s_g, np.float64)[:, None]).T, **qa}
