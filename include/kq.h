@@ -64,7 +64,8 @@ typedef enum {
   KQ_OP_GPTAQ_QUANTIZE = 5,
   KQ_OP_LAYER_OBJECTIVE = 6,
   KQ_OP_APPLY_QUANTIZED = 7, /* n_tok argument of kq_workspace_size = batch */
-  KQ_OP_YAQA_QUANTIZE = 8
+  KQ_OP_YAQA_QUANTIZE = 8,
+  KQ_OP_APPLY_QUANTIZED_A4 = 9 /* n_tok argument of kq_workspace_size = batch */
 } kq_op;
 
 /* Grid and sweep configuration (KronQ summary, Method and experiments:
@@ -97,6 +98,8 @@ const char* kq_version(void);
  *          KQ_OP_APPLY_QUANTIZED: the product with the packed codes (one
  *          launch per 4 vectors of the batch; the two transforms lie
  *          outside the bracket).
+ *          KQ_OP_APPLY_QUANTIZED_A4: the integer product (one launch per 16
+ *          vectors; the transforms and the input quantization lie outside).
  *   start, stop  events created by the caller (who owns and destroys them);
  *          both NULL switches the hook off.
  * Errors: KQ_ERR_UNSUPPORTED for other ops, KQ_ERR_ARG if exactly one event
@@ -281,6 +284,34 @@ kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* 
                              const int8_t* sign_in, const int8_t* sign_out, int64_t blk_in,
                              int64_t blk_out, const float* x, int64_t batch, int64_t d_out,
                              int64_t d_in, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weights and activations both quantized (the W2A4 setting; KronQ explainer,
+ * gist.science, "Quantizzazione di Pesi e Attivazioni": activations follow
+ * the QuaRot recipe). The rotated input x2 = V S_X^-1 x of each vector is
+ * rounded to 4 bits on its own symmetric grid,
+ *   s_b = clip * max_k |x2_bk| / 7,   a_bk = clamp(rint(x2_bk / s_b), -8, 7)
+ * (fp32, ties to even; an all-zero vector has s_b = 0 and a_b = 0), and
+ *   y = S_G^-1 U^T (W^' (s a)),
+ * with the product W^' (s a) exact in integers (2-bit codes times 4-bit
+ * inputs) before one scaling per row and vector.
+ *   packed              2-bit codes from kq_pack_codes, one grid per row
+ *   scale, zero         the grids of kq_gptaq_quantize (d_out floats each)
+ *   s_x, s_g, sign_in, sign_out, blk_in, blk_out   as kq_apply_quantized
+ *   x                   batch x d_in fp32, row-major (not modified)
+ *   clip                clipping ratio of the activation grid, 0 < clip <= 1
+ *   y                   batch x d_out fp32 output
+ *   act_codes           NULL, or batch x d_in int8 output: the codes a
+ *   act_scale           NULL, or batch floats output: the scales s
+ * d_in must be a multiple of 512 and d_out of 4. packed, x, y, s_x and
+ * act_codes must be 16-byte aligned. Workspace from
+ * kq_workspace_size(KQ_OP_APPLY_QUANTIZED_A4, d_out, d_in, batch, ...).
+ * Asynchronous. Errors: KQ_ERR_ARG (NULL, alignment, clip), KQ_ERR_SHAPE. */
+kq_status kq_apply_quantized_a4(const uint32_t* packed, const float* scale, const float* zero,
+                                const float* s_x, const float* s_g, const int8_t* sign_in,
+                                const int8_t* sign_out, int64_t blk_in, int64_t blk_out,
+                                const float* x, int64_t batch, int64_t d_out, int64_t d_in,
+                                float clip, float* y, int8_t* act_codes, float* act_scale,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

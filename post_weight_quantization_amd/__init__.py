@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     kq_accumulate_cov,
     kq_allocate_bits,
     kq_apply_quantized,
+    kq_apply_quantized_a4,
     kq_biip,
     kq_cholesky_inv,
     kq_form_p,

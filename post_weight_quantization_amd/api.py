@@ -253,3 +253,34 @@ def kq_apply_quantized(packed, bits: int, scale, zero, group: int, s_x, s_g, sig
                                    _ptr(s_g), _ptr(sign_in), _ptr(sign_out), blk_in, blk_out, _ptr(x),
                                    batch, d_out, d_in, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def kq_apply_quantized_a4(packed, scale, zero, s_x, s_g, sign_in, sign_out, x, clip: float = 1.0,
+                          blk_in: int = 0, blk_out: int = 0, y=None, act_codes=None, act_scale=None,
+                          ws=None, stream=None):
+    """The product with 2-bit weights and 4-bit activations: x2 = V S_X^-1 x
+    is rounded per vector to s * a (a in [-8, 7], s = clip * max|x2| / 7) and
+    y = S_G^-1 U^T W^' (s a). Returns y (batch x d_out); act_codes (batch x
+    d_in int8) and act_scale (batch fp32), if given, receive a and s."""
+    _need_cuda(packed, scale, zero, s_x, s_g, sign_in, sign_out, x, y, act_codes, act_scale)
+    batch, d_in = x.shape
+    d_out = packed.shape[0]
+    _expect(x, (batch, d_in), torch.float32, "x")
+    _expect(packed, (d_out, kq_packed_row_words(d_in, 2)), packed.dtype, "packed")
+    _expect(scale, (d_out,), torch.float32, "scale")
+    _expect(zero, (d_out,), torch.float32, "zero")
+    _expect(s_x, (d_in,), torch.float32, "s_x")
+    _expect(s_g, (d_out,), torch.float32, "s_g")
+    _expect(sign_in, (d_in,), torch.int8, "sign_in")
+    _expect(sign_out, (d_out,), torch.int8, "sign_out")
+    _expect(y, (batch, d_out), torch.float32, "y")
+    _expect(act_codes, (batch, d_in), torch.int8, "act_codes")
+    _expect(act_scale, (batch,), torch.float32, "act_scale")
+    if y is None:
+        y = torch.empty(batch, d_out, dtype=torch.float32, device=x.device)
+    ws = _ws(kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED_A4, d_out, d_in, batch), x.device, ws)
+    check(N.lib.kq_apply_quantized_a4(_ptr(packed), _ptr(scale), _ptr(zero), _ptr(s_x), _ptr(s_g),
+                                      _ptr(sign_in), _ptr(sign_out), blk_in, blk_out, _ptr(x), batch,
+                                      d_out, d_in, float(clip), _ptr(y), _ptr(act_codes),
+                                      _ptr(act_scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return y

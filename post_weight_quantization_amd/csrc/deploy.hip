@@ -844,6 +844,286 @@ kq_status run_mx(const uint32_t* packed, int64_t rw, const float* scale, const f
   return mark_kernel(KQ_OP_APPLY_QUANTIZED, 1, s);
 }
 
+
+// ---- Weights and activations both quantized: 2-bit codes, 4-bit inputs.
+// Each vector's rotated input x2 = V S_X^-1 x is rounded on a symmetric grid
+// of its own: s = (clip max_k |x2_k|) / 7 and a_k = clamp(rint(x2_k / s), -8,
+// 7), in fp32 with ties to even (an all-zero vector has s = 0, a = 0). The
+// product is then integer arithmetic on the matrix cores: the codes enter
+// as fp4 (q / 2) as in the path above and the input codes as e4m3 integers
+// with block scale 2, sixteen vectors in the 16 B columns of one
+// v_mfma_scale_f32_16x16x128_f8f6f4. Every partial sum sum_k q_k a_k is an
+// integer below 3 * 8 * d_in < 2^24, so fp32 holds it exactly and the
+// order of the sums does not matter; y1 = scale s (sum q a - zero sum a).
+//
+// B layout: vector tile T (16 vectors), super-step S (512 columns), step q,
+// lane l = 16 g + n: 32 bytes at xa[((T nss + S) 4 + q) 64 + l] for vector
+// 16 T + n; column u of the super-step sits at (q, g, byte) as in the MX
+// placement above. Staged per vector as (q 4 + g) 32 + byte.
+constexpr int A4_TILE = 16;           // vectors per column tile
+constexpr int A4_SSB = 4 * 64 * 32;   // bytes per tile and super-step
+constexpr float A4_QMAX = 7.f;
+
+__device__ inline int a4_slot(int u) {
+  const int G = (u >> 6) & 3, q = 2 * (u >> 8) + ((u >> 5) & 1), p = u & 31;
+  const int j = 8 * (2 * (p >> 4) + (p & 1)) + ((p & 15) >> 1);
+  const int k = 32 * G + j;
+  const int g = (k & 63) >> 4, jb = (k & 15) + 16 * (k >> 6);
+  return (q * 4 + g) * 32 + jb;
+}
+
+__device__ inline int a4_code(float v, float s) {
+  if (!(s > 0.f)) return 0;
+  return int(fminf(fmaxf(rintf(v / s), -8.f), A4_QMAX));
+}
+
+// Largest value over the workgroup (every thread gets it). part: >= 16 floats.
+__device__ inline float block_max(float m, float* part) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = 0.f;
+  for (int w = 0; w < int(blockDim.x >> 6); ++w) r = fmaxf(r, part[w]);
+  return r;
+}
+
+// Quantize columns e .. e + 3 of a super-step-aligned run of one vector
+// (values v) into the staging bytes and, if wanted, the caller's codes.
+__device__ inline int a4_put4(float4 v, float s, int e, uint8_t* stg, int8_t* codes_out) {
+  const int c0 = a4_code(v.x, s), c1 = a4_code(v.y, s), c2 = a4_code(v.z, s), c3 = a4_code(v.w, s);
+  const int base = e & ~(MX_SS - 1), u = e & (MX_SS - 1);
+  stg[base + a4_slot(u)] = kE4M3Int[c0 + 8];
+  stg[base + a4_slot(u + 1)] = kE4M3Int[c1 + 8];
+  stg[base + a4_slot(u + 2)] = kE4M3Int[c2 + 8];
+  stg[base + a4_slot(u + 3)] = kE4M3Int[c3 + 8];
+  if (codes_out)
+    *reinterpret_cast<char4*>(codes_out + e) = make_char4(char(c0), char(c1), char(c2), char(c3));
+  return c0 + c1 + c2 + c3;
+}
+
+// Staged bytes of super-steps [S0, S0 + nS) of vector b -> their places in xa.
+__device__ inline void a4_store(const uint8_t* stg, int nS, int64_t b, int64_t S0, int64_t nss,
+                                uint8_t* __restrict__ xa) {
+  const int64_t T = b / A4_TILE, n = b % A4_TILE;
+  for (int i = threadIdx.x; i < nS * 32; i += blockDim.x) {
+    const int S = i >> 5, r = (i >> 1) & 15, h = i & 1;  // run r = 4 q + g, half h
+    const int q = r >> 2, g = r & 3;
+    uint8_t* dst = xa + ((T * nss + S0 + S) * 4 + q) * (64 * 32) + (16 * g + n) * 32 + 16 * h;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(stg + S * MX_SS + r * 32 + 16 * h);
+  }
+}
+
+// x2 = gain * H_blk (x[b] sign_in / s_x) over L columns. FUSED (the chunk is
+// the whole vector): quantize it here. Otherwise write x2 and the chunk's
+// largest magnitude for quantize_a4_kernel.
+template <bool FUSED>
+__global__ __launch_bounds__(1024) void transform_in_a4_kernel(
+    const float* __restrict__ x, int64_t d_in, int lgL, int lgb, const int8_t* __restrict__ si,
+    const float* __restrict__ s_x, float gain, float clip, float* __restrict__ x2,
+    float* __restrict__ pmax, uint8_t* __restrict__ xa, float* __restrict__ ascale,
+    int* __restrict__ asum, int8_t* __restrict__ codes_out, float* __restrict__ scale_out) {
+  __shared__ float s[TCHP];
+  __shared__ __align__(16) uint8_t stg[FUSED ? TCH : 16];
+  __shared__ float part[16];
+  __shared__ int ipart[16];
+  const int L = 1 << lgL;
+  const int64_t per_row = d_in >> lgL;
+  const int64_t b = blockIdx.x / per_row;
+  const int64_t c0 = int64_t(blockIdx.x % per_row) << lgL;
+  const float* src = x + b * d_in + c0;
+  for (int e = 4 * threadIdx.x; e < L; e += 4 * blockDim.x) {
+    const float4 v = *reinterpret_cast<const float4*>(src + e);
+    const float4 sx = *reinterpret_cast<const float4*>(s_x + c0 + e);
+    s[padi(e)] = v.x * float(si[c0 + e]) / sx.x;
+    s[padi(e + 1)] = v.y * float(si[c0 + e + 1]) / sx.y;
+    s[padi(e + 2)] = v.z * float(si[c0 + e + 2]) / sx.z;
+    s[padi(e + 3)] = v.w * float(si[c0 + e + 3]) / sx.w;
+  }
+  __syncthreads();
+  lds_fwht(s, L, 0, lgb);
+  __syncthreads();
+  float mx = 0.f;
+  for (int e = 4 * threadIdx.x; e < L; e += 4 * blockDim.x) {
+    const float4 v = make_float4(gain * s[padi(e)], gain * s[padi(e + 1)], gain * s[padi(e + 2)],
+                                 gain * s[padi(e + 3)]);
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    if (!FUSED) *reinterpret_cast<float4*>(x2 + b * d_in + c0 + e) = v;
+  }
+  mx = block_max(mx, part);
+  if constexpr (!FUSED) {
+    if (threadIdx.x == 0) {
+      pmax[blockIdx.x] = mx;
+      if (c0 == 0) asum[b] = 0;
+    }
+  } else {
+    const float sc = (clip * mx) / A4_QMAX;
+    int8_t* co = codes_out ? codes_out + b * d_in : nullptr;
+    int cs = 0;
+    for (int e = 4 * threadIdx.x; e < L; e += 4 * blockDim.x) {
+      const float4 v = make_float4(gain * s[padi(e)], gain * s[padi(e + 1)], gain * s[padi(e + 2)],
+                                   gain * s[padi(e + 3)]);
+      cs += a4_put4(v, sc, e, stg, co);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cs += __shfl_xor(cs, o);
+    if ((threadIdx.x & 63) == 0) ipart[threadIdx.x >> 6] = cs;
+    __syncthreads();
+    a4_store(stg, L / MX_SS, b, 0, d_in / MX_SS, xa);
+    if (threadIdx.x == 0) {
+      int t = 0;
+      for (int w = 0; w < int(blockDim.x >> 6); ++w) t += ipart[w];
+      asum[b] = t;
+      ascale[b] = sc;
+      if (scale_out) scale_out[b] = sc;
+    }
+  }
+}
+
+// One workgroup of 128 threads per (vector, super-step): the vector's scale
+// from its chunk maxima, then its 512 values quantized and placed.
+__global__ __launch_bounds__(128) void quantize_a4_kernel(
+    const float* __restrict__ x2, const float* __restrict__ pmax, int nparts, int64_t d_in,
+    int64_t nss, float clip, uint8_t* __restrict__ xa, float* __restrict__ ascale,
+    int* __restrict__ asum, int8_t* __restrict__ codes_out, float* __restrict__ scale_out) {
+  __shared__ __align__(16) uint8_t stg[MX_SS];
+  __shared__ int ipart[2];
+  const int64_t b = blockIdx.x / nss, S = blockIdx.x % nss;
+  float mx = 0.f;
+  for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, pmax[b * nparts + p]);
+  const float sc = (clip * mx) / A4_QMAX;
+  const int e = 4 * threadIdx.x;
+  const float4 v = *reinterpret_cast<const float4*>(x2 + b * d_in + S * MX_SS + e);
+  int cs = a4_put4(v, sc, e, stg, codes_out ? codes_out + b * d_in + S * MX_SS : nullptr);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cs += __shfl_xor(cs, o);
+  if ((threadIdx.x & 63) == 0) ipart[threadIdx.x >> 6] = cs;
+  __syncthreads();
+  a4_store(stg, 1, b, S, nss, xa);
+  if (threadIdx.x == 0) {
+    atomicAdd(asum + b, ipart[0] + ipart[1]);  // integer: the order does not matter
+    if (S == 0) {
+      ascale[b] = sc;
+      if (scale_out) scale_out[b] = sc;
+    }
+  }
+}
+
+// y1[16 tile + v][rows] = scale (s_v (sum_k q_k a_vk - zero sum_k a_vk)) for
+// v < nvec and rows blockIdx.x * rpw .. + rpw - 1 (rpw <= 32). K ranges of RK
+// super-steps; wave w takes ranges w, w + waves, ... and holds a range's B
+// operands (all 16 vectors) in registers while it streams the rows.
+template <int RK>
+__global__ __launch_bounds__(1024) void qmatvec_a4_kernel(
+    const uint32_t* __restrict__ packed, int rw, const float* __restrict__ scale,
+    const float* __restrict__ zero, const uint8_t* __restrict__ xa, const float* __restrict__ ascale,
+    const int* __restrict__ asum, int64_t nss, int64_t d_out, int nkr, int rpw, int tile, int nvec,
+    float* __restrict__ y1) {
+  __shared__ float red[16][32 * A4_TILE];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int64_t rbeg = int64_t(blockIdx.x) * rpw;
+  const int nrows = int(min(int64_t(rpw), d_out - rbeg));
+  for (int i = lane; i < 32 * A4_TILE; i += 64) red[w][i] = 0.f;
+  const int n = lane & 15, G = lane >> 4;
+  const bool bcol = n < nvec;
+  const int ntile = (nrows + 15) / 16;
+  const int items = ((nkr - 1 - w) / nw + 1) * ntile;
+  auto load_a = [&](int it, uint4 (&dst)[RK][2]) {
+    const int kr = w + (it / ntile) * nw, t0 = (it % ntile) * 16;
+    const int64_t row = rbeg + min(t0 + n, nrows - 1);  // past the end: the last row, not stored
+#pragma unroll
+    for (int t = 0; t < RK; ++t) {
+      const int64_t S = min(int64_t(kr) * RK + t, nss - 1);  // past the end: unused
+      const uint4* ap = reinterpret_cast<const uint4*>(packed + row * rw + S * (MX_SS / 16) + G * 4);
+      dst[t][0] = ap[0];
+      dst[t][1] = ap[4];
+    }
+  };
+  v8i_t bop[RK][4];
+  uint4 an[RK][2];
+  load_a(0, an);
+  int cur_kr = -1;
+  for (int it = 0; it < items; ++it) {
+    const int kr = w + (it / ntile) * nw, t0 = (it % ntile) * 16;
+    if (kr != cur_kr) {
+      cur_kr = kr;
+#pragma unroll
+      for (int t = 0; t < RK; ++t) {
+        const int64_t S = int64_t(kr) * RK + t;
+        const bool ok = bcol && S < nss;
+        const uint8_t* bp = xa + ((int64_t(tile) * nss + (S < nss ? S : 0)) * 4) * (64 * 32) + lane * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4* p = reinterpret_cast<const uint4*>(bp + q * (64 * 32));
+          const uint4 lo = ok ? p[0] : make_uint4(0u, 0u, 0u, 0u);
+          const uint4 hi = ok ? p[1] : make_uint4(0u, 0u, 0u, 0u);
+          bop[t][q] = v8i_t{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        }
+      }
+    }
+    uint4 ac[RK][2];
+#pragma unroll
+    for (int t = 0; t < RK; ++t) {
+      ac[t][0] = an[t][0];
+      ac[t][1] = an[t][1];
+    }
+    if (it + 1 < items) load_a(it + 1, an);
+    v4f_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < RK; ++t) {
+      if (int64_t(kr) * RK + t >= nss) break;
+      const uint32_t wd[8] = {ac[t][0].x, ac[t][0].y, ac[t][0].z, ac[t][0].w,
+                              ac[t][1].x, ac[t][1].y, ac[t][1].z, ac[t][1].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x0 = wd[2 * q], x1 = wd[2 * q + 1];
+        const v8i_t aop = {int(x0 & 0x33333333u), int((x0 >> 2) & 0x33333333u),
+                           int(x1 & 0x33333333u), int((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+        // A scale 2^0, B scale 2^1 (E8M0 0x7f, 0x80): undoes the halved codes
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][q], acc, 4, 0, 0, 0x7f7f7f7f, 0,
+                                                               int(0x80808080u));
+      }
+    }
+    // acc[i] = C[4 G + i][n]: row t0 + 4 G + i, vector n
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t0 + 4 * G + i;
+      if (bcol && r < nrows) red[w][r * A4_TILE + n] += acc[i];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrows * nvec; i += blockDim.x) {
+    const int r = i / nvec, v = i % nvec;
+    float acc = 0.f;
+    for (int u = 0; u < nw; ++u) acc += red[u][r * A4_TILE + v];
+    const int64_t row = rbeg + r, vec = int64_t(tile) * A4_TILE + v;
+    y1[vec * d_out + row] = scale[row] * (ascale[vec] * (acc - zero[row] * float(asum[vec])));
+  }
+}
+
+struct A4Ws {
+  float* x2;
+  float* pmax;
+  uint8_t* xa;
+  float* ascale;
+  int* asum;
+};
+
+// Sized for any input block (at most d_in / 512 transform chunks per vector);
+// x2 is used only when a vector spans several chunks.
+A4Ws a4_take(Arena& ar, int64_t d_in, int64_t batch) {
+  A4Ws w;
+  w.x2 = ar.take<float>(size_t(batch) * d_in);
+  w.pmax = ar.take<float>(size_t(batch) * (d_in / MX_SS));
+  w.xa = ar.take<uint8_t>(size_t(cdiv(batch, A4_TILE)) * (d_in / MX_SS) * A4_SSB);
+  w.ascale = ar.take<float>(size_t(batch));
+  w.asum = ar.take<int>(size_t(batch));
+  return w;
+}
+
 }  // namespace
 
 int64_t packed_row_words(int64_t d_in, int bits) {
@@ -905,6 +1185,62 @@ kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const 
     default: KQ_TRY(run_bits<8>(packed, rw, scale, zero, ngroups, grouped, s_x, si, bi, x, batch, d_out, d_in, xq, y1, s)); break;
   }
   }
+  const int64_t Lo = transform_len(d_out, bo);
+  const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));
+  transform_out_kernel<<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(
+      y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), y);
+  KQ_HIP(hipGetLastError());
+  return KQ_OK;
+}
+
+
+size_t apply_a4_ws_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
+  Arena ar{nullptr, 0, 0};
+  a4_take(ar, d_in, batch);
+  ar.take<float>(size_t(batch) * d_out);  // y1
+  return ar.used;
+}
+
+kq_status apply_a4_run(const uint32_t* packed, const float* scale, const float* zero,
+                       const float* s_x, const float* s_g, const int8_t* si, const int8_t* so,
+                       int64_t bi, int64_t bo, const float* x, int64_t batch, int64_t d_out,
+                       int64_t d_in, float clip, float* y, int8_t* codes_out, float* scale_out,
+                       Arena& ws, hipStream_t s) {
+  const int64_t Li = transform_len(d_in, bi), nparts = d_in / Li, nss = d_in / MX_SS;
+  const A4Ws w = a4_take(ws, d_in, batch);
+  float* y1 = ws.take<float>(size_t(batch) * d_out);
+  if (!w.x2 || !w.pmax || !w.xa || !w.ascale || !w.asum || !y1)
+    return fail(KQ_ERR_WORKSPACE, "apply_quantized_a4: workspace too small");
+  const unsigned tin = unsigned(std::min<int64_t>(1024, Li / 4));
+  const float gain = float(1.0 / std::sqrt(double(bi)));
+  if (nparts == 1) {
+    transform_in_a4_kernel<true><<<unsigned(batch), tin, 0, s>>>(
+        x, d_in, ilog2(Li), ilog2(bi), si, s_x, gain, clip, nullptr, w.pmax, w.xa, w.ascale, w.asum,
+        codes_out, scale_out);
+    KQ_HIP(hipGetLastError());
+  } else {
+    transform_in_a4_kernel<false><<<unsigned(batch * nparts), tin, 0, s>>>(
+        x, d_in, ilog2(Li), ilog2(bi), si, s_x, gain, clip, w.x2, w.pmax, w.xa, w.ascale, w.asum,
+        codes_out, scale_out);
+    KQ_HIP(hipGetLastError());
+    quantize_a4_kernel<<<unsigned(batch * nss), 128, 0, s>>>(w.x2, w.pmax, int(nparts), d_in, nss, clip,
+                                                             w.xa, w.ascale, w.asum, codes_out, scale_out);
+    KQ_HIP(hipGetLastError());
+  }
+  constexpr int RK = 2;
+  const int nkr = int(cdiv(nss, RK));
+  int nw = std::min(nkr, 16);
+  while (nkr % nw) --nw;
+  const int rpw = cdiv(d_out, 32) >= 256 ? 32 : 16;
+  const int64_t rw = packed_row_words(d_in, 2);
+  KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED_A4, 0, s));
+  for (int64_t t = 0; t < cdiv(batch, A4_TILE); ++t) {
+    const int nvec = int(std::min<int64_t>(A4_TILE, batch - t * A4_TILE));
+    qmatvec_a4_kernel<RK><<<unsigned(cdiv(d_out, rpw)), 64 * nw, 0, s>>>(
+        packed, int(rw), scale, zero, w.xa, w.ascale, w.asum, nss, d_out, nkr, rpw, int(t), nvec, y1);
+    KQ_HIP(hipGetLastError());
+  }
+  KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED_A4, 1, s));
   const int64_t Lo = transform_len(d_out, bo);
   const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));
   transform_out_kernel<<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(

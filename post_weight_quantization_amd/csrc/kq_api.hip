@@ -32,11 +32,12 @@ void clear_error() { g_err[0] = 0; }
 
 namespace {
 // per op: events recorded around the op's main kernel
-thread_local hipEvent_t g_kernel_ev[8][2] = {};
+constexpr int N_OPS = 10;
+thread_local hipEvent_t g_kernel_ev[N_OPS][2] = {};
 }
 
 kq_status mark_kernel(kq_op op, int edge, hipStream_t s) {
-  if (op < 0 || op >= 8 || g_kernel_ev[op][edge] == nullptr) return KQ_OK;
+  if (op < 0 || op >= N_OPS || g_kernel_ev[op][edge] == nullptr) return KQ_OK;
   KQ_HIP(hipEventRecord(g_kernel_ev[op][edge], s));
   return KQ_OK;
 }
@@ -91,9 +92,10 @@ const char* kq_version(void) { return "kq 0.1 gfx950"; }
 
 kq_status kq_set_kernel_events(kq_op op, hipEvent_t start, hipEvent_t stop) {
   clear_error();
-  if (op != KQ_OP_ACCUMULATE_COV && op != KQ_OP_APPLY_QUANTIZED)
+  if (op != KQ_OP_ACCUMULATE_COV && op != KQ_OP_APPLY_QUANTIZED && op != KQ_OP_APPLY_QUANTIZED_A4)
     return fail(KQ_ERR_UNSUPPORTED,
-                "set_kernel_events: only KQ_OP_ACCUMULATE_COV and KQ_OP_APPLY_QUANTIZED have a timed kernel");
+                "set_kernel_events: only KQ_OP_ACCUMULATE_COV and the two KQ_OP_APPLY_QUANTIZED ops have a "
+                "timed kernel");
   if ((start == nullptr) != (stop == nullptr))
     return fail(KQ_ERR_ARG, "set_kernel_events: pass both events or neither");
   g_kernel_ev[op][0] = start;
@@ -149,6 +151,10 @@ kq_status kq_workspace_size(kq_op op, int64_t d_out, int64_t d_in, int64_t n_tok
     case KQ_OP_YAQA_QUANTIZE:
       if (d_out < 1 || d_in < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
       *bytes = yaqa_ws_bytes(d_out, d_in, true);
+      return KQ_OK;
+    case KQ_OP_APPLY_QUANTIZED_A4:
+      if (d_out < 1 || n_tok < 1) return fail(KQ_ERR_SHAPE, "workspace_size: bad sizes");
+      *bytes = apply_a4_ws_bytes(d_out, d_in, n_tok);
       return KQ_OK;
   }
   return fail(KQ_ERR_ARG, "workspace_size: unknown op %d", int(op));
@@ -387,6 +393,36 @@ kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* 
   Arena ar{static_cast<char*>(ws), ws_bytes, 0};
   return apply_run(packed, bits, scale, zero, group, s_x, s_g, sign_in, sign_out, bi, bo, x, batch,
                    d_out, d_in, y, ar, stream);
+}
+
+kq_status kq_apply_quantized_a4(const uint32_t* packed, const float* scale, const float* zero,
+                                const float* s_x, const float* s_g, const int8_t* sign_in,
+                                const int8_t* sign_out, int64_t blk_in, int64_t blk_out,
+                                const float* x, int64_t batch, int64_t d_out, int64_t d_in,
+                                float clip, float* y, int8_t* act_codes, float* act_scale,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (!packed || !scale || !zero || !s_x || !s_g || !sign_in || !sign_out || !x || !y)
+    return fail(KQ_ERR_ARG, "apply_quantized_a4: NULL argument");
+  if (!(clip > 0.f && clip <= 1.f))
+    return fail(KQ_ERR_ARG, "apply_quantized_a4: clip must be in (0, 1]");
+  if (d_out < 4 || d_out % 4 || batch < 1)
+    return fail(KQ_ERR_SHAPE, "apply_quantized_a4: d_out must be a multiple of 4 and batch >= 1");
+  if (d_in < 512 || d_in % 512)
+    return fail(KQ_ERR_SHAPE, "apply_quantized_a4: d_in must be a multiple of 512");
+  if (d_in > (int64_t(1) << 24))
+    return fail(KQ_ERR_SHAPE, "apply_quantized_a4: d_in above 2^24");
+  int64_t bi = 0, bo = 0;
+  KQ_TRY(resolve_block(d_in, blk_in, &bi, "input"));
+  KQ_TRY(resolve_block(d_out, blk_out, &bo, "output"));
+  const void* ptrs[5] = {packed, x, y, s_x, act_codes};
+  for (const void* p : ptrs)
+    if (!aligned16(p))
+      return fail(KQ_ERR_ARG, "apply_quantized_a4: packed, x, y, s_x, act_codes must be 16-byte aligned");
+  KQ_TRY(check_ws(ws, ws_bytes, apply_a4_ws_bytes(d_out, d_in, batch), "apply_quantized_a4"));
+  Arena ar{static_cast<char*>(ws), ws_bytes, 0};
+  return apply_a4_run(packed, scale, zero, s_x, s_g, sign_in, sign_out, bi, bo, x, batch, d_out, d_in,
+                      clip, y, act_codes, act_scale, ar, stream);
 }
 
 }  // extern "C"

@@ -149,6 +149,12 @@ kq_status objective_run(const float* W0, const float* What, const float* HX, con
 int64_t packed_row_words(int64_t d_in, int bits);
 kq_status pack_run(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, uint32_t* packed,
                    hipStream_t s);
+size_t apply_a4_ws_bytes(int64_t d_out, int64_t d_in, int64_t batch);
+kq_status apply_a4_run(const uint32_t* packed, const float* scale, const float* zero,
+                       const float* s_x, const float* s_g, const int8_t* si, const int8_t* so,
+                       int64_t bi, int64_t bo, const float* x, int64_t batch, int64_t d_out,
+                       int64_t d_in, float clip, float* y, int8_t* codes_out, float* scale_out,
+                       Arena& ws, hipStream_t s);
 size_t apply_ws_bytes(int64_t d_out, int64_t d_in, int64_t batch);
 kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const float* zero,
                     int group, const float* s_x, const float* s_g, const int8_t* si,

@@ -142,3 +142,36 @@ def test_yaqa_validation():
     st, msg = _err(N.lib.kq_yaqa_quantize(fake, fake, fake, fake, 100, 200, ctypes.byref(cfg), fake,
                                           fake, fake, fake, need.value - 1, None))
     assert st == N.KQ_ERR_WORKSPACE
+
+
+def test_apply_a4_validation():
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+    f = N.lib.kq_apply_quantized_a4
+
+    def call(packed=fake, x=fake, batch=2, d_out=64, d_in=1024, clip=1.0, codes=None, ws_bytes=1 << 30,
+             blk_in=0):
+        return _err(f(packed, fake, fake, fake, fake, fake, fake, blk_in, 0, x, batch, d_out, d_in, clip,
+                      fake, codes, None, fake, ws_bytes, None))
+
+    st, msg = call(packed=None)
+    assert st == N.KQ_ERR_ARG and "NULL" in msg
+    for clip in (0.0, -0.5, 1.5, float("nan")):
+        st, msg = call(clip=clip)
+        assert st == N.KQ_ERR_ARG and "clip" in msg
+    st, _ = call(d_in=1000)
+    assert st == N.KQ_ERR_SHAPE
+    st, _ = call(d_out=66)
+    assert st == N.KQ_ERR_SHAPE
+    st, _ = call(batch=0)
+    assert st == N.KQ_ERR_SHAPE
+    st, _ = call(blk_in=3)
+    assert st == N.KQ_ERR_SHAPE
+    st, msg = call(codes=ctypes.c_void_p(0x10004))
+    assert st == N.KQ_ERR_ARG and "aligned" in msg
+    need = ctypes.c_size_t()
+    assert N.lib.kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED_A4, 64, 1024, 20, 0, None,
+                                   ctypes.byref(need)) == 0
+    # x2 and y1 in fp32, one byte per input value in two 16-vector tiles
+    assert need.value >= 4 * 20 * 1024 + 4 * 20 * 64 + 32 * 1024
+    st, _ = call(batch=20, ws_bytes=need.value - 1)
+    assert st == N.KQ_ERR_WORKSPACE
