@@ -237,9 +237,30 @@ def run_streaming(spec, X, Xq, G, HX, D, HG, ws, chunk=16384, reps=3):
             "chunked_mtok_s": round(n / res[chunk] / 1e3, 2)}
 
 
+_SPIN = {}
+
+
+def hold_gpu(ms=0.5):
+    """Enqueue a spin kernel of about `ms` milliseconds on the current stream,
+    so that the host queues the call that follows before the GPU reaches it:
+    its events then time the GPU's work, not the host's launches."""
+    import torch
+
+    if "per_ms" not in _SPIN:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN["per_ms"] = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(ms * _SPIN["per_ms"]))
+
+
 def time_apply(packed, bits, scale, zero, group, s_x, s_g, si, so, d_out, d_in, batch, reps=20):
     """Mean time of one kq_apply_quantized call and of its product kernel (event
-    hook), over `reps` calls after warm-up; inputs resident on the device."""
+    hook), over `reps` calls after warm-up; inputs resident on the device, the
+    calls queued ahead of the GPU (hold_gpu)."""
     import torch
 
     import post_weight_quantization_amd as kq
@@ -257,11 +278,45 @@ def time_apply(packed, bits, scale, zero, group, s_x, s_g, si, so, d_out, d_in, 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
     torch.cuda.synchronize()
     for k in range(reps):
+        hold_gpu()
         ev[k][0].record(stream)
         kq.kq_set_kernel_events(N.KQ_OP_APPLY_QUANTIZED, ev[k][1], ev[k][2], stream)
         call()
         ev[k][3].record(stream)
     kq.kq_set_kernel_events(N.KQ_OP_APPLY_QUANTIZED)
+    torch.cuda.synchronize()
+    call_us = float(np.mean([e[0].elapsed_time(e[3]) for e in ev])) * 1e3
+    kern_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    return call_us, kern_us
+
+
+def time_apply_a4(packed, scale, zero, s_x, s_g, si, so, d_out, d_in, batch, clip=0.9, reps=20):
+    """Mean time of one kq_apply_quantized_a4 call and of its product launches
+    (event hook: every 16-vector launch of the call), inputs resident, the
+    calls queued ahead of the GPU (hold_gpu)."""
+    import torch
+
+    import post_weight_quantization_amd as kq
+    from post_weight_quantization_amd import _native as N
+
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(batch)
+    x = torch.randn(batch, d_in, device="cuda", generator=g)
+    y = torch.empty(batch, d_out, device="cuda")
+    ws = torch.empty(kq.kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED_A4, d_out, d_in, batch),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: kq.kq_apply_quantized_a4(packed, scale, zero, s_x, s_g, si, so, x, clip, y=y, ws=ws)
+    for _ in range(3):
+        call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for k in range(reps):
+        hold_gpu()
+        ev[k][0].record(stream)
+        kq.kq_set_kernel_events(N.KQ_OP_APPLY_QUANTIZED_A4, ev[k][1], ev[k][2], stream)
+        call()
+        ev[k][3].record(stream)
+    kq.kq_set_kernel_events(N.KQ_OP_APPLY_QUANTIZED_A4)
     torch.cuda.synchronize()
     call_us = float(np.mean([e[0].elapsed_time(e[3]) for e in ev])) * 1e3
     kern_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
@@ -299,6 +354,20 @@ def run_inference(spec, codes, scale, zero, s_x, s_g, si, so):
             rec[f"b{batch}"] = {"call_us": round(call_us, 2), "product_us": round(kern_us, 2),
                                 "product_gbs": round(nbytes / kern_us / 1e3, 1),
                                 "product_hbm_frac": round(nbytes / kern_us / 1e3 / (PEAK_HBM / 1e9), 4)}
+        if bits == 2 and group == 0 and d_in % 512 == 0:
+            # 4-bit activations: one product launch for the batch, the codes
+            # and grids read once; per vector its d_in code bytes read and
+            # its d_out fp32 outputs written
+            a4 = {}
+            for batch in (1, 16, 64, 256):
+                call_us, kern_us = time_apply_a4(packed, sc.reshape(-1), zr.reshape(-1), sx, sg, sgi, sgo,
+                                                 d_out, d_in, batch)
+                nbytes = packed.numel() * 4 + 8 * d_out + batch * (d_in + 4 * d_out)
+                a4[f"b{batch}"] = {"call_us": round(call_us, 2), "product_us": round(kern_us, 2),
+                                   "product_gbs": round(nbytes / kern_us / 1e3, 1),
+                                   "product_hbm_frac": round(nbytes / kern_us / 1e3 / (PEAK_HBM / 1e9), 4),
+                                   "tops": round(2 * d_out * d_in * batch / kern_us / 1e6, 2)}
+            rec["a4"] = a4
         out[name] = rec
     return out
 

@@ -98,8 +98,9 @@ const char* kq_version(void);
  *          KQ_OP_APPLY_QUANTIZED: the product with the packed codes (one
  *          launch per 4 vectors of the batch; the two transforms lie
  *          outside the bracket).
- *          KQ_OP_APPLY_QUANTIZED_A4: the integer product (one launch per 16
- *          vectors; the transforms and the input quantization lie outside).
+ *          KQ_OP_APPLY_QUANTIZED_A4: the integer product (one launch for
+ *          the whole batch; the transforms and the input quantization lie
+ *          outside).
  *   start, stop  events created by the caller (who owns and destroys them);
  *          both NULL switches the hook off.
  * Errors: KQ_ERR_UNSUPPORTED for other ops, KQ_ERR_ARG if exactly one event

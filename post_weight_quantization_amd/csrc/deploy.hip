@@ -612,9 +612,11 @@ constexpr int MX_DIG = 6;          // digits per value
 constexpr int MX_BYTES = 4 * 4 * MX_DIG * 32;  // digit bytes per super-step and vector
 constexpr int MX_SCALES = 4 * MX_DIG;          // scale words per super-step and vector
 
-// e4m3 encodings of the integers -8 .. 7 (index n + 8)
-__device__ __constant__ uint8_t kE4M3Int[16] = {0xD0, 0xCE, 0xCC, 0xCA, 0xC8, 0xC4, 0xC0, 0xB8,
-                                                0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E};
+// e4m3 encoding of an integer n in [-16, 16] (exact: 3 mantissa bits), by
+// the hardware conversion
+__device__ inline uint8_t e4m3_int(int n) {
+  return uint8_t(__builtin_amdgcn_cvt_pk_fp8_f32(float(n), 0.f, 0, false) & 0xFF);
+}
 
 // x2 = gain * H_blk (x[b] sign_in / s_x) over L columns, written as B digits
 // xb[b][S][q][g][l][32 bytes], scale words xs[b][S][G][l] (byte q) and the
@@ -668,7 +670,7 @@ __global__ __launch_bounds__(1024) void transform_in_mx_kernel(
     for (int l = 0; l < MX_DIG; ++l) {
       const int n = ((r + 8) & 15) - 8;  // balanced base-16 digit
       r = (r - n) >> 4;
-      dig[(((S * 4 + q) * 4 + g) * MX_DIG + l) * 32 + jb] = kE4M3Int[n + 8];
+      dig[(((S * 4 + q) * 4 + g) * MX_DIG + l) * 32 + jb] = e4m3_int(n);
     }
     if ((e & 31) == 0) {
 #pragma unroll
@@ -894,10 +896,10 @@ __device__ inline float block_max(float m, float* part) {
 __device__ inline int a4_put4(float4 v, float s, int e, uint8_t* stg, int8_t* codes_out) {
   const int c0 = a4_code(v.x, s), c1 = a4_code(v.y, s), c2 = a4_code(v.z, s), c3 = a4_code(v.w, s);
   const int base = e & ~(MX_SS - 1), u = e & (MX_SS - 1);
-  stg[base + a4_slot(u)] = kE4M3Int[c0 + 8];
-  stg[base + a4_slot(u + 1)] = kE4M3Int[c1 + 8];
-  stg[base + a4_slot(u + 2)] = kE4M3Int[c2 + 8];
-  stg[base + a4_slot(u + 3)] = kE4M3Int[c3 + 8];
+  stg[base + a4_slot(u)] = e4m3_int(c0);
+  stg[base + a4_slot(u + 1)] = e4m3_int(c1);
+  stg[base + a4_slot(u + 2)] = e4m3_int(c2);
+  stg[base + a4_slot(u + 3)] = e4m3_int(c3);
   if (codes_out)
     *reinterpret_cast<char4*>(codes_out + e) = make_char4(char(c0), char(c1), char(c2), char(c3));
   return c0 + c1 + c2 + c3;
@@ -916,8 +918,9 @@ __device__ inline void a4_store(const uint8_t* stg, int nS, int64_t b, int64_t S
 }
 
 // x2 = gain * H_blk (x[b] sign_in / s_x) over L columns. FUSED (the chunk is
-// the whole vector): quantize it here. Otherwise write x2 and the chunk's
-// largest magnitude for quantize_a4_kernel.
+// the whole vector): quantize it here, with the vector's code sum in
+// asum[b]. Otherwise write x2 and the chunk's largest magnitude for
+// quantize_a4_kernel.
 template <bool FUSED>
 __global__ __launch_bounds__(1024) void transform_in_a4_kernel(
     const float* __restrict__ x, int64_t d_in, int lgL, int lgb, const int8_t* __restrict__ si,
@@ -953,10 +956,7 @@ __global__ __launch_bounds__(1024) void transform_in_a4_kernel(
   }
   mx = block_max(mx, part);
   if constexpr (!FUSED) {
-    if (threadIdx.x == 0) {
-      pmax[blockIdx.x] = mx;
-      if (c0 == 0) asum[b] = 0;
-    }
+    if (threadIdx.x == 0) pmax[blockIdx.x] = mx;
   } else {
     const float sc = (clip * mx) / A4_QMAX;
     int8_t* co = codes_out ? codes_out + b * d_in : nullptr;
@@ -982,7 +982,8 @@ __global__ __launch_bounds__(1024) void transform_in_a4_kernel(
 }
 
 // One workgroup of 128 threads per (vector, super-step): the vector's scale
-// from its chunk maxima, then its 512 values quantized and placed.
+// from its chunk maxima, then its 512 values quantized and placed; the sum
+// of their codes goes to asum[b][S].
 __global__ __launch_bounds__(128) void quantize_a4_kernel(
     const float* __restrict__ x2, const float* __restrict__ pmax, int nparts, int64_t d_in,
     int64_t nss, float clip, uint8_t* __restrict__ xa, float* __restrict__ ascale,
@@ -1002,7 +1003,7 @@ __global__ __launch_bounds__(128) void quantize_a4_kernel(
   __syncthreads();
   a4_store(stg, 1, b, S, nss, xa);
   if (threadIdx.x == 0) {
-    atomicAdd(asum + b, ipart[0] + ipart[1]);  // integer: the order does not matter
+    asum[b * nss + S] = ipart[0] + ipart[1];
     if (S == 0) {
       ascale[b] = sc;
       if (scale_out) scale_out[b] = sc;
@@ -1011,22 +1012,34 @@ __global__ __launch_bounds__(128) void quantize_a4_kernel(
 }
 
 // y1[16 tile + v][rows] = scale (s_v (sum_k q_k a_vk - zero sum_k a_vk)) for
-// v < nvec and rows blockIdx.x * rpw .. + rpw - 1 (rpw <= 32). K ranges of RK
-// super-steps; wave w takes ranges w, w + waves, ... and holds a range's B
-// operands (all 16 vectors) in registers while it streams the rows.
+// the tile's vectors v and the rows rb * rpw .. + rpw - 1 (rpw a multiple of
+// 16) of row block rb; the waves' partial sums meet in LDS (red, nw x rpw x
+// 16 floats, sized at launch). Workgroup b runs on XCD b % 8 and takes, in the order that XCD
+// receives them, every vector tile of one row block after another: the
+// tiles of a row block run together on one XCD and read its codes from HBM
+// once, through that XCD's L2. K ranges of RK super-steps; wave w takes
+// ranges w, w + waves, ... and holds a range's B operands (all 16 vectors)
+// in registers while it streams the rows.
 template <int RK>
 __global__ __launch_bounds__(1024) void qmatvec_a4_kernel(
     const uint32_t* __restrict__ packed, int rw, const float* __restrict__ scale,
     const float* __restrict__ zero, const uint8_t* __restrict__ xa, const float* __restrict__ ascale,
-    const int* __restrict__ asum, int64_t nss, int64_t d_out, int nkr, int rpw, int tile, int nvec,
-    float* __restrict__ y1) {
-  __shared__ float red[16][32 * A4_TILE];
+    const int* __restrict__ asum, int nsum, int64_t nss, int64_t d_out, int nkr, int rpw, int ntiles,
+    int64_t batch, float* __restrict__ y1) {
+  extern __shared__ float red[];
+  __shared__ int vpart[1024];
+  __shared__ float vsum[A4_TILE];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  const int64_t rbeg = int64_t(blockIdx.x) * rpw;
+  const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
+  const int tile = seq % ntiles;
+  const int64_t rbeg = (int64_t(seq / ntiles) * 8 + xcd) * rpw;
+  if (rbeg >= d_out) return;  // the grid is rounded up to whole rounds of 8
+  const int nvec = int(min(int64_t(A4_TILE), batch - int64_t(tile) * A4_TILE));
   const int nrows = int(min(int64_t(rpw), d_out - rbeg));
-  for (int i = lane; i < 32 * A4_TILE; i += 64) red[w][i] = 0.f;
+  float* redw = red + w * rpw * A4_TILE;
+  for (int i = lane; i < rpw * A4_TILE; i += 64) redw[i] = 0.f;
   const int n = lane & 15, G = lane >> 4;
   const bool bcol = n < nvec;
   const int ntile = (nrows + 15) / 16;
@@ -1045,6 +1058,11 @@ __global__ __launch_bounds__(1024) void qmatvec_a4_kernel(
   v8i_t bop[RK][4];
   uint4 an[RK][2];
   load_a(0, an);
+  // sum_k a_k of each vector from its nsum partial sums: each thread loads
+  // one now, to be added up after the rows (integers: any order)
+  const int64_t vbase = int64_t(tile) * A4_TILE * nsum;
+  const int npart = nvec * nsum;
+  const int pre = int(threadIdx.x) < npart ? asum[vbase + threadIdx.x] : 0;
   int cur_kr = -1;
   for (int it = 0; it < items; ++it) {
     const int kr = w + (it / ntile) * nw, t0 = (it % ntile) * 16;
@@ -1091,16 +1109,26 @@ __global__ __launch_bounds__(1024) void qmatvec_a4_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = t0 + 4 * G + i;
-      if (bcol && r < nrows) red[w][r * A4_TILE + n] += acc[i];
+      if (bcol && r < nrows) redw[r * A4_TILE + n] += acc[i];
     }
+  }
+  vpart[threadIdx.x] = pre;
+  __syncthreads();
+  if (int(threadIdx.x) < nvec) {
+    int t = 0;
+    for (int k = 0; k < nsum; ++k) {
+      const int i = int(threadIdx.x) * nsum + k;
+      t += i < int(blockDim.x) ? vpart[i] : asum[vbase + i];
+    }
+    vsum[threadIdx.x] = float(t);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nrows * nvec; i += blockDim.x) {
     const int r = i / nvec, v = i % nvec;
     float acc = 0.f;
-    for (int u = 0; u < nw; ++u) acc += red[u][r * A4_TILE + v];
+    for (int u = 0; u < nw; ++u) acc += red[(u * rpw + r) * A4_TILE + v];
     const int64_t row = rbeg + r, vec = int64_t(tile) * A4_TILE + v;
-    y1[vec * d_out + row] = scale[row] * (ascale[vec] * (acc - zero[row] * float(asum[vec])));
+    y1[vec * d_out + row] = scale[row] * (ascale[vec] * (acc - zero[row] * vsum[v]));
   }
 }
 
@@ -1120,7 +1148,7 @@ A4Ws a4_take(Arena& ar, int64_t d_in, int64_t batch) {
   w.pmax = ar.take<float>(size_t(batch) * (d_in / MX_SS));
   w.xa = ar.take<uint8_t>(size_t(cdiv(batch, A4_TILE)) * (d_in / MX_SS) * A4_SSB);
   w.ascale = ar.take<float>(size_t(batch));
-  w.asum = ar.take<int>(size_t(batch));
+  w.asum = ar.take<int>(size_t(batch) * (d_in / MX_SS));  // code sums: per vector, or per super-step
   return w;
 }
 
@@ -1231,15 +1259,22 @@ kq_status apply_a4_run(const uint32_t* packed, const float* scale, const float* 
   const int nkr = int(cdiv(nss, RK));
   int nw = std::min(nkr, 16);
   while (nkr % nw) --nw;
-  const int rpw = cdiv(d_out, 32) >= 256 ? 32 : 16;
   const int64_t rw = packed_row_words(d_in, 2);
+  const int64_t ntiles = cdiv(batch, A4_TILE);
+  // rows per workgroup: 32 (16 if that leaves < 256 workgroups); with several
+  // vector tiles, up to 128 while >= 512 workgroups remain, so that each
+  // workgroup's B operands serve more rows
+  int rpw = cdiv(d_out, 32) >= 256 ? 32 : 16;
+  while (rpw < 128 && cdiv(d_out, 2 * rpw) * ntiles >= 512) rpw *= 2;
+  const int64_t nrb = cdiv(d_out, rpw);
+  const size_t red_bytes = size_t(nw) * rpw * A4_TILE * sizeof(float);  // <= 128 KB
+  KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(qmatvec_a4_kernel<RK>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(red_bytes)));
   KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED_A4, 0, s));
-  for (int64_t t = 0; t < cdiv(batch, A4_TILE); ++t) {
-    const int nvec = int(std::min<int64_t>(A4_TILE, batch - t * A4_TILE));
-    qmatvec_a4_kernel<RK><<<unsigned(cdiv(d_out, rpw)), 64 * nw, 0, s>>>(
-        packed, int(rw), scale, zero, w.xa, w.ascale, w.asum, nss, d_out, nkr, rpw, int(t), nvec, y1);
-    KQ_HIP(hipGetLastError());
-  }
+  qmatvec_a4_kernel<RK><<<unsigned(8 * cdiv(nrb, 8) * ntiles), 64 * nw, red_bytes, s>>>(
+      packed, int(rw), scale, zero, w.xa, w.ascale, w.asum, nparts == 1 ? 1 : int(nss), nss, d_out, nkr,
+      rpw, int(ntiles), batch, y1);
+  KQ_HIP(hipGetLastError());
   KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED_A4, 1, s));
   const int64_t Lo = transform_len(d_out, bo);
   const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));

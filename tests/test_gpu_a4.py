@@ -71,10 +71,12 @@ def _check(codes, scale, zero, s_x, s_g, si, so, x, clip=1.0, bi=0, bo=0):
 
 # one super-step; a ragged K range (3 super-steps); a vector split over
 # transform chunks (unfused quantization); a whole 8192 vector in one chunk;
-# batches of 1, 16 (one full tile), 17 and 40 (a partial tile)
+# batches of 1, 16 (one full tile), 17 and 40 (a partial tile); many tiles,
+# where a workgroup takes 128 rows (the last row block ragged at 2100)
 @pytest.mark.parametrize("d_out,d_in,batch,bi,bo,clip", [
     (256, 512, 1, 0, 0, 1.0), (260, 1536, 17, 512, 0, 0.9), (128, 4096, 16, 0, 0, 1.0),
-    (64, 12288, 5, 4096, 32, 0.8), (96, 8192, 40, 0, 0, 1.0), (512, 2048, 3, 256, 128, 1.0)])
+    (64, 12288, 5, 4096, 32, 0.8), (96, 8192, 40, 0, 0, 1.0), (512, 2048, 3, 256, 128, 1.0),
+    (4096, 1024, 256, 256, 0, 0.9), (2100, 1024, 600, 0, 0, 1.0)])
 def test_a4_against_oracle(d_out, d_in, batch, bi, bo, clip):
     rng = np.random.default_rng(d_out + d_in + batch)
     c = _case(d_out, d_in, rng)
