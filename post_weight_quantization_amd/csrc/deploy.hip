@@ -1132,6 +1132,160 @@ __global__ __launch_bounds__(1024) void qmatvec_a4_kernel(
   }
 }
 
+// Larger batches: a matrix-core GEMM. A workgroup of 4 waves owns 256 rows x
+// 32 vectors (two vector tiles). Wave w streams the codes of its 64 rows
+// (four 16-row tiles) straight into registers; the B operands of the two
+// tiles pass through LDS one 512-column super-step at a time, double
+// buffered, in a layout where each lane's 32 bytes are two 16-byte halves
+// 1 KB apart (conflict-free 16-byte reads). Loads run two super-steps ahead. Each wave's 4 x 2 tile grid
+// reuses every fragment: 32 MFMAs per super-step per wave, one barrier.
+// Workgroups are grouped by XCD as in qmatvec_a4_kernel.
+constexpr int QG_ROWS = 256, QG_RT = 4, QG_VT = 2;
+constexpr int QG_STAGE = QG_VT * A4_SSB;  // 16 KB of B per super-step
+constexpr int QG_PRE = 8;                 // code-sum partials each thread preloads
+
+__global__ __launch_bounds__(256) void qgemm_a4_kernel(
+    const uint32_t* __restrict__ packed, int rw, const float* __restrict__ scale,
+    const float* __restrict__ zero, const uint8_t* __restrict__ xa, const float* __restrict__ ascale,
+    const int* __restrict__ asum, int nsum, int64_t nss, int64_t d_out, int64_t batch, int nvb,
+    float* __restrict__ y1) {
+  __shared__ __align__(16) uint8_t bs[2][QG_STAGE];
+  __shared__ int vsum[QG_VT * A4_TILE];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
+  const int vb = seq % nvb;
+  const int64_t rbeg = (int64_t(seq / nvb) * 8 + xcd) * QG_ROWS;
+  if (rbeg >= d_out) return;  // the grid is rounded up to whole rounds of 8
+  const int64_t ntiles = (batch + A4_TILE - 1) / A4_TILE;
+  const int64_t v0 = int64_t(vb) * (QG_VT * A4_TILE);
+  const int nv = int(min(int64_t(QG_VT * A4_TILE), batch - v0));
+  const int n = lane & 15, G = lane >> 4;
+
+  // code sums of this block's vectors: partials loaded now, added at the end
+  const int npart = nv * nsum;
+  int pre[QG_PRE];
+#pragma unroll
+  for (int k = 0; k < QG_PRE; ++k) {
+    const int i = t + 256 * k;
+    pre[k] = i < npart ? asum[v0 * nsum + i] : 0;
+  }
+  if (t < QG_VT * A4_TILE) vsum[t] = 0;
+
+  auto load_a = [&](int64_t S, uint4 (&dst)[QG_RT][2]) {
+#pragma unroll
+    for (int rt = 0; rt < QG_RT; ++rt) {
+      const int64_t row = min(rbeg + 64 * w + 16 * rt + n, d_out - 1);  // past the end: not stored
+      const uint4* ap = reinterpret_cast<const uint4*>(packed + row * rw + S * (MX_SS / 16) + G * 4);
+      dst[rt][0] = ap[0];
+      dst[rt][1] = ap[4];
+    }
+  };
+  // thread t moves 16-byte chunks c = 4 t + k of the stage; chunk c is
+  // vector tile vt = c / 512, step q, lane l, half h of the tile's 8 KB
+  // (c % 512 = 128 q + 2 l + h); absent tiles are zeros
+  auto load_b = [&](int64_t S, uint4 (&dst)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 4 * t + k;
+      const int64_t T = 2 * int64_t(vb) + (c >> 9);
+      dst[k] = T < ntiles ? *reinterpret_cast<const uint4*>(xa + (T * nss + S) * A4_SSB + (c & 511) * 16)
+                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_b = [&](int buf, const uint4 (&src)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 4 * t + k, u = c & 511;
+      const int q = u >> 7, l = (u >> 1) & 63, h = u & 1;
+      *reinterpret_cast<uint4*>(&bs[buf][(c >> 9) * A4_SSB + q * 2048 + h * 1024 + l * 16]) = src[k];
+    }
+  };
+
+  v4f_t acc[QG_RT][QG_VT];
+#pragma unroll
+  for (int rt = 0; rt < QG_RT; ++rt)
+#pragma unroll
+    for (int vt = 0; vt < QG_VT; ++vt) acc[rt][vt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+  // loads run two super-steps ahead: a1, b1 for S + 1 and a2, b2 for S + 2
+  uint4 a1[QG_RT][2], a2[QG_RT][2], b1[4], b2[4];
+  load_b(0, b1);
+  load_a(0, a1);
+  if (nss > 1) {
+    load_b(1, b2);
+    load_a(1, a2);
+  }
+  store_b(0, b1);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b1[k] = b2[k];
+  for (int64_t S = 0; S < nss; ++S) {
+    const int buf = int(S & 1);
+    uint4 ac[QG_RT][2];
+#pragma unroll
+    for (int rt = 0; rt < QG_RT; ++rt) {
+      ac[rt][0] = a1[rt][0];
+      ac[rt][1] = a1[rt][1];
+      a1[rt][0] = a2[rt][0];
+      a1[rt][1] = a2[rt][1];
+    }
+    if (S + 2 < nss) {
+      load_a(S + 2, a2);
+      load_b(S + 2, b2);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v8i_t b[QG_VT];
+#pragma unroll
+      for (int vt = 0; vt < QG_VT; ++vt) {
+        const uint8_t* p = &bs[buf][vt * A4_SSB + q * 2048 + lane * 16];
+        const uint4 lo = *reinterpret_cast<const uint4*>(p);
+        const uint4 hi = *reinterpret_cast<const uint4*>(p + 1024);
+        b[vt] = v8i_t{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      }
+#pragma unroll
+      for (int rt = 0; rt < QG_RT; ++rt) {
+        const uint32_t wd[8] = {ac[rt][0].x, ac[rt][0].y, ac[rt][0].z, ac[rt][0].w,
+                                ac[rt][1].x, ac[rt][1].y, ac[rt][1].z, ac[rt][1].w};
+        const uint32_t x0 = wd[2 * q], x1 = wd[2 * q + 1];
+        const v8i_t aop = {int(x0 & 0x33333333u), int((x0 >> 2) & 0x33333333u),
+                           int(x1 & 0x33333333u), int((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+#pragma unroll
+        for (int vt = 0; vt < QG_VT; ++vt)
+          acc[rt][vt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, b[vt], acc[rt][vt], 4, 0, 0,
+                                                                         0x7f7f7f7f, 0, int(0x80808080u));
+      }
+    }
+    if (S + 1 < nss) store_b(buf ^ 1, b1);  // that buffer's last reads were before the previous barrier
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b1[k] = b2[k];
+  }
+#pragma unroll
+  for (int k = 0; k < QG_PRE; ++k)
+    if (t + 256 * k < npart) atomicAdd(&vsum[(t + 256 * k) / nsum], pre[k]);
+  for (int i = t + 256 * QG_PRE; i < npart; i += 256) atomicAdd(&vsum[i / nsum], asum[v0 * nsum + i]);
+  __syncthreads();
+  // acc[rt][vt][i] = C[16 rt + 4 G + i][16 vt + n] of the wave's 64 rows
+#pragma unroll
+  for (int rt = 0; rt < QG_RT; ++rt) {
+    const int64_t row0 = rbeg + 64 * w + 16 * rt + 4 * G;
+    if (row0 >= d_out) continue;  // d_out % 4 == 0: rows row0 .. row0 + 3 all exist
+    const float4 sc = make_float4(scale[row0], scale[row0 + 1], scale[row0 + 2], scale[row0 + 3]);
+    const float4 zr = make_float4(zero[row0], zero[row0 + 1], zero[row0 + 2], zero[row0 + 3]);
+#pragma unroll
+    for (int vt = 0; vt < QG_VT; ++vt) {
+      const int v = 16 * vt + n;
+      if (v >= nv) continue;
+      const float s = ascale[v0 + v], vs = float(vsum[v]);
+      const v4f_t a = acc[rt][vt];
+      *reinterpret_cast<float4*>(y1 + (v0 + v) * d_out + row0) =
+          make_float4(sc.x * (s * (a[0] - zr.x * vs)), sc.y * (s * (a[1] - zr.y * vs)),
+                      sc.z * (s * (a[2] - zr.z * vs)), sc.w * (s * (a[3] - zr.w * vs)));
+    }
+  }
+}
+
 struct A4Ws {
   float* x2;
   float* pmax;
@@ -1270,10 +1424,19 @@ kq_status apply_a4_run(const uint32_t* packed, const float* scale, const float* 
   const size_t red_bytes = size_t(nw) * rpw * A4_TILE * sizeof(float);  // <= 128 KB
   KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(qmatvec_a4_kernel<RK>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(red_bytes)));
+  const int nsum = nparts == 1 ? 1 : int(nss);
   KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED_A4, 0, s));
-  qmatvec_a4_kernel<RK><<<unsigned(8 * cdiv(nrb, 8) * ntiles), 64 * nw, red_bytes, s>>>(
-      packed, int(rw), scale, zero, w.xa, w.ascale, w.asum, nparts == 1 ? 1 : int(nss), nss, d_out, nkr,
-      rpw, int(ntiles), batch, y1);
+  // the GEMM when its grid gives every CU a workgroup; below that the
+  // K-split product keeps more loads in flight
+  const int64_t nvb = cdiv(batch, QG_VT * A4_TILE), nrbg = cdiv(d_out, QG_ROWS);
+  if (batch > A4_TILE && nvb * nrbg >= 256) {
+    qgemm_a4_kernel<<<unsigned(8 * cdiv(nrbg, 8) * nvb), 256, 0, s>>>(
+        packed, int(rw), scale, zero, w.xa, w.ascale, w.asum, nsum, nss, d_out, batch, int(nvb), y1);
+  } else {
+    qmatvec_a4_kernel<RK><<<unsigned(8 * cdiv(nrb, 8) * ntiles), 64 * nw, red_bytes, s>>>(
+        packed, int(rw), scale, zero, w.xa, w.ascale, w.asum, nsum, nss, d_out, nkr, rpw, int(ntiles), batch,
+        y1);
+  }
   KQ_HIP(hipGetLastError());
   KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED_A4, 1, s));
   const int64_t Lo = transform_len(d_out, bo);
