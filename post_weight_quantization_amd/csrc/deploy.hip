@@ -1133,23 +1133,44 @@ __global__ __launch_bounds__(1024) void qmatvec_a4_kernel(
 }
 
 // Larger batches: a matrix-core GEMM. A workgroup of 4 waves owns 256 rows x
-// 32 vectors (two vector tiles). Wave w streams the codes of its 64 rows
-// (four 16-row tiles) straight into registers; the B operands of the two
-// tiles pass through LDS one 512-column super-step at a time, double
-// buffered, in a layout where each lane's 32 bytes are two 16-byte halves
-// 1 KB apart (conflict-free 16-byte reads). Loads run two super-steps ahead. Each wave's 4 x 2 tile grid
-// reuses every fragment: 32 MFMAs per super-step per wave, one barrier.
-// Workgroups are grouped by XCD as in qmatvec_a4_kernel.
+// 32 vectors (two vector tiles) and streams both operands through a ring of
+// three LDS stages, one 512-column super-step each, with
+// global_load_lds_dwordx4 (LDS DMA: lane l's 16 bytes land at the
+// instruction's base + 16 l). Layouts, one DMA instruction per 1 KB block:
+//   codes: block (w, rt, h) holds, for lane l = 16 G + n, the 16 bytes at
+//     64 h + 16 G of row 64 w + 16 rt + n's super-step: exactly the A
+//     operand half that lane reads, so each wave fills and reads only its own
+//     8 blocks and every read is one conflict-free 16-byte read;
+//   activations: block (vt, q, h) holds half h of lane l's 32 bytes of vector
+//     tile vt, step q.
+// Each wave's 4 x 2 grid of 16 x 16 tiles reuses every fragment: 32 MFMAs
+// per super-step, one barrier. Workgroups are grouped by XCD as in
+// qmatvec_a4_kernel.
 constexpr int QG_ROWS = 256, QG_RT = 4, QG_VT = 2;
-constexpr int QG_STAGE = QG_VT * A4_SSB;  // 16 KB of B per super-step
-constexpr int QG_PRE = 8;                 // code-sum partials each thread preloads
+constexpr int QG_ABYTES = QG_ROWS * (MX_SS / 4);    // 32 KB of codes per super-step
+constexpr int QG_STAGE = QG_ABYTES + QG_VT * A4_SSB; // plus 16 KB of activations
+constexpr int QG_NST = 3;                           // ring depth
+constexpr int QG_DMA = 12;                          // DMA instructions per wave and stage
+constexpr int QG_PRE = 8;                           // code-sum partials each thread preloads
+
+__device__ inline void a4_dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void a4_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
 
 __global__ __launch_bounds__(256) void qgemm_a4_kernel(
     const uint32_t* __restrict__ packed, int rw, const float* __restrict__ scale,
     const float* __restrict__ zero, const uint8_t* __restrict__ xa, const float* __restrict__ ascale,
     const int* __restrict__ asum, int nsum, int64_t nss, int64_t d_out, int64_t batch, int nvb,
     float* __restrict__ y1) {
-  __shared__ __align__(16) uint8_t bs[2][QG_STAGE];
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ int vsum[QG_VT * A4_TILE];
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -1161,6 +1182,7 @@ __global__ __launch_bounds__(256) void qgemm_a4_kernel(
   const int64_t v0 = int64_t(vb) * (QG_VT * A4_TILE);
   const int nv = int(min(int64_t(QG_VT * A4_TILE), batch - v0));
   const int n = lane & 15, G = lane >> 4;
+  const uint32_t ring_base = uint32_t(reinterpret_cast<uintptr_t>(ring));
 
   // code sums of this block's vectors: partials loaded now, added at the end
   const int npart = nv * nsum;
@@ -1172,34 +1194,33 @@ __global__ __launch_bounds__(256) void qgemm_a4_kernel(
   }
   if (t < QG_VT * A4_TILE) vsum[t] = 0;
 
-  auto load_a = [&](int64_t S, uint4 (&dst)[QG_RT][2]) {
+  // this lane's DMA sources at super-step 0: 8 code blocks (rt, h), then 4
+  // activation blocks (vt, q, h) = 4 w .. 4 w + 3 (absent tiles read tile 0:
+  // those columns are never stored)
+  const uint8_t* src[QG_DMA];
+  int64_t step[QG_DMA];
 #pragma unroll
-    for (int rt = 0; rt < QG_RT; ++rt) {
-      const int64_t row = min(rbeg + 64 * w + 16 * rt + n, d_out - 1);  // past the end: not stored
-      const uint4* ap = reinterpret_cast<const uint4*>(packed + row * rw + S * (MX_SS / 16) + G * 4);
-      dst[rt][0] = ap[0];
-      dst[rt][1] = ap[4];
-    }
+  for (int k = 0; k < 8; ++k) {
+    const int rt = k >> 1, h = k & 1;
+    const int64_t row = min(rbeg + 64 * w + 16 * rt + n, d_out - 1);  // past the end: not stored
+    src[k] = reinterpret_cast<const uint8_t*>(packed + row * rw) + 64 * h + 16 * G;
+    step[k] = MX_SS / 4;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int blk = 4 * w + k, vt = blk >> 3, q = (blk >> 1) & 3, h = blk & 1;
+    const int64_t T = 2 * int64_t(vb) + vt;
+    src[8 + k] = xa + (T < ntiles ? T : 0) * nss * A4_SSB + (q * 64 + lane) * 32 + 16 * h;
+    step[8 + k] = A4_SSB;
+  }
+  auto lds_block = [&](int k) {  // LDS byte offset of this wave's DMA block k within a stage
+    if (k < 8) return (w * 8 + k) * 1024;
+    return QG_ABYTES + (4 * w + (k - 8)) * 1024;
   };
-  // thread t moves 16-byte chunks c = 4 t + k of the stage; chunk c is
-  // vector tile vt = c / 512, step q, lane l, half h of the tile's 8 KB
-  // (c % 512 = 128 q + 2 l + h); absent tiles are zeros
-  auto load_b = [&](int64_t S, uint4 (&dst)[4]) {
+  auto issue = [&](int64_t S) {
+    const uint32_t sb = ring_base + uint32_t((S % QG_NST) * QG_STAGE);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = 4 * t + k;
-      const int64_t T = 2 * int64_t(vb) + (c >> 9);
-      dst[k] = T < ntiles ? *reinterpret_cast<const uint4*>(xa + (T * nss + S) * A4_SSB + (c & 511) * 16)
-                          : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_b = [&](int buf, const uint4 (&src)[4]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = 4 * t + k, u = c & 511;
-      const int q = u >> 7, l = (u >> 1) & 63, h = u & 1;
-      *reinterpret_cast<uint4*>(&bs[buf][(c >> 9) * A4_SSB + q * 2048 + h * 1024 + l * 16]) = src[k];
-    }
+    for (int k = 0; k < QG_DMA; ++k) a4_dma16(src[k] + S * step[k], sb + uint32_t(lds_block(k)));
   };
 
   v4f_t acc[QG_RT][QG_VT];
@@ -1207,59 +1228,49 @@ __global__ __launch_bounds__(256) void qgemm_a4_kernel(
   for (int rt = 0; rt < QG_RT; ++rt)
 #pragma unroll
     for (int vt = 0; vt < QG_VT; ++vt) acc[rt][vt] = v4f_t{0.f, 0.f, 0.f, 0.f};
-  // loads run two super-steps ahead: a1, b1 for S + 1 and a2, b2 for S + 2
-  uint4 a1[QG_RT][2], a2[QG_RT][2], b1[4], b2[4];
-  load_b(0, b1);
-  load_a(0, a1);
-  if (nss > 1) {
-    load_b(1, b2);
-    load_a(1, a2);
-  }
-  store_b(0, b1);
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) b1[k] = b2[k];
+  issue(0);
+  if (nss > 1) issue(1);
   for (int64_t S = 0; S < nss; ++S) {
-    const int buf = int(S & 1);
-    uint4 ac[QG_RT][2];
+    // own DMA of stage S done (stage S + 1 may stay in flight), then every
+    // wave's; the barrier also retires all reads of the slot stage S + 2 reuses
+    if (S + 1 < nss) a4_wait_vm<QG_DMA>();
+    else a4_wait_vm<0>();
+    __syncthreads();
+    if (S + 2 < nss) issue(S + 2);
+    // all of the super-step's fragments first (one LDS latency per step,
+    // not one per MFMA group: a SIMD runs a single wave here), then its 32
+    // MFMAs back to back
+    const uint8_t* st = ring + (S % QG_NST) * QG_STAGE;
+    v8i_t b[4][QG_VT];
+    uint4 a[QG_RT][2];
 #pragma unroll
-    for (int rt = 0; rt < QG_RT; ++rt) {
-      ac[rt][0] = a1[rt][0];
-      ac[rt][1] = a1[rt][1];
-      a1[rt][0] = a2[rt][0];
-      a1[rt][1] = a2[rt][1];
-    }
-    if (S + 2 < nss) {
-      load_a(S + 2, a2);
-      load_b(S + 2, b2);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v8i_t b[QG_VT];
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int vt = 0; vt < QG_VT; ++vt) {
-        const uint8_t* p = &bs[buf][vt * A4_SSB + q * 2048 + lane * 16];
+        const uint8_t* p = st + QG_ABYTES + ((vt * 4 + q) * 2) * 1024 + lane * 16;
         const uint4 lo = *reinterpret_cast<const uint4*>(p);
         const uint4 hi = *reinterpret_cast<const uint4*>(p + 1024);
-        b[vt] = v8i_t{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        b[q][vt] = v8i_t{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
       }
 #pragma unroll
+    for (int rt = 0; rt < QG_RT; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        a[rt][h] = *reinterpret_cast<const uint4*>(st + (w * 8 + 2 * rt + h) * 1024 + lane * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
       for (int rt = 0; rt < QG_RT; ++rt) {
-        const uint32_t wd[8] = {ac[rt][0].x, ac[rt][0].y, ac[rt][0].z, ac[rt][0].w,
-                                ac[rt][1].x, ac[rt][1].y, ac[rt][1].z, ac[rt][1].w};
-        const uint32_t x0 = wd[2 * q], x1 = wd[2 * q + 1];
+        // step q = 2 h + o: words 2 o, 2 o + 1 of half h
+        const uint4 x4 = a[rt][q >> 1];
+        const uint32_t x0 = (q & 1) ? x4.z : x4.x, x1 = (q & 1) ? x4.w : x4.y;
         const v8i_t aop = {int(x0 & 0x33333333u), int((x0 >> 2) & 0x33333333u),
                            int(x1 & 0x33333333u), int((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
 #pragma unroll
         for (int vt = 0; vt < QG_VT; ++vt)
-          acc[rt][vt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, b[vt], acc[rt][vt], 4, 0, 0,
+          acc[rt][vt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, b[q][vt], acc[rt][vt], 4, 0, 0,
                                                                          0x7f7f7f7f, 0, int(0x80808080u));
       }
-    }
-    if (S + 1 < nss) store_b(buf ^ 1, b1);  // that buffer's last reads were before the previous barrier
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) b1[k] = b2[k];
   }
 #pragma unroll
   for (int k = 0; k < QG_PRE; ++k)
@@ -1430,7 +1441,10 @@ kq_status apply_a4_run(const uint32_t* packed, const float* scale, const float* 
   // K-split product keeps more loads in flight
   const int64_t nvb = cdiv(batch, QG_VT * A4_TILE), nrbg = cdiv(d_out, QG_ROWS);
   if (batch > A4_TILE && nvb * nrbg >= 256) {
-    qgemm_a4_kernel<<<unsigned(8 * cdiv(nrbg, 8) * nvb), 256, 0, s>>>(
+    constexpr size_t ring_bytes = size_t(QG_NST) * QG_STAGE;  // 144 KB
+    KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(qgemm_a4_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, int(ring_bytes)));
+    qgemm_a4_kernel<<<unsigned(8 * cdiv(nrbg, 8) * nvb), 256, ring_bytes, s>>>(
         packed, int(rw), scale, zero, w.xa, w.ascale, w.asum, nsum, nss, d_out, batch, int(nvb), y1);
   } else {
     qmatvec_a4_kernel<RK><<<unsigned(8 * cdiv(nrb, 8) * ntiles), 64 * nw, red_bytes, s>>>(
