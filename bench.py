@@ -89,7 +89,7 @@ def run_gpu(spec, steps, warmup, data):
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     names = ["cov", "biip", "sens", "chol", "gptaq"]
     stream = torch.cuda.current_stream()
-    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(ev=None, k=None):
         W.copy_(W0)
@@ -106,7 +106,11 @@ def run_gpu(spec, steps, warmup, data):
         if ev: ev[3].record(stream)
         kq.kq_cholesky_inv(HX, spec.damp, U, ws=ws)
         if ev: ev[4].record(stream)
+        if k is not None:
+            kq.kq_set_kernel_events(N.KQ_OP_GPTAQ_QUANTIZE, kev[k][2], kev[k][3], stream)
         kq.kq_gptaq_quantize(W, U, D, spec.bits, spec.group, spec.block, codes, scale, zero, ws=ws)
+        if k is not None:
+            kq.kq_set_kernel_events(N.KQ_OP_GPTAQ_QUANTIZE)
         if ev: ev[5].record(stream)
         return out
 
@@ -127,6 +131,8 @@ def run_gpu(spec, steps, warmup, data):
     stage_ms = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
                 for i, nm in enumerate(names)}
     cov_kernel_ms = float(np.mean([kev[k][0].elapsed_time(kev[k][1]) for k in range(steps)]))
+    trail_kernel_ms = (float(np.mean([kev[k][2].elapsed_time(kev[k][3]) for k in range(steps)]))
+                       if spec.d_in > 512 else None)
     # quality check outside the timed region
     W0p = None
     obj = None
@@ -152,7 +158,8 @@ def run_gpu(spec, steps, warmup, data):
     inf = run_inference(spec, codes, scale, zero, s_x, s_g, si, so)
     fb = run_output_feedback(spec, W0p, HX, D, HG, U, obj) if W0p is not None and not spec.group else None
     cap = run_streaming(spec, X, Xq, G, HX, D, HG, ws)
-    return dict(wall_s=wall, stage_ms=stage_ms, cov_kernel_ms=cov_kernel_ms, sens=sens, obj=obj,
+    return dict(wall_s=wall, stage_ms=stage_ms, cov_kernel_ms=cov_kernel_ms, trail_kernel_ms=trail_kernel_ms,
+                sens=sens, obj=obj,
                 obj_rtn=obj_rtn, inference=inf, streaming=cap, output_feedback=fb)
 
 
@@ -469,6 +476,19 @@ def main():
         "gptaq_tflops": round(costs["solve_flops"] / st["gptaq"] / 1e9, 2),
         "no_cov_ms": round(sum(v for k, v in st.items() if k != "cov"), 3),
     }
+    stages["cov_frac_bf16"] = round(costs["cov_flops"] / (st["cov"] * 1e-3) / PEAK_BF16, 4)
+    stages["biip_frac_hbm"] = round(costs["biip_bytes"] / (st["biip"] * 1e-3) / PEAK_HBM, 4)
+    stages["chol_frac_fp32"] = round(costs["chol_flops"] / (st["chol"] * 1e-3) / PEAK_FP32_MFMA, 4)
+    stages["gptaq_frac_fp32"] = round(costs["solve_flops"] / (st["gptaq"] * 1e-3) / PEAK_FP32_MFMA, 4)
+    trailing = None
+    if g["trail_kernel_ms"]:
+        # the sweep's largest lazy GEMM: d_out x (d_in - 512) x 512, event-timed
+        tf = 2.0 * spec.d_out * (spec.d_in - 512) * 512
+        tms = g["trail_kernel_ms"]
+        trailing = {"kernel": "gemm_f32_kernel (first superblock's trailing update)",
+                    "shape": [spec.d_out, spec.d_in - 512, 512], "kernel_ms": round(tms, 4),
+                    "achieved": round(tf / (tms * 1e-3) / 1e12, 2), "peak": PEAK_FP32_MFMA / 1e12,
+                    "unit": "TFLOP/s", "frac": round(tf / (tms * 1e-3) / PEAK_FP32_MFMA, 4)}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(spec, data, min(args.cpu_prefix, spec.n_tok))
@@ -487,6 +507,7 @@ def main():
                    "inputs": spec.dtype, "bits": spec.bits, "group": spec.group,
                    "block": spec.block, "damp": spec.damp},
         "roofline": roof,
+        "trailing_gemm": trailing,
         "stages": stages,
         "sensitivity": g["sens"][2],
         "objective": g["obj"], "objective_rtn": g["obj_rtn"],

@@ -95,6 +95,9 @@ const char* kq_version(void);
  *          together; the drift pre-pass and the split reduction lie outside
  *          the bracket). For fp32 inputs the bracket holds the three
  *          products and the drift pass.
+ *          KQ_OP_GPTAQ_QUANTIZE: the first 512-column superblock's lazy
+ *          trailing update, the sweep's largest GEMM (d_out x (d_in - 512)
+ *          x 512; none if d_in <= 512).
  *          KQ_OP_APPLY_QUANTIZED: the product with the packed codes (one
  *          launch per 4 vectors of the batch; the two transforms lie
  *          outside the bracket).

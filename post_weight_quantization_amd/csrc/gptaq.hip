@@ -375,7 +375,11 @@ kq_status gptaq_run(float* W, const float* U, const float* D, int64_t d_out, int
     if (far > 0) {
       GemmArgs gt = gemm_args(E, SB, U + s0 * n + s1, n, Wbar + s1, n, d_out, far, s1 - s0, -1.f,
                               1.f, 0);
+      // the first superblock's update is the largest lazy GEMM: the one the
+      // kernel-event hook brackets
+      if (s0 == 0) KQ_TRY(mark_kernel(KQ_OP_GPTAQ_QUANTIZE, 0, s));
       KQ_TRY(gemm_f32(gt, s));
+      if (s0 == 0) KQ_TRY(mark_kernel(KQ_OP_GPTAQ_QUANTIZE, 1, s));
     }
   }
   return KQ_OK;

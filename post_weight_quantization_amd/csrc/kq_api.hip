@@ -92,10 +92,11 @@ const char* kq_version(void) { return "kq 0.1 gfx950"; }
 
 kq_status kq_set_kernel_events(kq_op op, hipEvent_t start, hipEvent_t stop) {
   clear_error();
-  if (op != KQ_OP_ACCUMULATE_COV && op != KQ_OP_APPLY_QUANTIZED && op != KQ_OP_APPLY_QUANTIZED_A4)
+  if (op != KQ_OP_ACCUMULATE_COV && op != KQ_OP_GPTAQ_QUANTIZE && op != KQ_OP_APPLY_QUANTIZED &&
+      op != KQ_OP_APPLY_QUANTIZED_A4)
     return fail(KQ_ERR_UNSUPPORTED,
-                "set_kernel_events: only KQ_OP_ACCUMULATE_COV and the two KQ_OP_APPLY_QUANTIZED ops have a "
-                "timed kernel");
+                "set_kernel_events: only KQ_OP_ACCUMULATE_COV, KQ_OP_GPTAQ_QUANTIZE and the two "
+                "KQ_OP_APPLY_QUANTIZED ops have a timed kernel");
   if ((start == nullptr) != (stop == nullptr))
     return fail(KQ_ERR_ARG, "set_kernel_events: pass both events or neither");
   g_kernel_ev[op][0] = start;

@@ -71,6 +71,9 @@ def test_kernel_event_hook_validation():
     assert N.lib.kq_set_kernel_events(N.KQ_OP_BIIP, None, None) == N.KQ_ERR_UNSUPPORTED
     assert N.lib.kq_set_kernel_events(N.KQ_OP_ACCUMULATE_COV, fake, None) == N.KQ_ERR_ARG
     assert N.lib.kq_set_kernel_events(N.KQ_OP_ACCUMULATE_COV, None, None) == N.KQ_OK
+    for op in (N.KQ_OP_GPTAQ_QUANTIZE, N.KQ_OP_APPLY_QUANTIZED, N.KQ_OP_APPLY_QUANTIZED_A4):
+        assert N.lib.kq_set_kernel_events(op, None, None) == N.KQ_OK
+    assert N.lib.kq_set_kernel_events(N.KQ_OP_YAQA_QUANTIZE, None, None) == N.KQ_ERR_UNSUPPORTED
 
 
 def test_inference_entry_points_validate_on_host():
