@@ -33,6 +33,39 @@ constexpr int CHP = CH + CH / 32;
 constexpr int CHRP = CHR + CHR / 32;
 
 // Row pass: chunk = R rows x L cols (R*L = CHR, b | L, L | cols).
+// One radix-2^NB pass over bits [Q, Q + NB) of the flat LDS index with Q and
+// NB known at compile time. A group's base has those bits clear and its
+// offsets J = j << Q use only them, so padi(base + J) = padi(base) + J +
+// (J >> 5): every access is the base plus a constant.
+template <int Q, int NB>
+__device__ inline void fwht_pass_ct(float* s, int n_el) {
+  const int ngroups = n_el >> NB;
+  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
+    const int base = ((g >> Q) << (Q + NB)) | (g & ((1 << Q) - 1));
+    float* p = s + padi(base);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < (1 << NB); ++j) v[j] = p[(j << Q) + ((j << Q) >> 5)];
+    bfly8(v, NB);
+#pragma unroll
+    for (int j = 0; j < (1 << NB); ++j) p[(j << Q) + ((j << Q) >> 5)] = v[j];
+  }
+  __syncthreads();
+}
+
+// Butterflies over bits [0, LGB), radix 8 (the last pass narrower).
+template <int LGB, int Q = 0>
+__device__ inline void fwht_ct(float* s, int n_el) {
+  if constexpr (Q < LGB) {
+    constexpr int NB = LGB - Q < 3 ? LGB - Q : 3;
+    fwht_pass_ct<Q, NB>(s, n_el);
+    fwht_ct<LGB, Q + NB>(s, n_el);
+  }
+}
+
+// LGB > 0: the Hadamard block's bits fixed at compile time (the workloads'
+// 4096 and 8192 blocks); LGB = 0: any block, from lgb.
+template <int LGB>
 __global__ __launch_bounds__(256) void fwht_rows_kernel(float* M, int64_t rows, int64_t cols,
                                                         int lgL, int lgb, const float* rowf,
                                                         const float* colf, float gain) {
@@ -71,7 +104,8 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(float* M, int64_t rows, 
     s[padi(e + 3)] = v.w;
   }
   __syncthreads();
-  lds_fwht(s, CHR, 0, lgb);
+  if constexpr (LGB > 0) fwht_ct<LGB>(s, CHR);
+  else lds_fwht(s, CHR, 0, lgb);
   for (int e = 4 * t; e < CHR; e += 4 * blockDim.x) {
     const int rr = e >> lgL, c = e & (L - 1);
     const int64_t row = r0 + rr;
@@ -205,7 +239,13 @@ kq_status fwht_rows(float* M, int64_t rows, int64_t cols, int64_t blk, const flo
   const int64_t R = CHR / L;
   if (L > CHR) return fail(KQ_ERR_UNSUPPORTED, "biip: Hadamard blocks above %d are not supported", CHR);
   const int64_t chunks = cdiv(rows, R) * (cols / L);
-  fwht_rows_kernel<<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, ilog2(L), ilog2(blk), rowf, colf, gain);
+  const int lgb = ilog2(blk);
+  if (lgb == 12)
+    fwht_rows_kernel<12><<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, ilog2(L), lgb, rowf, colf, gain);
+  else if (lgb == 13)
+    fwht_rows_kernel<13><<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, ilog2(L), lgb, rowf, colf, gain);
+  else
+    fwht_rows_kernel<0><<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, ilog2(L), lgb, rowf, colf, gain);
   KQ_HIP(hipGetLastError());
   return KQ_OK;
 }
