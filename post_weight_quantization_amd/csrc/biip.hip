@@ -33,36 +33,6 @@ constexpr int CHP = CH + CH / 32;
 constexpr int CHRP = CHR + CHR / 32;
 
 // Row pass: chunk = R rows x L cols (R*L = CHR, b | L, L | cols).
-// One radix-2^NB pass over bits [Q, Q + NB) of the flat LDS index with Q and
-// NB known at compile time. A group's base has those bits clear and its
-// offsets J = j << Q use only them, so padi(base + J) = padi(base) + J +
-// (J >> 5): every access is the base plus a constant.
-template <int Q, int NB>
-__device__ inline void fwht_pass_ct(float* s, int n_el) {
-  const int ngroups = n_el >> NB;
-  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
-    const int base = ((g >> Q) << (Q + NB)) | (g & ((1 << Q) - 1));
-    float* p = s + padi(base);
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < (1 << NB); ++j) v[j] = p[(j << Q) + ((j << Q) >> 5)];
-    bfly8(v, NB);
-#pragma unroll
-    for (int j = 0; j < (1 << NB); ++j) p[(j << Q) + ((j << Q) >> 5)] = v[j];
-  }
-  __syncthreads();
-}
-
-// Butterflies over bits [0, LGB), radix 8 (the last pass narrower).
-template <int LGB, int Q = 0>
-__device__ inline void fwht_ct(float* s, int n_el) {
-  if constexpr (Q < LGB) {
-    constexpr int NB = LGB - Q < 3 ? LGB - Q : 3;
-    fwht_pass_ct<Q, NB>(s, n_el);
-    fwht_ct<LGB, Q + NB>(s, n_el);
-  }
-}
-
 // LGB > 0: the Hadamard block's bits fixed at compile time (the workloads'
 // 4096 and 8192 blocks); LGB = 0: any block, from lgb.
 template <int LGB>
@@ -104,8 +74,7 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(float* M, int64_t rows, 
     s[padi(e + 3)] = v.w;
   }
   __syncthreads();
-  if constexpr (LGB > 0) fwht_ct<LGB>(s, CHR);
-  else lds_fwht(s, CHR, 0, lgb);
+  lds_fwht_blk<LGB>(s, CHR, lgb);
   for (int e = 4 * t; e < CHR; e += 4 * blockDim.x) {
     const int rr = e >> lgL, c = e & (L - 1);
     const int64_t row = r0 + rr;

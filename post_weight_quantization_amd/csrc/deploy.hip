@@ -48,6 +48,7 @@
 #include "kq_internal.h"
 #include "fwht_lds.h"
 
+#include <type_traits>
 #include <utility>
 
 namespace kq {
@@ -100,6 +101,16 @@ inline int ilog2(int64_t v) {
   return k;
 }
 
+// Launch helper: f(std::integral_constant<int, LGB>) with the transforms'
+// FWHT passes fixed at compile time for the workloads' 4096 and 8192 blocks
+// (LGB = 12, 13), generic otherwise (LGB = 0).
+template <class F>
+void with_lgb(int lgb, F&& f) {
+  if (lgb == 12) f(std::integral_constant<int, 12>{});
+  else if (lgb == 13) f(std::integral_constant<int, 13>{});
+  else f(std::integral_constant<int, 0>{});
+}
+
 // Transform chunk: the largest L with blk | L, L | n, L <= TCH.
 int64_t transform_len(int64_t n, int64_t blk) {
   int64_t L = blk;
@@ -111,7 +122,7 @@ int64_t transform_len(int64_t n, int64_t blk) {
 // of vector b, written as prepared chunks xq[b][c] (XW words each). One
 // workgroup per chunk of columns; blockDim is a multiple of 64 dividing L
 // (or 64 when L = 32).
-template <int BITS>
+template <int BITS, int LGB>
 __global__ __launch_bounds__(1024) void transform_in_kernel(const float* __restrict__ x, int64_t d_in,
                                                             int lgL, int lgb,
                                                             const int8_t* __restrict__ si,
@@ -132,7 +143,7 @@ __global__ __launch_bounds__(1024) void transform_in_kernel(const float* __restr
     s[padi(e + 3)] = v.w * float(si[c0 + e + 3]) / sx.w;
   }
   __syncthreads();
-  lds_fwht(s, L, 0, lgb);
+  lds_fwht_blk<LGB>(s, L, lgb);
   const int64_t nchunk = d_in / CODES;
   uint32_t* dst = xq + (b * nchunk + (c0 >> 5)) * XW;  // this chunk's first prepared chunk
   if constexpr (BITS == 3) {
@@ -192,6 +203,7 @@ __global__ __launch_bounds__(1024) void transform_in_kernel(const float* __restr
 }
 
 // y[b][r0 + e] = gain * sign_out / s_g * (H_blk y1[b])[r0 + e]
+template <int LGB>
 __global__ __launch_bounds__(1024) void transform_out_kernel(const float* __restrict__ y1,
                                                              int64_t d_out, int lgL, int lgb,
                                                              const int8_t* __restrict__ so,
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(1024) void transform_out_kernel(const float* __rest
     s[padi(e + 3)] = v.w;
   }
   __syncthreads();
-  lds_fwht(s, L, 0, lgb);
+  lds_fwht_blk<LGB>(s, L, lgb);
   float* dst = y + b * d_out + r0;
   for (int e = threadIdx.x; e < L; e += blockDim.x)
     dst[e] = gain * s[padi(e)] * float(so[r0 + e]) / s_g[r0 + e];
@@ -564,8 +576,10 @@ kq_status run_bits(const uint32_t* packed, int64_t rw, const float* scale, const
                    float* y1, hipStream_t s) {
   const int64_t Li = transform_len(d_in, bi);
   const unsigned tin = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Li / 4)));
-  transform_in_kernel<BITS><<<unsigned(batch * (d_in / Li)), tin, 0, s>>>(
-      x, d_in, ilog2(Li), ilog2(bi), si, s_x, float(1.0 / std::sqrt(double(bi))), xq);
+  with_lgb(ilog2(bi), [&](auto C) {
+    transform_in_kernel<BITS, decltype(C)::value><<<unsigned(batch * (d_in / Li)), tin, 0, s>>>(
+        x, d_in, ilog2(Li), ilog2(bi), si, s_x, float(1.0 / std::sqrt(double(bi))), xq);
+  });
   KQ_HIP(hipGetLastError());
   const int64_t nchunk = d_in / CODES;
   KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED, 0, s));
@@ -621,6 +635,7 @@ __device__ inline uint8_t e4m3_int(int n) {
 // x2 = gain * H_blk (x[b] sign_in / s_x) over L columns, written as B digits
 // xb[b][S][q][g][l][32 bytes], scale words xs[b][S][G][l] (byte q) and the
 // chunk's sum of x2 in xsum[b][blockIdx % per_row].
+template <int LGB>
 __global__ __launch_bounds__(1024) void transform_in_mx_kernel(
     const float* __restrict__ x, int64_t d_in, int lgL, int lgb, const int8_t* __restrict__ si,
     const float* __restrict__ s_x, float gain, uint8_t* __restrict__ xb, uint32_t* __restrict__ xs,
@@ -644,7 +659,7 @@ __global__ __launch_bounds__(1024) void transform_in_mx_kernel(
   }
   for (int i = threadIdx.x; i < L / 32 * MX_DIG; i += blockDim.x) scl[i] = 0u;
   __syncthreads();
-  lds_fwht(s, L, 0, lgb);
+  lds_fwht_blk<LGB>(s, L, lgb);
   float tsum = 0.f;
   // one value per lane; the 32 lanes of a half-wave hold one chunk
   for (int e = threadIdx.x; e < L; e += blockDim.x) {
@@ -832,8 +847,11 @@ kq_status run_mx(const uint32_t* packed, int64_t rw, const float* scale, const f
                  hipStream_t s) {
   const int64_t Li = transform_len(d_in, bi);
   const int64_t nss = d_in / MX_SS, nparts = d_in / Li;
-  transform_in_mx_kernel<<<unsigned(batch * nparts), unsigned(std::min<int64_t>(1024, Li / 4)), 0, s>>>(
-      x, d_in, ilog2(Li), ilog2(bi), si, s_x, float(1.0 / std::sqrt(double(bi))), xb, xs, xsum);
+  with_lgb(ilog2(bi), [&](auto C) {
+    transform_in_mx_kernel<decltype(C)::value>
+        <<<unsigned(batch * nparts), unsigned(std::min<int64_t>(1024, Li / 4)), 0, s>>>(
+            x, d_in, ilog2(Li), ilog2(bi), si, s_x, float(1.0 / std::sqrt(double(bi))), xb, xs, xsum);
+  });
   KQ_HIP(hipGetLastError());
   KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED, 0, s));
   for (int64_t b0 = 0; b0 < batch; b0 += 2) {
@@ -921,7 +939,7 @@ __device__ inline void a4_store(const uint8_t* stg, int nS, int64_t b, int64_t S
 // the whole vector): quantize it here, with the vector's code sum in
 // asum[b]. Otherwise write x2 and the chunk's largest magnitude for
 // quantize_a4_kernel.
-template <bool FUSED>
+template <bool FUSED, int LGB>
 __global__ __launch_bounds__(1024) void transform_in_a4_kernel(
     const float* __restrict__ x, int64_t d_in, int lgL, int lgb, const int8_t* __restrict__ si,
     const float* __restrict__ s_x, float gain, float clip, float* __restrict__ x2,
@@ -945,7 +963,7 @@ __global__ __launch_bounds__(1024) void transform_in_a4_kernel(
     s[padi(e + 3)] = v.w * float(si[c0 + e + 3]) / sx.w;
   }
   __syncthreads();
-  lds_fwht(s, L, 0, lgb);
+  lds_fwht_blk<LGB>(s, L, lgb);
   __syncthreads();
   float mx = 0.f;
   for (int e = 4 * threadIdx.x; e < L; e += 4 * blockDim.x) {
@@ -1380,8 +1398,10 @@ kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const 
   }
   const int64_t Lo = transform_len(d_out, bo);
   const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));
-  transform_out_kernel<<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(
-      y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), y);
+  with_lgb(ilog2(bo), [&](auto C) {
+    transform_out_kernel<decltype(C)::value><<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(
+        y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), y);
+  });
   KQ_HIP(hipGetLastError());
   return KQ_OK;
 }
@@ -1407,14 +1427,18 @@ kq_status apply_a4_run(const uint32_t* packed, const float* scale, const float* 
   const unsigned tin = unsigned(std::min<int64_t>(1024, Li / 4));
   const float gain = float(1.0 / std::sqrt(double(bi)));
   if (nparts == 1) {
-    transform_in_a4_kernel<true><<<unsigned(batch), tin, 0, s>>>(
-        x, d_in, ilog2(Li), ilog2(bi), si, s_x, gain, clip, nullptr, w.pmax, w.xa, w.ascale, w.asum,
-        codes_out, scale_out);
+    with_lgb(ilog2(bi), [&](auto C) {
+      transform_in_a4_kernel<true, decltype(C)::value><<<unsigned(batch), tin, 0, s>>>(
+          x, d_in, ilog2(Li), ilog2(bi), si, s_x, gain, clip, nullptr, w.pmax, w.xa, w.ascale, w.asum,
+          codes_out, scale_out);
+    });
     KQ_HIP(hipGetLastError());
   } else {
-    transform_in_a4_kernel<false><<<unsigned(batch * nparts), tin, 0, s>>>(
-        x, d_in, ilog2(Li), ilog2(bi), si, s_x, gain, clip, w.x2, w.pmax, w.xa, w.ascale, w.asum,
-        codes_out, scale_out);
+    with_lgb(ilog2(bi), [&](auto C) {
+      transform_in_a4_kernel<false, decltype(C)::value><<<unsigned(batch * nparts), tin, 0, s>>>(
+          x, d_in, ilog2(Li), ilog2(bi), si, s_x, gain, clip, w.x2, w.pmax, w.xa, w.ascale, w.asum,
+          codes_out, scale_out);
+    });
     KQ_HIP(hipGetLastError());
     quantize_a4_kernel<<<unsigned(batch * nss), 128, 0, s>>>(w.x2, w.pmax, int(nparts), d_in, nss, clip,
                                                              w.xa, w.ascale, w.asum, codes_out, scale_out);
@@ -1455,8 +1479,10 @@ kq_status apply_a4_run(const uint32_t* packed, const float* scale, const float* 
   KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED_A4, 1, s));
   const int64_t Lo = transform_len(d_out, bo);
   const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));
-  transform_out_kernel<<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(
-      y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), y);
+  with_lgb(ilog2(bo), [&](auto C) {
+    transform_out_kernel<decltype(C)::value><<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(
+        y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), y);
+  });
   KQ_HIP(hipGetLastError());
   return KQ_OK;
 }

@@ -50,4 +50,42 @@ __device__ inline void lds_fwht(float* s, int n_el, int bit_lo, int nbits) {
   }
 }
 
+// One radix-2^NB pass over bits [Q, Q + NB) of the flat LDS index with Q and
+// NB known at compile time. A group's base has those bits clear and its
+// offsets J = j << Q use only them, so padi(base + J) = padi(base) + J +
+// (J >> 5): every access is the base plus a constant.
+template <int Q, int NB>
+__device__ inline void lds_fwht_pass_ct(float* s, int n_el) {
+  const int ngroups = n_el >> NB;
+  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
+    const int base = ((g >> Q) << (Q + NB)) | (g & ((1 << Q) - 1));
+    float* p = s + padi(base);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < (1 << NB); ++j) v[j] = p[(j << Q) + ((j << Q) >> 5)];
+    bfly8(v, NB);
+#pragma unroll
+    for (int j = 0; j < (1 << NB); ++j) p[(j << Q) + ((j << Q) >> 5)] = v[j];
+  }
+  __syncthreads();
+}
+
+// Butterflies over bits [0, LGB), radix 8 (the last pass narrower).
+template <int LGB, int Q = 0>
+__device__ inline void lds_fwht_ct(float* s, int n_el) {
+  if constexpr (Q < LGB) {
+    constexpr int NB = LGB - Q < 3 ? LGB - Q : 3;
+    lds_fwht_pass_ct<Q, NB>(s, n_el);
+    lds_fwht_ct<LGB, Q + NB>(s, n_el);
+  }
+}
+
+// Butterflies over bits [0, lgb): the compile-time passes for LGB > 0 (then
+// lgb must equal LGB), the generic ones for LGB = 0.
+template <int LGB>
+__device__ inline void lds_fwht_blk(float* s, int n_el, int lgb) {
+  if constexpr (LGB > 0) lds_fwht_ct<LGB>(s, n_el);
+  else lds_fwht(s, n_el, 0, lgb);
+}
+
 }  // namespace kq
