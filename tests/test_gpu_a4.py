@@ -74,12 +74,13 @@ def _check(codes, scale, zero, s_x, s_g, si, so, x, clip=1.0, bi=0, bo=0):
 # batches of 1, 16 (one full tile), 17 and 40 (a partial tile); many tiles,
 # where a workgroup takes 128 rows (the last row block ragged at 2100);
 # grids of >= 256 workgroups of 256 rows x 32 vectors take the GEMM (ragged
-# rows and vectors at 2100 x 930, whole blocks at 2048 x 1024)
+# rows and vectors at 2100 x 930, whole blocks at 2048 x 1024); a long K
+# with several vector tiles on the K-split product (2100 x 24576, batch 120)
 @pytest.mark.parametrize("d_out,d_in,batch,bi,bo,clip", [
     (256, 512, 1, 0, 0, 1.0), (260, 1536, 17, 512, 0, 0.9), (128, 4096, 16, 0, 0, 1.0),
     (64, 12288, 5, 4096, 32, 0.8), (96, 8192, 40, 0, 0, 1.0), (512, 2048, 3, 256, 128, 1.0),
     (4096, 1024, 256, 256, 0, 0.9), (2100, 1024, 600, 0, 0, 1.0), (2100, 512, 930, 0, 0, 1.0),
-    (2048, 1536, 1024, 512, 0, 0.9)])
+    (2048, 1536, 1024, 512, 0, 0.9), (2100, 24576, 120, 0, 0, 1.0)])
 def test_a4_against_oracle(d_out, d_in, batch, bi, bo, clip):
     rng = np.random.default_rng(d_out + d_in + batch)
     c = _case(d_out, d_in, rng)
@@ -88,7 +89,7 @@ def test_a4_against_oracle(d_out, d_in, batch, bi, bo, clip):
 
 
 @pytest.mark.parametrize("d_out,d_in,batch", [(260, 1536, 1), (64, 512, 16), (200, 2560, 17),
-                                              (8, 4096, 40), (2100, 1024, 930)])
+                                              (8, 4096, 40), (2100, 1024, 930), (2100, 24576, 120)])
 def test_a4_integer_product_bit_exact(d_out, d_in, batch):
     """Identity transforms and integer inputs of largest magnitude 7: y is
     sum_k q_k a_k - zero sum_k a_k exactly."""
@@ -145,7 +146,7 @@ def test_a4_close_to_the_weight_only_product():
 
 @pytest.mark.slow
 @pytest.mark.parametrize("d_out,d_in,batch", [(4096, 4096, 16), (8192, 28672, 16), (11008, 4096, 33),
-                                              (8192, 28672, 256)])
+                                              (8192, 28672, 256), (8192, 28672, 64)])
 def test_a4_full_size(d_out, d_in, batch):
     rng = np.random.default_rng(d_out + batch)
     c = _case(d_out, d_in, rng)
