@@ -306,7 +306,8 @@ kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* 
  *   y                   batch x d_out fp32 output
  *   act_codes           NULL, or batch x d_in int8 output: the codes a
  *   act_scale           NULL, or batch floats output: the scales s
- * d_in must be a multiple of 512 and d_out of 4. packed, x, y, s_x and
+ * d_in must be a multiple of 512, d_out of 4, and 1 <= batch <= 65536 (the
+ * launch grids' limit). packed, x, y, s_x and
  * act_codes must be 16-byte aligned. Workspace from
  * kq_workspace_size(KQ_OP_APPLY_QUANTIZED_A4, d_out, d_in, batch, ...).
  * Asynchronous. Errors: KQ_ERR_ARG (NULL, alignment, clip), KQ_ERR_SHAPE. */

@@ -407,8 +407,8 @@ kq_status kq_apply_quantized_a4(const uint32_t* packed, const float* scale, cons
     return fail(KQ_ERR_ARG, "apply_quantized_a4: NULL argument");
   if (!(clip > 0.f && clip <= 1.f))
     return fail(KQ_ERR_ARG, "apply_quantized_a4: clip must be in (0, 1]");
-  if (d_out < 4 || d_out % 4 || batch < 1)
-    return fail(KQ_ERR_SHAPE, "apply_quantized_a4: d_out must be a multiple of 4 and batch >= 1");
+  if (d_out < 4 || d_out % 4 || batch < 1 || batch > 65536)
+    return fail(KQ_ERR_SHAPE, "apply_quantized_a4: d_out must be a multiple of 4 and 1 <= batch <= 65536");
   if (d_in < 512 || d_in % 512)
     return fail(KQ_ERR_SHAPE, "apply_quantized_a4: d_in must be a multiple of 512");
   if (d_in > (int64_t(1) << 24))

@@ -167,6 +167,8 @@ def test_apply_a4_validation():
     assert st == N.KQ_ERR_SHAPE
     st, _ = call(batch=0)
     assert st == N.KQ_ERR_SHAPE
+    st, msg = call(batch=65537)
+    assert st == N.KQ_ERR_SHAPE and "65536" in msg
     st, _ = call(blk_in=3)
     assert st == N.KQ_ERR_SHAPE
     st, msg = call(codes=ctypes.c_void_p(0x10004))
