@@ -280,7 +280,8 @@ kq_status kq_pack_codes(const uint8_t* codes, int64_t d_out, int64_t d_in, int32
  *                       blk_in, blk_out (0 = largest power of two dividing)
  *   x                   batch x d_in fp32, row-major (not modified)
  *   y                   batch x d_out fp32 output
- * d_in must be a multiple of 32 (of 128 with groups). Workspace from
+ * d_in must be a multiple of 32 (of 128 with groups), and 1 <= batch <=
+ * 65536 (the launch grids' limit). Workspace from
  * kq_workspace_size(KQ_OP_APPLY_QUANTIZED, d_out, d_in, batch, ...).
  * Asynchronous; fp32 arithmetic. */
 kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* scale,

@@ -380,8 +380,8 @@ kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* 
     return fail(KQ_ERR_ARG, "apply_quantized: bits must be 2, 3, 4 or 8");
   if (group != 0 && group != 128)
     return fail(KQ_ERR_UNSUPPORTED, "apply_quantized: group must be 0 or 128");
-  if (d_out < 4 || d_out % 4 || batch < 1)
-    return fail(KQ_ERR_SHAPE, "apply_quantized: d_out must be a multiple of 4 and batch >= 1");
+  if (d_out < 4 || d_out % 4 || batch < 1 || batch > 65536)
+    return fail(KQ_ERR_SHAPE, "apply_quantized: d_out must be a multiple of 4 and 1 <= batch <= 65536");
   if (d_in < 32 || d_in % 32 || (group && d_in % group))
     return fail(KQ_ERR_SHAPE, "apply_quantized: d_in must be a multiple of 32 (of the group size)");
   int64_t bi = 0, bo = 0;

@@ -90,6 +90,9 @@ def test_inference_entry_points_validate_on_host():
     assert N.lib.kq_apply_quantized(*args(2, 64, 64, 128, 1 << 30)) == N.KQ_ERR_UNSUPPORTED
     assert N.lib.kq_apply_quantized(*args(2, 0, 64, 48, 1 << 30)) == N.KQ_ERR_SHAPE
     assert N.lib.kq_apply_quantized(*args(2, 0, 6, 64, 1 << 30)) == N.KQ_ERR_SHAPE
+    big = list(args(2, 0, 64, 64, 1 << 30))
+    big[12] = 65537  # batch
+    assert N.lib.kq_apply_quantized(*big) == N.KQ_ERR_SHAPE
     st = N.lib.kq_apply_quantized(*args(2, 0, 64, 64, 16))
     assert st == N.KQ_ERR_WORKSPACE
     assert N.lib.kq_pack_codes(None, 4, 4, 2, fake, None) == N.KQ_ERR_ARG
