@@ -311,7 +311,9 @@ kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* 
  * launch grids' limit). packed, x, y, s_x and
  * act_codes must be 16-byte aligned. Workspace from
  * kq_workspace_size(KQ_OP_APPLY_QUANTIZED_A4, d_out, d_in, batch, ...).
- * Asynchronous. Errors: KQ_ERR_ARG (NULL, alignment, clip), KQ_ERR_SHAPE. */
+ * Asynchronous. Errors: KQ_ERR_ARG (NULL, alignment, clip), KQ_ERR_SHAPE
+ * (sizes, blocks), KQ_ERR_UNSUPPORTED (a block above 8192), KQ_ERR_WORKSPACE,
+ * KQ_ERR_HIP. */
 kq_status kq_apply_quantized_a4(const uint32_t* packed, const float* scale, const float* zero,
                                 const float* s_x, const float* s_g, const int8_t* sign_in,
                                 const int8_t* sign_out, int64_t blk_in, int64_t blk_out,
