@@ -463,3 +463,25 @@ def test_allocation_matches_brute_force():
         n = spec_n if trial % 2 == 0 else list(rng.integers(1, 50, 7))
         avg = [2.5, 2.2, 3.0, 3.7][trial % 4]
         assert oracle.allocate_bits(s, n, (2, 3, 4), avg) == _brute_force_alloc(s, n, (2, 3, 4), avg)
+
+
+@pytest.mark.parametrize("bits,block", [(2, 128), (3, 64), (4, 256)])
+def test_folded_sweep_equals_literal_recursion(bits, block):
+    """With one grid per channel (taken from W0), the sweep with the literal
+    drift term W0_p P_{p, >p} added after each column equals the plain GPTQ
+    sweep (P = 0) of the folded matrix W0 + W0 P: P is strictly upper and W0
+    is constant, so the added terms sum to W0 P before any column is reached."""
+    rng = np.random.default_rng(bits * 100 + block)
+    n_tok, d_in, d_out = 600, 256, 24
+    x = rng.standard_normal((n_tok, d_in)) * np.exp(rng.standard_normal(d_in))
+    xq = x + 0.05 * rng.standard_normal((n_tok, d_in))
+    HX, D, _ = oracle.covariances(x.astype(np.float32), xq.astype(np.float32), None)
+    U = oracle.inv_factor(HX, 0.01)
+    P = oracle.form_p(D, U)
+    assert np.all(np.tril(P) == 0)
+    W0 = 0.02 * rng.standard_normal((d_out, d_in))
+    g = oracle.grid_fp32(W0.astype(np.float32), bits)
+    lit = oracle.sweep(W0, U, P, bits, 0, block, grid0=g)
+    fold = oracle.sweep(W0 + W0 @ P, U, None, bits, 0, block, grid0=g)
+    np.testing.assert_array_equal(lit["codes"], fold["codes"])
+    np.testing.assert_allclose(lit["what"], fold["what"], rtol=0, atol=1e-12)
