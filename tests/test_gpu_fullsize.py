@@ -101,7 +101,9 @@ def run(request):
     torch.cuda.empty_cache()
 
 
-def _channels(d, rng, n=128, first=16):
+def _channels(d, rng, n=272, first=16):
+    """n sampled channels (the first `first`, the outliers, always among them):
+    n^2 - n = 73712 off-diagonal entries per covariance at n = 272."""
     c = np.concatenate([np.arange(min(first, d)), rng.choice(np.arange(first, d), n - first,
                                                               replace=False)])
     return np.sort(c)
