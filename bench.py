@@ -51,10 +51,12 @@ def stage_costs(spec):
     cov_flops = n * (n + 1) * N + 2 * n * n * N + m * (m + 1) * N
     # BiIP: two single-side passes (read + write fp32) over W, H_X, D, H_G, plus one read of W for norms
     biip_bytes = 16 * (m * n + 2 * n * n + m * m) + 4 * m * n
+    # its floor: every element of W, H_X, D, H_G read once and written once
+    biip_min_bytes = 8 * (m * n + 2 * n * n + m * m)
     chol_flops = 2 * n ** 3 / 3                     # Cholesky n^3/3 + triangular inverse n^3/3
     solve_flops = 2 * n ** 3 / 3 + 2 * m * n * n    # P formation + fold W0 P (P strictly upper) + trailing updates
-    return dict(cov_flops=cov_flops, biip_bytes=biip_bytes, chol_flops=chol_flops,
-                solve_flops=solve_flops)
+    return dict(cov_flops=cov_flops, biip_bytes=biip_bytes, biip_min_bytes=biip_min_bytes,
+                chol_flops=chol_flops, solve_flops=solve_flops)
 
 
 def run_gpu(spec, steps, warmup, data):
@@ -420,7 +422,8 @@ def cpu_baseline(spec, data, prefix):
     sample = (f"covariances over the first {prefix} of {spec.n_tok} tokens, time scaled x"
               f"{spec.n_tok // prefix}; BiIP, factor, P and sweep at full size "
               f"(measured {sum(t.values()):.1f} s)")
-    return dict(value=est * 1e3, unit="ms", cores=int(cores), kind="oracle", sample=sample,
+    return dict(value=est * 1e3, unit="ms", cores=int(cores), nproc=os.cpu_count(), kind="oracle",
+                sample=sample,
                 stages_s={k: round(v, 3) for k, v in t.items()})
 
 
@@ -478,6 +481,7 @@ def main():
     }
     stages["cov_frac_bf16"] = round(costs["cov_flops"] / (st["cov"] * 1e-3) / PEAK_BF16, 4)
     stages["biip_frac_hbm"] = round(costs["biip_bytes"] / (st["biip"] * 1e-3) / PEAK_HBM, 4)
+    stages["biip_frac_hbm_read_once"] = round(costs["biip_min_bytes"] / (st["biip"] * 1e-3) / PEAK_HBM, 4)
     stages["chol_frac_fp32"] = round(costs["chol_flops"] / (st["chol"] * 1e-3) / PEAK_FP32_MFMA, 4)
     stages["gptaq_frac_fp32"] = round(costs["solve_flops"] / (st["gptaq"] * 1e-3) / PEAK_FP32_MFMA, 4)
     trailing = None

@@ -28,6 +28,7 @@ def test_cost_model_counts_entries():
         assert c["cov_flops"] == 2 * N * (lower(n) + n * n + lower(m))
         passes = 2
         assert c["biip_bytes"] == passes * 8 * (m * n + n * n + n * n + m * m) + 4 * m * n
+        assert c["biip_min_bytes"] == 8 * (m * n + n * n + n * n + m * m)
 
 
 def test_cost_model_at_the_bench_layer():
