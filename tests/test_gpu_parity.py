@@ -43,7 +43,10 @@ def test_cov_f32_config0():
     assert rel_fro(host(HG), oHG) < 1e-5
 
 
-@pytest.mark.parametrize("n_tok,d_in,d_out", [(1000, 264, 512), (4096, 512, 256), (64, 256, 8)])
+# ragged tiles and token tails; one token; a tail only (no full 32-token
+# stage); one full stage plus one token; the minimum width of 8 channels
+@pytest.mark.parametrize("n_tok,d_in,d_out", [(1000, 264, 512), (4096, 512, 256), (64, 256, 8),
+                                              (1, 8, 8), (31, 264, 24), (33, 8, 520)])
 def test_cov_bf16_ragged(n_tok, d_in, d_out):
     rng = np.random.default_rng(n_tok + d_in)
     sig = np.exp(rng.standard_normal(d_in)).astype(np.float32)
@@ -61,6 +64,24 @@ def test_cov_bf16_ragged(n_tok, d_in, d_out):
     # symmetric outputs are exactly mirrored
     np.testing.assert_array_equal(host(HX), host(HX).T)
     np.testing.assert_array_equal(host(HG), host(HG).T)
+
+
+@pytest.mark.parametrize("want", [("HX",), ("D",), ("HG",), ("HX", "HG"), ("D", "HG")])
+def test_cov_bf16_output_subsets(want):
+    """Any subset of the three outputs may be requested (the others are NULL
+    and skipped); each requested one matches the oracle."""
+    rng = np.random.default_rng(len(want) * 7 + len(want[0]))
+    n_tok, d_in, d_out = 700, 264, 136
+    X = _bf16(rng, (n_tok, d_in), 1.0)
+    Xq = _bf16(rng, (n_tok, d_in), 1.0)
+    G = _bf16(rng, (n_tok, d_out), 2.0)
+    HX, D, HG = kq.kq_accumulate_cov(dev(X), dev(Xq), dev(G), 1.0 / n_tok, 0.0, want=want)
+    oHX, oD, oHG = oracle.covariances(X, Xq, G)
+    for name, got, ref in (("HX", HX, oHX), ("D", D, oD), ("HG", HG, oHG)):
+        if name in want:
+            assert rel_fro(host(got), ref) < 1e-4, name
+        else:
+            assert got is None, name
 
 
 def test_cov_bf16_chunked_beta():
