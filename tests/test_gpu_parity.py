@@ -126,6 +126,36 @@ def test_biip_against_oracle(d_out, d_in, bo, bi):
     assert rel_fro(host(tHG), HG2) < 1e-5
 
 
+@pytest.mark.parametrize("d_out,d_in,bo,bi", [(8, 8, 0, 0), (24, 40, 8, 8), (100, 36, 4, 4)])
+def test_biip_small_and_degenerate(d_out, d_in, bo, bi):
+    """Small shapes and blocks, with a zero column and a zero row in W and
+    a zero diagonal entry of H_X and of H_G: their scales are 1 (reading R3)
+    and everything else matches the oracle."""
+    rng = np.random.default_rng(d_out * d_in)
+    HX = spd(rng, d_in, 1e2)
+    HX[2, :] = 0.0
+    HX[:, 2] = 0.0
+    HG = spd(rng, d_out, 1e2)
+    HG[1, :] = 0.0
+    HG[:, 1] = 0.0
+    D = 0.01 * rng.standard_normal((d_in, d_in))
+    W = 0.02 * rng.standard_normal((d_out, d_in))
+    W[:, 5] = 0.0
+    W[3, :] = 0.0
+    si = rng.choice([-1, 1], d_in).astype(np.int8)
+    so = rng.choice([-1, 1], d_out).astype(np.int8)
+    f32 = lambda a: np.asarray(a, np.float32)
+    tW, tHX, tD, tHG = dev(f32(W)), dev(f32(HX)), dev(f32(D)), dev(f32(HG))
+    s_x, s_g = kq.kq_biip(tW, tHX, tD, tHG, dev(si), dev(so), bi, bo)
+    W2, HX2, D2, HG2, ox, og = oracle.biip(f32(W), f32(HX), f32(D), f32(HG), si, so, bi, bo)
+    sx, sg = host(s_x), host(s_g)
+    assert sx[2] == 1.0 and sx[5] == 1.0 and sg[1] == 1.0 and sg[3] == 1.0
+    assert rel_fro(sx, ox) < 1e-6
+    assert rel_fro(sg, og) < 1e-6
+    for got, ref in ((tW, W2), (tHX, HX2), (tD, D2), (tHG, HG2)):
+        assert rel_fro(host(got), ref) < 1e-5
+
+
 # ------------------------------------------------------------------ stage 5
 
 
