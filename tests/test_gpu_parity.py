@@ -230,7 +230,8 @@ def _sweep_case(d_out, n, bits, group, with_d, seed):
 
 @pytest.mark.parametrize("d_out,n,bits,group,with_d", [
     (64, 256, 2, 0, False), (200, 512, 2, 0, True), (256, 384, 3, 128, True),
-    (96, 256, 4, 128, False), (33, 128, 2, 0, True)])
+    (96, 256, 4, 128, False), (33, 128, 2, 0, True),
+    (64, 256, 8, 0, True), (40, 128, 1, 0, False), (1, 256, 2, 128, True)])
 def test_gptaq_forced_replay(d_out, n, bits, group, with_d):
     W0, codes, scale, zero, What, ref = _sweep_case(d_out, n, bits, group, with_d, d_out + n)
     rep = code_report(ref, codes.size)
