@@ -99,9 +99,9 @@ const char* kq_version(void);
  *          trailing update, the sweep's largest GEMM (d_out x (d_in - 512)
  *          x 512; none if d_in <= 512).
  *          KQ_OP_APPLY_QUANTIZED: the product with the packed codes (one
- *          launch per 2 vectors of the batch on the matrix-core path of
- *          2-bit per-channel codes, per 4 otherwise; the two transforms lie
- *          outside the bracket).
+ *          launch per 4 vectors of the batch; the two transforms, and the
+ *          sum of the matrix-core path's partial planes in the output
+ *          transform, lie outside the bracket).
  *          KQ_OP_APPLY_QUANTIZED_A4: the integer product (one launch for
  *          the whole batch; the transforms and the input quantization lie
  *          outside).

@@ -203,11 +203,14 @@ __global__ __launch_bounds__(1024) void transform_in_kernel(const float* __restr
 }
 
 // y[b][r0 + e] = gain * sign_out / s_g * (H_blk y1[b])[r0 + e]
+// where y1 is the sum of `planes` partial planes, `plane` floats apart,
+// added in plane order
 template <int LGB>
 __global__ __launch_bounds__(1024) void transform_out_kernel(const float* __restrict__ y1,
                                                              int64_t d_out, int lgL, int lgb,
                                                              const int8_t* __restrict__ so,
                                                              const float* __restrict__ s_g, float gain,
+                                                             int planes, int64_t plane,
                                                              float* __restrict__ y) {
   __shared__ float s[TCHP];
   const int L = 1 << lgL;
@@ -216,7 +219,14 @@ __global__ __launch_bounds__(1024) void transform_out_kernel(const float* __rest
   const int64_t r0 = int64_t(blockIdx.x % per_row) << lgL;
   const float* src = y1 + b * d_out + r0;
   for (int e = 4 * threadIdx.x; e < L; e += 4 * blockDim.x) {
-    const float4 v = *reinterpret_cast<const float4*>(src + e);
+    float4 v = *reinterpret_cast<const float4*>(src + e);
+    for (int p = 1; p < planes; ++p) {
+      const float4 u = *reinterpret_cast<const float4*>(src + p * plane + e);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
     s[padi(e)] = v.x;
     s[padi(e + 1)] = v.y;
     s[padi(e + 2)] = v.z;
@@ -716,129 +726,205 @@ __global__ __launch_bounds__(1024) void transform_in_mx_kernel(
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
-// y1[b0 + v][rows] = scale (W^' x2 - zero sum x2) for v < NV, rows
-// blockIdx.x * rpw .. + rpw - 1 (a multiple of 16). K ranges of RK
-// super-steps; wave w takes ranges w, w + waves, ... and holds a range's B
-// operands in registers while it streams the rows.
-template <int NV, int RK>
+// 16 bytes per lane from global memory straight into LDS: lane i's land at
+// lds_addr + 16 i. Complete once vmcnt has counted the load down.
+__device__ inline void a4_dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void a4_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Sum over the 16 lanes of a DPP row, left in every lane of the row: lane
+// pairs (quad_perm 1 0 3 2), then quads (2 3 0 1), then the mirrored half
+// row adds the other quad of its 8 lanes and the mirrored row the other 8.
+__device__ inline float row16_sum(float t) {
+  t += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t), 0xB1, 0xF, 0xF, false));
+  t += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t), 0x4E, 0xF, 0xF, false));
+  t += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t), 0x141, 0xF, 0xF, false));
+  t += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t), 0x140, 0xF, 0xF, false));
+  return t;
+}
+
+// An empty use of a wave's B operands, ordered with the DMA asm around it.
+__device__ inline void mx_hold_b(const v8i_t (&b)[4], uint32_t sc) {
+  asm volatile("" : : "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(sc));
+}
+
+// Partial products of the matrix-core path. Workgroup (row block rb, K
+// group g) covers rows rb * rpw .. + rpw - 1 and super-steps g * nw .. +
+// nw - 1, one per wave: y1p[g][b0 + v][row] = scale (sum over those
+// columns of W^' x2, less zero sum x2 in group 0) for v < NV, so the K
+// groups' planes add up to y1. A 16-column B tile holds the digit columns of
+// two vectors; NV > 2 takes a second tile, which shares every decoded A
+// operand. A wave loads its super-step's B operands once and streams its
+// 16-row code tiles through a private LDS ring of `depth` stages (one
+// 16-row tile, 2 KB, per stage), filled by DMA `depth - 1` tiles ahead.
+constexpr int MX_STAGE = 2048;
+template <int NV>
 __global__ __launch_bounds__(1024) void qmatvec_mx_kernel(
     const uint32_t* __restrict__ packed, int rw, const float* __restrict__ scale,
     const float* __restrict__ zero, const uint8_t* __restrict__ xb, const uint32_t* __restrict__ xs,
-    const float* __restrict__ xsum, int nparts, int64_t nss, int64_t d_out, int nkr, int rpw, int b0,
-    int64_t batch, float* __restrict__ y1) {
-  __shared__ float red[16][64];
+    const float* __restrict__ xsum, int nparts, int64_t nss, int64_t d_out, int kgroups, int rpw,
+    int depth, int b0, int64_t batch, float* __restrict__ y1p) {
+  constexpr int NT = (NV + 1) / 2;  // B tiles
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  const int64_t rbeg = int64_t(blockIdx.x) * rpw;
+  const int g = blockIdx.x % kgroups;
+  const int64_t rbeg = int64_t(blockIdx.x / kgroups) * rpw;
   const int nrows = int(min(int64_t(rpw), d_out - rbeg));
-  for (int i = lane; i < 64; i += 64) red[w][i] = 0.f;
+  const int64_t S = int64_t(g) * nw + w;  // this wave's super-step, < nss
+  float* red = reinterpret_cast<float*>(lds + size_t(nw) * depth * MX_STAGE);  // [nw][rpw][NV]
+  const uint32_t ring = uint32_t(reinterpret_cast<uintptr_t>(lds)) + uint32_t(w * depth * MX_STAGE);
   const int n = lane & 15, G = lane >> 4;
-  const bool bcol = n < MX_DIG * NV;  // columns past the vectors' digits stay zero
-  const int vcol = bcol ? n / MX_DIG : 0, lcol = n % MX_DIG;
-  // The wave's items: its K ranges (w, w + nw, ...) times the 16-row tiles,
-  // ranges outer. The codes of item it + 1 load while item it computes; a
-  // range's B operands load when the range starts.
-  const int ntile = (nrows + 15) / 16;
-  const int items = ((nkr - 1 - w) / nw + 1) * ntile;
-  auto load_a = [&](int it, uint4 (&dst)[RK][2]) {
-    const int kr = w + (it / ntile) * nw, t0 = (it % ntile) * 16;
-    const int64_t row = rbeg + min(t0 + n, nrows - 1);  // past the end: the last row, not stored
+  const int lcol = n % MX_DIG;
+  // tile tt, column n: digit lcol of vector 2 tt + n / 6; columns past the
+  // vectors' digits stay zero
+  bool bcol[NT];
+  int vcol[NT];
 #pragma unroll
-    for (int t = 0; t < RK; ++t) {
-      const int64_t S = min(int64_t(kr) * RK + t, nss - 1);  // past the end: unused
-      const uint4* ap = reinterpret_cast<const uint4*>(packed + row * rw + S * (MX_SS / 16) + G * 4);
-      dst[t][0] = ap[0];  // codes 64 G .. 64 G + 63 of the super-step
-      dst[t][1] = ap[4];  // codes 256 + 64 G .. 256 + 64 G + 63
+  for (int tt = 0; tt < NT; ++tt) {
+    bcol[tt] = n < MX_DIG * min(2, NV - 2 * tt);
+    vcol[tt] = bcol[tt] ? 2 * tt + n / MX_DIG : 0;
+  }
+  // B operands first: they are in flight before any DMA
+  v8i_t bop[NT][4];
+  uint32_t bsc[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const uint8_t* bp = xb + ((b0 + vcol[tt]) * nss + S) * MX_BYTES;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4* p = reinterpret_cast<const uint4*>(bp + ((q * 4 + G) * MX_DIG + lcol) * 32);
+      const uint4 lo = bcol[tt] ? p[0] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 hi = bcol[tt] ? p[1] : make_uint4(0u, 0u, 0u, 0u);
+      bop[tt][q] = v8i_t{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
     }
+    bsc[tt] = bcol[tt] ? xs[((b0 + vcol[tt]) * nss + S) * MX_SCALES + G * MX_DIG + lcol] : 0u;
+  }
+  // tile t of the codes: rows rbeg + 16 t + n (past the end: the last row,
+  // not stored), this lane's 16 bytes of each 64-byte half of the super-step
+  const int items = (nrows + 15) / 16;
+  const uint8_t* arow = reinterpret_cast<const uint8_t*>(packed + S * (MX_SS / 16) + G * 4);
+  auto issue = [&](int t) {
+    const int64_t row = rbeg + min(16 * t + n, nrows - 1);
+    const uint8_t* src = arow + row * int64_t(rw) * 4;
+    const uint32_t dst = ring + uint32_t((t % depth) * MX_STAGE);
+    a4_dma16(src, dst);
+    a4_dma16(src + 64, dst + 1024);
   };
-  v8i_t bop[RK][4];
-  uint32_t bsc[RK];
-  uint4 an[RK][2];
-  load_a(0, an);
-  int cur_kr = -1;
+  issue(0);
+  a4_wait_vm<0>();  // B and tile 0
+  // B is used here, so the compiler's own wait for it falls at this point,
+  // before any later DMA is in flight
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) mx_hold_b(bop[tt], bsc[tt]);
+  int issued = 1;
   for (int it = 0; it < items; ++it) {
-    const int kr = w + (it / ntile) * nw, t0 = (it % ntile) * 16;
-    if (kr != cur_kr) {
-      cur_kr = kr;
-#pragma unroll
-      for (int t = 0; t < RK; ++t) {
-        const int64_t S = int64_t(kr) * RK + t;
-        const bool ok = bcol && S < nss;
-        const uint8_t* bp = xb + ((b0 + vcol) * nss + (ok ? S : 0)) * MX_BYTES;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4* p = reinterpret_cast<const uint4*>(bp + ((q * 4 + G) * MX_DIG + lcol) * 32);
-          const uint4 lo = ok ? p[0] : make_uint4(0u, 0u, 0u, 0u);
-          const uint4 hi = ok ? p[1] : make_uint4(0u, 0u, 0u, 0u);
-          bop[t][q] = v8i_t{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-        }
-        bsc[t] = ok ? xs[((b0 + vcol) * nss + S) * MX_SCALES + G * MX_DIG + lcol] : 0u;
+    if (it > 0) {
+      // tile it done; the tiles after it may stay in flight (two DMAs each)
+      switch (issued - it - 1) {
+        case 0: a4_wait_vm<0>(); break;
+        case 1: a4_wait_vm<2>(); break;
+        case 2: a4_wait_vm<4>(); break;
+        case 3: a4_wait_vm<6>(); break;
+        case 4: a4_wait_vm<8>(); break;
+        case 5: a4_wait_vm<10>(); break;
+        case 6: a4_wait_vm<12>(); break;
+        default: a4_wait_vm<14>(); break;
       }
     }
-    uint4 ac[RK][2];
+    // refill: the slot of tile it - 1 is free, its reads are done
+    while (issued < items && issued < it + depth) issue(issued++);
+    const uint8_t* st = lds + size_t(w * depth + it % depth) * MX_STAGE;
+    const uint4 lo = *reinterpret_cast<const uint4*>(st + lane * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(st + 1024 + lane * 16);
+    const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    v4f_t acc[NT];
 #pragma unroll
-    for (int t = 0; t < RK; ++t) {
-      ac[t][0] = an[t][0];
-      ac[t][1] = an[t][1];
-    }
-    if (it + 1 < items) load_a(it + 1, an);
-    v4f_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = v4f_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < RK; ++t) {
-      if (int64_t(kr) * RK + t >= nss) break;
-      const uint32_t wd[8] = {ac[t][0].x, ac[t][0].y, ac[t][0].z, ac[t][0].w,
-                              ac[t][1].x, ac[t][1].y, ac[t][1].z, ac[t][1].w};
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x0 = wd[2 * q], x1 = wd[2 * q + 1];
+      const v8i_t aop = {int(x0 & 0x33333333u), int((x0 >> 2) & 0x33333333u),
+                         int(x1 & 0x33333333u), int((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t x0 = wd[2 * q], x1 = wd[2 * q + 1];
-        const v8i_t aop = {int(x0 & 0x33333333u), int((x0 >> 2) & 0x33333333u),
-                           int(x1 & 0x33333333u), int((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
-        if (q == 0) acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][0], acc, 4, 0, 0, 0x7f7f7f7f, 0, int(bsc[t]));
-        if (q == 1) acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][1], acc, 4, 0, 0, 0x7f7f7f7f, 1, int(bsc[t]));
-        if (q == 2) acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][2], acc, 4, 0, 0, 0x7f7f7f7f, 2, int(bsc[t]));
-        if (q == 3) acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[t][3], acc, 4, 0, 0, 0x7f7f7f7f, 3, int(bsc[t]));
+      for (int tt = 0; tt < NT; ++tt) {
+        const int sc = int(bsc[tt]);
+        if (q == 0) acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[tt][0], acc[tt], 4, 0, 0, 0x7f7f7f7f, 0, sc);
+        if (q == 1) acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[tt][1], acc[tt], 4, 0, 0, 0x7f7f7f7f, 1, sc);
+        if (q == 2) acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[tt][2], acc[tt], 4, 0, 0, 0x7f7f7f7f, 2, sc);
+        if (q == 3) acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[tt][3], acc[tt], 4, 0, 0, 0x7f7f7f7f, 3, sc);
       }
     }
-    // acc[i] = C[4 G + i][n]: add the digit columns of each vector
+    // acc[tt][i] = C[4 G + i][n] of B tile tt: add the digit columns of each vector
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float t = (bcol && vcol == v) ? acc[i] : 0.f;
-        t += __shfl_xor(t, 8);
-        t += __shfl_xor(t, 4);
-        t += __shfl_xor(t, 2);
-        t += __shfl_xor(t, 1);
-        const int r = t0 + 4 * G + i;
-        if (n == 0 && r < nrows) red[w][r * NV + v] += t;
+        const int tt = v / 2;
+        const float t = row16_sum((bcol[tt] && vcol[tt] == v) ? acc[tt][i] : 0.f);
+        const int r = 16 * it + 4 * G + i;
+        if (n == 0 && r < nrows) red[(w * rpw + r) * NV + v] = t;
       }
   }
   __syncthreads();
+  float* dst = y1p + int64_t(g) * batch * d_out;
   for (int i = threadIdx.x; i < nrows * NV; i += blockDim.x) {
     const int r = i / NV, v = i % NV;
     float acc = 0.f;
-    for (int u = 0; u < nw; ++u) acc += red[u][i];
-    float xs_sum = 0.f;
-    for (int pp = 0; pp < nparts; ++pp) xs_sum += xsum[(b0 + v) * nparts + pp];
+    for (int u = 0; u < nw; ++u) acc += red[u * rpw * NV + i];
     const int64_t row = rbeg + r;
-    y1[(b0 + v) * d_out + row] = scale[row] * (acc - zero[row] * xs_sum);
+    if (g == 0) {
+      float xs_sum = 0.f;
+      for (int pp = 0; pp < nparts; ++pp) xs_sum += xsum[(b0 + v) * nparts + pp];
+      acc -= zero[row] * xs_sum;
+    }
+    dst[(b0 + v) * d_out + row] = scale[row] * acc;
   }
 }
 
+// Launch shape of the matrix-core product: K groups of at most 16
+// super-steps (one per wave), then rows per workgroup (16 .. 128) as many
+// as still leave >= 256 workgroups, then the ring depth that the LDS holds.
+struct MxPlan {
+  int kgroups, nw, rpw;
+};
+MxPlan mx_plan(int64_t d_out, int64_t d_in) {
+  const int64_t nss = d_in / MX_SS;
+  int64_t kg = 1;
+  while (nss % kg || nss / kg > 16) ++kg;
+  int rpw = 128;
+  while (rpw > 16 && cdiv(d_out, rpw) * kg < 256) rpw >>= 1;
+  return MxPlan{int(kg), int(nss / kg), rpw};
+}
+int64_t mx_planes(int64_t d_in) { return d_in % MX_SS == 0 ? mx_plan(16, d_in).kgroups : 1; }
+
+constexpr size_t MX_LDS = 160 * 1024;
 template <int NV>
-void launch_qmatvec_mx(const uint32_t* packed, int64_t rw, const float* scale, const float* zero,
-                       const uint8_t* xb, const uint32_t* xs, const float* xsum, int nparts,
-                       int64_t nss, int64_t d_out, int b0, int64_t batch, float* y1, hipStream_t s) {
-  constexpr int RK = 2;
-  const int nkr = int(cdiv(nss, RK));
-  // waves per workgroup: the largest divisor of the range count up to 16
-  int nw = std::min(nkr, 16);
-  while (nkr % nw) --nw;
-  // rows per workgroup: 32 (two 16-row tiles) unless that leaves < 256 workgroups
-  const int rpw = cdiv(d_out, 32) >= 256 ? 32 : 16;
-  qmatvec_mx_kernel<NV, RK><<<unsigned(cdiv(d_out, rpw)), 64 * nw, 0, s>>>(
-      packed, int(rw), scale, zero, xb, xs, xsum, nparts, nss, d_out, nkr, rpw, b0, batch, y1);
+kq_status launch_qmatvec_mx(const uint32_t* packed, int64_t rw, const float* scale, const float* zero,
+                            const uint8_t* xb, const uint32_t* xs, const float* xsum, int nparts,
+                            int64_t nss, int64_t d_out, int b0, int64_t batch, float* y1p, hipStream_t s) {
+  const MxPlan pl = mx_plan(d_out, nss * MX_SS);
+  const size_t red_bytes = size_t(pl.nw) * pl.rpw * NV * sizeof(float);
+  const int ntile = pl.rpw / 16;
+  const int fit = int((MX_LDS - red_bytes) / (size_t(pl.nw) * MX_STAGE));
+  const int depth = std::max(1, std::min({8, ntile, fit}));
+  const size_t bytes = size_t(pl.nw) * depth * MX_STAGE + red_bytes;
+  KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(qmatvec_mx_kernel<NV>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes)));
+  qmatvec_mx_kernel<NV><<<unsigned(cdiv(d_out, pl.rpw) * pl.kgroups), 64 * pl.nw, bytes, s>>>(
+      packed, int(rw), scale, zero, xb, xs, xsum, nparts, nss, d_out, pl.kgroups, pl.rpw, depth, b0,
+      batch, y1p);
+  KQ_HIP(hipGetLastError());
+  return KQ_OK;
 }
 
 kq_status run_mx(const uint32_t* packed, int64_t rw, const float* scale, const float* zero,
@@ -854,12 +940,17 @@ kq_status run_mx(const uint32_t* packed, int64_t rw, const float* scale, const f
   });
   KQ_HIP(hipGetLastError());
   KQ_TRY(mark_kernel(KQ_OP_APPLY_QUANTIZED, 0, s));
-  for (int64_t b0 = 0; b0 < batch; b0 += 2) {
-    if (batch - b0 >= 2)
-      launch_qmatvec_mx<2>(packed, rw, scale, zero, xb, xs, xsum, int(nparts), nss, d_out, int(b0), batch, y1, s);
+  for (int64_t b0 = 0; b0 < batch; b0 += 4) {
+    const int64_t left = batch - b0;
+    const int b = int(b0);
+    if (left >= 4)
+      KQ_TRY(launch_qmatvec_mx<4>(packed, rw, scale, zero, xb, xs, xsum, int(nparts), nss, d_out, b, batch, y1, s));
+    else if (left == 3)
+      KQ_TRY(launch_qmatvec_mx<3>(packed, rw, scale, zero, xb, xs, xsum, int(nparts), nss, d_out, b, batch, y1, s));
+    else if (left == 2)
+      KQ_TRY(launch_qmatvec_mx<2>(packed, rw, scale, zero, xb, xs, xsum, int(nparts), nss, d_out, b, batch, y1, s));
     else
-      launch_qmatvec_mx<1>(packed, rw, scale, zero, xb, xs, xsum, int(nparts), nss, d_out, int(b0), batch, y1, s);
-    KQ_HIP(hipGetLastError());
+      KQ_TRY(launch_qmatvec_mx<1>(packed, rw, scale, zero, xb, xs, xsum, int(nparts), nss, d_out, b, batch, y1, s));
   }
   return mark_kernel(KQ_OP_APPLY_QUANTIZED, 1, s);
 }
@@ -1171,18 +1262,6 @@ constexpr int QG_NST = 3;                           // ring depth
 constexpr int QG_DMA = 12;                          // DMA instructions per wave and stage
 constexpr int QG_PRE = 8;                           // code-sum partials each thread preloads
 
-__device__ inline void a4_dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ inline void a4_wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
 __global__ __launch_bounds__(256) void qgemm_a4_kernel(
     const uint32_t* __restrict__ packed, int rw, const float* __restrict__ scale,
     const float* __restrict__ zero, const uint8_t* __restrict__ xa, const float* __restrict__ ascale,
@@ -1365,7 +1444,7 @@ size_t apply_ws_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
     a2.take<float>(size_t(batch) * (d_in / MX_SS));                 // sums of x2
   }
   Arena ar{nullptr, 0, std::max(a1.used, a2.used)};
-  ar.take<float>(size_t(batch) * d_out);  // y1
+  ar.take<float>(size_t(batch) * d_out * mx_planes(d_in));  // y1, or its K-group planes
   return ar.used;
 }
 
@@ -1374,9 +1453,11 @@ kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const 
                     const int8_t* so, int64_t bi, int64_t bo, const float* x, int64_t batch,
                     int64_t d_out, int64_t d_in, float* y, Arena& ws, hipStream_t s) {
   const int64_t rw = packed_row_words(d_in, bits);
-  const size_t front = apply_ws_bytes(d_out, d_in, batch) - size_t(batch) * d_out * sizeof(float);
+  const int planes = use_mx(bits, group, d_in) ? int(mx_planes(d_in)) : 1;
+  const size_t y1_floats = size_t(batch) * d_out * mx_planes(d_in);
+  const size_t front = apply_ws_bytes(d_out, d_in, batch) - y1_floats * sizeof(float);
   char* base = ws.take<char>(front);
-  float* y1 = ws.take<float>(size_t(batch) * d_out);
+  float* y1 = ws.take<float>(y1_floats);
   if (!base || !y1) return fail(KQ_ERR_WORKSPACE, "apply_quantized: workspace too small");
   if (use_mx(bits, group, d_in)) {
     Arena fa{base, front, 0};
@@ -1400,7 +1481,8 @@ kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const 
   const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));
   with_lgb(ilog2(bo), [&](auto C) {
     transform_out_kernel<decltype(C)::value><<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(
-        y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), y);
+        y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), planes,
+        batch * d_out, y);
   });
   KQ_HIP(hipGetLastError());
   return KQ_OK;
@@ -1481,7 +1563,8 @@ kq_status apply_a4_run(const uint32_t* packed, const float* scale, const float* 
   const unsigned tout = unsigned(std::max<int64_t>(64, std::min<int64_t>(1024, Lo / 4)));
   with_lgb(ilog2(bo), [&](auto C) {
     transform_out_kernel<decltype(C)::value><<<unsigned(batch * (d_out / Lo)), tout, 0, s>>>(
-        y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), y);
+        y1, d_out, ilog2(Lo), ilog2(bo), so, s_g, float(1.0 / std::sqrt(double(bo))), 1,
+        batch * d_out, y);
   });
   KQ_HIP(hipGetLastError());
   return KQ_OK;

@@ -97,6 +97,36 @@ def test_apply_ragged(bits, group, batch):
     assert rel_fro(got, want) < 1e-5
 
 
+@pytest.mark.parametrize("batch", [3, 4, 5, 6, 7, 9])
+def test_apply_matrix_core_launch_splits(batch):
+    # 2-bit per-row codes with d_in a multiple of 512 take the matrix-core
+    # product: one launch per four vectors, then one for the 1-3 left over
+    # (batch 9 = 4 + 4 + 1). 260 rows end in a partial 16-row tile; 1536
+    # columns are 3 super-steps, so the two-per-range launches end in a
+    # ragged range
+    rng = np.random.default_rng(500 + batch)
+    c = _case(260, 1536, 2, 0, rng)
+    x = rng.standard_normal((batch, 1536)).astype(np.float32)
+    x[batch // 2] *= 1e-3  # vectors of different magnitudes share a launch
+    got, want = _run(*c, 2, 0, x, bi=512, bo=0)
+    for v in range(batch):
+        assert rel_fro(got[v:v + 1], want[v:v + 1]) < 1e-5, v
+
+
+@pytest.mark.parametrize("d_out,d_in,batch", [(4100, 8704, 5), (4100, 8704, 1), (1028, 17408, 3)])
+def test_apply_matrix_core_k_groups(d_out, d_in, batch):
+    # 17 and 34 super-steps split into 17 groups of columns, each group's
+    # partial product in its own plane; 4100 rows take 128-row workgroups
+    # (a wave streams 8 row tiles through its ring, the last workgroup 4
+    # rows), 1028 rows 64-row workgroups (the last 4 rows)
+    rng = np.random.default_rng(d_in + batch)
+    c = _case(d_out, d_in, 2, 0, rng)
+    x = rng.standard_normal((batch, d_in)).astype(np.float32)
+    got, want = _run(*c, 2, 0, x)
+    for v in range(batch):
+        assert rel_fro(got[v:v + 1], want[v:v + 1]) < 1e-5, v
+
+
 @pytest.mark.parametrize("bits", [2, 3, 8])
 def test_apply_dynamic_range(bits):
     # Hadamard blocks of 32 keep every 32-column chunk of the transformed
