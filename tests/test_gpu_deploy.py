@@ -21,6 +21,7 @@ if have_gpu():
     import torch
 
     import post_weight_quantization_amd as kq
+    import post_weight_quantization_amd._native as N
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
@@ -125,6 +126,25 @@ def test_apply_matrix_core_k_groups(d_out, d_in, batch):
     got, want = _run(*c, 2, 0, x)
     for v in range(batch):
         assert rel_fro(got[v:v + 1], want[v:v + 1]) < 1e-5, v
+
+
+def test_apply_matrix_core_workspace_reuse():
+    # one workspace, sized for 6 vectors, serves a 6-vector call and then a
+    # 2-vector call: the K groups' partial planes are laid out by the
+    # call's own batch, and every entry the second call reads is its own
+    d_out, d_in = 4100, 8704
+    rng = np.random.default_rng(91)
+    codes, scale, zero, s_x, s_g, si, so = _case(d_out, d_in, 2, 0, rng)
+    packed = kq.kq_pack_codes(dev(codes), 2)
+    ws = torch.empty(kq.kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED, d_out, d_in, 6), dtype=torch.uint8,
+                     device="cuda")
+    for batch in (6, 2):
+        x = rng.standard_normal((batch, d_in)).astype(np.float32)
+        y = kq.kq_apply_quantized(packed, 2, dev(scale), dev(zero), 0, dev(s_x), dev(s_g), dev(si),
+                                  dev(so), dev(x), ws=ws)
+        want = deploy.infer(x, deploy.pack_codes(codes, 2), 2, scale, zero, 0, s_x, s_g, si, so)
+        for v in range(batch):
+            assert rel_fro(host(y)[v:v + 1], want[v:v + 1]) < 1e-5, (batch, v)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 8])
