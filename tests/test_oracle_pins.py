@@ -423,6 +423,32 @@ def test_grid_golden():
         np.testing.assert_allclose(what[0], case["dequant"], atol=1e-7, err_msg=case["why"])
 
 
+def test_group_grid_golden():
+    """Group grids are taken from the working values when the sweep reaches
+    the group (reading R6), feedback and drift term included; the hand-worked
+    cases differ from grids taken from the original weights."""
+    for case in _load("group_grid.json")["cases"]:
+        W0 = np.array(case["W0"], dtype=np.float64)
+        U = np.array(case["U"], dtype=np.float64)
+        P = None if case["P"] is None else np.array(case["P"], dtype=np.float64)
+        for block in (2, 4):  # lazy and unblocked forms agree
+            res = oracle.sweep(W0, U, P, case["bits"], case["group"], block=block)
+            np.testing.assert_array_equal(res["scale"], np.float32(case["scale"]), err_msg=case["name"])
+            np.testing.assert_array_equal(res["zero"], np.float32(case["zero"]), err_msg=case["name"])
+            np.testing.assert_array_equal(res["codes"], case["codes"], err_msg=case["name"])
+            np.testing.assert_array_equal(res["what"], case["dequant"], err_msg=case["name"])
+        other = np.float32(case["grid_from_W0_would_be"]["scale"])
+        assert np.any(other != np.float32(case["scale"]))
+
+
+def test_cv_in_out_golden():
+    """CV_in runs over the input channels (columns), CV_out over the rows (reading R9)."""
+    for case in _load("cv_in_out.json")["cases"]:
+        cvi, cvo = oracle.cv_in_out(np.array(case["W"]))
+        assert cvi * cvi == pytest.approx(case["cv_in_squared"], rel=1e-12, abs=1e-15), case["why"]
+        assert cvo * cvo == pytest.approx(case["cv_out_squared"], rel=1e-12, abs=1e-15), case["why"]
+
+
 def test_config0_objective_beats_rtn():
     spec = layer_specs(0)[0]
     L = make_layer(spec)
