@@ -183,3 +183,45 @@ def test_apply_a4_validation():
     assert need.value >= 4 * 20 * 1024 + 4 * 20 * 64 + 32 * 1024
     st, _ = call(batch=20, ws_bytes=need.value - 1)
     assert st == N.KQ_ERR_WORKSPACE
+
+
+def test_bindings_reject_wrong_shapes_before_any_launch():
+    """Every binding checks the shape and dtype of each tensor it hands to the
+    library as a raw pointer; a wrong one raises ValueError on the host (these
+    CPU tensors would otherwise be rejected only for not being on the GPU)."""
+    import torch
+
+    from post_weight_quantization_amd import api
+
+    f32, i8, u8 = torch.float32, torch.int8, torch.uint8
+    z = lambda *s, dt=f32: torch.zeros(*s, dtype=dt)
+    cases = [
+        ("HX", lambda: api.kq_accumulate_cov(z(64, 256), z(64, 256), z(64, 128), 1.0, 0.0,
+                                             HX=z(255, 256))),
+        ("G", lambda: api.kq_accumulate_cov(z(64, 256), z(64, 256), z(63, 128), 1.0, 0.0)),
+        ("HG", lambda: api.kq_biip(z(128, 256), z(256, 256), None, z(128, 127), z(256, dt=i8),
+                                   z(128, dt=i8))),
+        ("sign_in", lambda: api.kq_biip(z(128, 256), z(256, 256), None, z(128, 128), z(256, dt=f32),
+                                        z(128, dt=i8))),
+        ("U", lambda: api.kq_cholesky_inv(z(256, 256), 0.01, U=z(128, 256))),
+        ("P", lambda: api.kq_form_p(z(256, 256), z(256, 256), P=z(256, 255))),
+        ("scale", lambda: api.kq_gptaq_quantize(z(64, 256), z(256, 256), None, 3, 128,
+                                                scale=z(64, 1), zero=z(64, 2))),
+        ("codes", lambda: api.kq_gptaq_quantize(z(64, 256), z(256, 256), None, 2,
+                                                codes=z(64, 256, dt=f32))),
+        ("D", lambda: api.kq_gptaq_quantize(z(64, 256), z(256, 256), z(64, 256), 2)),
+        ("HG", lambda: api.kq_layer_objective(z(64, 256), z(64, 256), z(256, 256), None, z(256, 256))),
+        ("U_out", lambda: api.kq_yaqa_quantize(z(64, 256), z(256, 256), z(256, 256), None, 2)),
+        ("packed", lambda: api.kq_apply_quantized(z(64, 4, dt=torch.int32), 2, z(64, 1), z(64, 1), 0,
+                                                  z(256), z(64), z(256, dt=i8), z(64, dt=i8),
+                                                  z(2, 256))),
+        ("scale", lambda: api.kq_apply_quantized(z(64, 24, dt=torch.int32), 3, z(64, 1), z(64, 1), 128,
+                                                 z(256), z(64), z(256, dt=i8), z(64, dt=i8),
+                                                 z(2, 256))),
+        ("packed", lambda: api.kq_pack_codes(z(64, 256, dt=u8), 2, packed=z(64, 15, dt=torch.int32))),
+        ("x", lambda: api.kq_apply_quantized_a4(z(64, 32, dt=torch.int32), z(64), z(64), z(512), z(64),
+                                                z(512, dt=i8), z(64, dt=i8), z(2, 512, dt=torch.float64))),
+    ]
+    for name, call in cases:
+        with pytest.raises(ValueError, match=rf"^{name}: expected"):
+            call()
