@@ -28,6 +28,7 @@ from .kronq import (  # noqa: F401
     biip_scales,
     covariance_diagonals,
     covariances,
+    covariances_chunked,
     cv_in_out,
     damped,
     decode_inputs,
@@ -43,6 +44,7 @@ from .kronq import (  # noqa: F401
     rtn,
     scaled_traces,
     sensitivity,
+    solve_layer,
     sweep,
     sylvester,
 )

@@ -516,6 +516,28 @@ def quantize_layer(X, Xq, G, W, sign_in, sign_out, bits: int, group: int = 0,
     the sweep and of round-to-nearest on the processed problem.
     """
     HX, D, HG = covariances(X, Xq, G, n_total)
+    return solve_layer(HX, D, HG, W, sign_in, sign_out, bits, group, block, damp)
+
+
+def covariances_chunked(token_chunks, n_total: int):
+    """covariances() summed over an iterable of (X, Xq, G) token chunks.
+
+    The covariances are sums over tokens, so a layer with more tokens than a
+    host holds at once in fp64 is accumulated a chunk at a time.
+    """
+    HX = D = HG = None
+    for X, Xq, G in token_chunks:
+        parts = covariances(X, Xq, G, n_total)
+        HX, D, HG = [p if acc is None else (acc if p is None else acc + p)
+                     for acc, p in zip((HX, D, HG), parts)]
+    return HX, D, HG
+
+
+def solve_layer(HX, D, HG, W, sign_in, sign_out, bits: int, group: int = 0,
+                block: int = 128, damp: float = 0.01):
+    """Everything after the covariances: BiIP -> sensitivity -> damped inverse
+    factor -> P -> sweep, with the objective of the sweep and of
+    round-to-nearest on the processed problem (see quantize_layer)."""
     W2, HX2, D2, HG2, s_x, s_g = biip(W, HX, D, HG, sign_in, sign_out)
     tx, tg, s = sensitivity(HX2, HG2)
     U = inv_factor(HX2, damp)

@@ -47,3 +47,19 @@ def code_report(res, n_total):
     mm = res["mismatches"]
     worst = max((m[4] for m in mm), default=0.0)
     return dict(n=len(mm), frac=len(mm) / n_total, worst=worst)
+
+
+def tile_rel_fro(a, b, t: int) -> float:
+    """Largest relative Frobenius error over the t x t tiles of a matrix
+    (rows of t entries for vectors): a wrong tile of small values fails
+    even when larger tiles dominate the whole matrix's norm. Tiles whose
+    reference is zero must match it exactly."""
+    a = np.atleast_2d(np.asarray(a, np.float64))
+    b = np.atleast_2d(np.asarray(b, np.float64))
+    worst = 0.0
+    for i in range(0, b.shape[0], t):
+        for j in range(0, b.shape[1], t):
+            rb = np.linalg.norm(b[i:i + t, j:j + t])
+            ra = np.linalg.norm(a[i:i + t, j:j + t] - b[i:i + t, j:j + t])
+            worst = max(worst, ra / rb if rb > 0 else (0.0 if ra == 0 else np.inf))
+    return float(worst)

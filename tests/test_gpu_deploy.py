@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import deploy
-from tests.gpu_util import dev, have_gpu, host, rel_fro
+from tests.gpu_util import dev, have_gpu, host, rel_fro, tile_rel_fro
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
@@ -166,6 +166,27 @@ def test_apply_dynamic_range(bits):
     assert rel_fro(got2, want2) < 1e-5
 
 
+@pytest.mark.parametrize("bits,group", [(2, 0), (3, 128), (4, 0)])
+def test_apply_one_chunk_per_vector(bits, group):
+    """Each vector holds a single nonzero 32-column chunk of the rotated input
+    (Hadamard blocks of 32), at magnitudes from 1e-6 to 1e6 or zero, so every
+    output of that vector comes from that chunk alone and is checked on its
+    own scale: per vector, and per 32-entry run of outputs."""
+    rng = np.random.default_rng(91 + bits)
+    d_out, d_in = 128, 1024
+    c = _case(d_out, d_in, bits, group, rng)
+    mags = [0.0, 1e-6, 1e-3, 1.0, 1e3, 1e6]
+    chunks = rng.choice(d_in // 32, len(mags), replace=False)
+    x = np.zeros((len(mags), d_in), np.float32)
+    for v, (m, k) in enumerate(zip(mags, chunks)):
+        x[v, 32 * k:32 * k + 32] = m * rng.standard_normal(32)
+    got, want = _run(*c, bits, group, x, bi=32, bo=0)
+    assert np.all(got[0] == 0.0)
+    for v in range(1, len(mags)):
+        assert rel_fro(got[v], want[v]) < 1e-5, (v, mags[v])
+        assert tile_rel_fro(got[v], want[v], 32) < 1e-4, (v, mags[v])
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("d_out,d_in,bits,group", [(4096, 4096, 2, 0), (11008, 4096, 3, 128),
                                                    (8192, 28672, 2, 0)])
@@ -175,5 +196,6 @@ def test_apply_full_size(d_out, d_in, bits, group):
     x = rng.standard_normal((4, d_in)).astype(np.float32)
     got, want = _run(*c, bits, group, x)
     err = rel_fro(got, want)
-    print(f"{d_out}x{d_in} {bits}-bit: rel {err:.3g}")
-    assert err < 1e-5
+    tile = max(tile_rel_fro(got[v], want[v], 256) for v in range(got.shape[0]))
+    print(f"{d_out}x{d_in} {bits}-bit: rel {err:.3g}, worst 256-output run {tile:.3g}")
+    assert err < 1e-5 and tile < 1e-4

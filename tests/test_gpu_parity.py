@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from synth import layer_specs, make_layer
-from tests.gpu_util import code_report, dev, have_gpu, host, rel_fro, spd
+from tests.gpu_util import code_report, dev, have_gpu, host, rel_fro, spd, tile_rel_fro
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
@@ -124,6 +124,9 @@ def test_biip_against_oracle(d_out, d_in, bo, bi):
     assert rel_fro(host(tHX), HX2) < 1e-5
     assert rel_fro(host(tD), D2) < 1e-5
     assert rel_fro(host(tHG), HG2) < 1e-5
+    # tile by tile: a wrong tile of small entries cannot hide behind the large ones
+    for got, ref in ((tW, W2), (tHX, HX2), (tD, D2), (tHG, HG2)):
+        assert tile_rel_fro(host(got), ref, 64) < 1e-4
 
 
 @pytest.mark.parametrize("d_out,d_in,bo,bi", [(8, 8, 0, 0), (24, 40, 8, 8), (100, 36, 4, 4)])
@@ -154,6 +157,7 @@ def test_biip_small_and_degenerate(d_out, d_in, bo, bi):
     assert rel_fro(sg, og) < 1e-6
     for got, ref in ((tW, W2), (tHX, HX2), (tD, D2), (tHG, HG2)):
         assert rel_fro(host(got), ref) < 1e-5
+        assert tile_rel_fro(host(got), ref, 4) < 1e-4
 
 
 # ------------------------------------------------------------------ stage 5

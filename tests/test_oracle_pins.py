@@ -107,6 +107,19 @@ def test_covariances_against_token_loop(bf16):
 # ------------------------------------------------------------------- objective
 
 
+def test_covariances_chunked_equal_whole():
+    """The covariances are sums over tokens: chunking the stream changes nothing."""
+    rng = np.random.default_rng(21)
+    X = _dyadic(rng, (96, 8))
+    Xq = _dyadic(rng, (96, 8))
+    G = _dyadic(rng, (96, 5))
+    whole = oracle.covariances(X, Xq, G)
+    parts = oracle.covariances_chunked(((X[c:c + 40], Xq[c:c + 40], G[c:c + 40])
+                                        for c in range(0, 96, 40)), 96)
+    for w, p in zip(whole, parts):
+        np.testing.assert_allclose(p, w, rtol=1e-13, atol=0)
+
+
 def test_kronecker_vec_identity():
     """tr[H_G dW H_X dW^T] = vec(dW)^T (H_X kron H_G) vec(dW), vec column-major."""
     rng = np.random.default_rng(3)
