@@ -59,7 +59,7 @@ def stage_costs(spec):
                 chol_flops=chol_flops, solve_flops=solve_flops)
 
 
-def run_gpu(spec, steps, warmup, data):
+def run_gpu(spec, steps, warmup, data, extras=True):
     import torch
 
     import post_weight_quantization_amd as kq
@@ -157,9 +157,11 @@ def run_gpu(spec, steps, warmup, data):
     except Exception as e:  # pragma: no cover - reporting only
         print(f"objective check failed: {e}", file=sys.stderr)
         obj_rtn = None
-    inf = run_inference(spec, codes, scale, zero, s_x, s_g, si, so)
-    fb = run_output_feedback(spec, W0p, HX, D, HG, U, obj) if W0p is not None and not spec.group else None
-    cap = run_streaming(spec, X, Xq, G, HX, D, HG, ws)
+    inf = fb = cap = None
+    if extras:
+        inf = run_inference(spec, codes, scale, zero, s_x, s_g, si, so)
+        fb = run_output_feedback(spec, W0p, HX, D, HG, U, obj) if W0p is not None and not spec.group else None
+        cap = run_streaming(spec, X, Xq, G, HX, D, HG, ws)
     return dict(wall_s=wall, stage_ms=stage_ms, cov_kernel_ms=cov_kernel_ms, trail_kernel_ms=trail_kernel_ms,
                 sens=sens, obj=obj,
                 obj_rtn=obj_rtn, inference=inf, streaming=cap, output_feedback=fb)
@@ -168,7 +170,7 @@ def run_gpu(spec, steps, warmup, data):
 def run_output_feedback(spec, W0p, HX, D, HG, U, obj_gptaq, reps=3):
     """The rounding with output-side feedback (generalized LDLQ on H_G' x H_X')
     on the same processed layer: U_out from H_G', the GPTAQ fold as target.
-    Time per call (the call synchronizes), its algorithmic flops, and the
+    Time per call (to the end of its last kernel), its algorithmic flops, and the
     layer objective beside the one-sided sweep's."""
     import torch
 
@@ -196,6 +198,7 @@ def run_output_feedback(spec, W0p, HX, D, HG, U, obj_gptaq, reps=3):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         kq.kq_yaqa_quantize(W, U, Uo, D, spec.bits, ws=ws)
+        torch.cuda.synchronize()
         ts.append(time.perf_counter() - t0)
     ms = 1e3 * float(np.median(ts))
     obj = kq.kq_layer_objective(W0p, W, HX, D, HG)
@@ -381,6 +384,148 @@ def run_inference(spec, codes, scale, zero, s_x, s_g, si, so):
     return out
 
 
+def measure_peaks(reps=3):
+    """The part's own ceilings, measured here (hand-written microbenchmarks in
+    libkq_peaks.so): HBM read-only stream over 4 GiB, copy of 2 GiB, and
+    back-to-back bf16 and fp32 MFMAs on every SIMD. Best of `reps` runs."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "post_weight_quantization_amd", "libkq_peaks.so"))
+    for f in (lib.kqp_read, lib.kqp_copy, lib.kqp_mfma_bf16, lib.kqp_mfma_f32):
+        f.restype = ctypes.c_int
+    lib.kqp_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kqp_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    for f in (lib.kqp_mfma_bf16, lib.kqp_mfma_f32):
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    nb = 4 << 30
+    buf = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty(nb // 8, dtype=torch.float32, device="cuda")
+
+    def best(call, units):
+        t = []
+        for _ in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"peak microbenchmark failed: HIP error {rc}")
+            t.append(a.elapsed_time(b))
+        return units / (min(t[1:]) * 1e-3)
+
+    read = best(lambda: lib.kqp_read(ctypes.c_void_p(buf.data_ptr()), nb, ctypes.c_void_p(sink.data_ptr()), sp), nb)
+    half = nb // 2
+    copy = best(lambda: lib.kqp_copy(ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(dst.data_ptr()), half, sp),
+                2 * half)
+    del buf, dst
+    blocks, it_b, it_f = 1024, 50000, 40000
+    bf16 = best(lambda: lib.kqp_mfma_bf16(blocks, it_b, 0.0078125, ctypes.c_void_p(sink.data_ptr()), sp),
+                blocks * 4 * 8 * it_b * 32768.0)
+    f32 = best(lambda: lib.kqp_mfma_f32(blocks, it_f, 0.0078125, ctypes.c_void_p(sink.data_ptr()), sp),
+               blocks * 4 * 8 * it_f * 4096.0)
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round(read / 1e9, 1), "hbm_copy_gbs": round(copy / 1e9, 1),
+            "bf16_mfma_tflops": round(bf16 / 1e12, 1), "fp32_mfma_tflops": round(f32 / 1e12, 2),
+            "spec": {"hbm_gbs": PEAK_HBM / 1e9, "bf16_mfma_tflops": PEAK_BF16 / 1e12,
+                     "fp32_mfma_tflops": PEAK_FP32_MFMA / 1e12},
+            "how": "read: 4 GiB once; copy: 2 GiB read + 2 GiB written; MFMA: 1024 workgroups of 4 waves, "
+                   "8 independent accumulators per wave, register operands; best of 3 timed runs"}
+
+
+def summarize(spec, g):
+    """Per-stage times, rates and fractions of one leg (published and measured peaks)."""
+    costs = stage_costs(spec)
+    st = g["stage_ms"]
+    stages = {
+        "cov_ms": round(st["cov"], 3),
+        "cov_tflops": round(costs["cov_flops"] / st["cov"] / 1e9, 1),
+        "biip_ms": round(st["biip"], 3),
+        "biip_gbs": round(costs["biip_bytes"] / st["biip"] / 1e6, 1),
+        "sens_ms": round(st["sens"], 3),
+        "chol_ms": round(st["chol"], 3),
+        "chol_tflops": round(costs["chol_flops"] / st["chol"] / 1e9, 2),
+        "gptaq_ms": round(st["gptaq"], 3),
+        "gptaq_tflops": round(costs["solve_flops"] / st["gptaq"] / 1e9, 2),
+        "no_cov_ms": round(sum(v for k, v in st.items() if k != "cov"), 3),
+    }
+    stages["cov_frac_bf16"] = round(costs["cov_flops"] / (st["cov"] * 1e-3) / PEAK_BF16, 4)
+    stages["biip_frac_hbm"] = round(costs["biip_bytes"] / (st["biip"] * 1e-3) / PEAK_HBM, 4)
+    stages["biip_frac_hbm_read_once"] = round(costs["biip_min_bytes"] / (st["biip"] * 1e-3) / PEAK_HBM, 4)
+    stages["chol_frac_fp32"] = round(costs["chol_flops"] / (st["chol"] * 1e-3) / PEAK_FP32_MFMA, 4)
+    stages["gptaq_frac_fp32"] = round(costs["solve_flops"] / (st["gptaq"] * 1e-3) / PEAK_FP32_MFMA, 4)
+    cov_ms = g["cov_kernel_ms"]
+    cov_tf = costs["cov_flops"] / (cov_ms * 1e-3)
+    cov_kernel = {"kernel": "cov_bf16_kernel", "kernel_ms": round(cov_ms, 4),
+                  "achieved": round(cov_tf / 1e12, 2), "frac": round(cov_tf / PEAK_BF16, 4)}
+    trailing = None
+    if g["trail_kernel_ms"]:
+        # the sweep's largest lazy GEMM: d_out x (d_in - 512) x 512, event-timed
+        tf = 2.0 * spec.d_out * (spec.d_in - 512) * 512
+        tms = g["trail_kernel_ms"]
+        trailing = {"kernel": "gemm_f32_kernel (first superblock's trailing update)",
+                    "shape": [spec.d_out, spec.d_in - 512, 512], "kernel_ms": round(tms, 4),
+                    "achieved": round(tf / (tms * 1e-3) / 1e12, 2), "peak": PEAK_FP32_MFMA / 1e12,
+                    "unit": "TFLOP/s", "frac": round(tf / (tms * 1e-3) / PEAK_FP32_MFMA, 4)}
+    return costs, stages, cov_kernel, trailing
+
+
+def with_measured(stages, cov_kernel, trailing, peaks):
+    """Fractions of the measured ceilings beside the published ones."""
+    if not peaks:
+        return
+    hbm = max(peaks["hbm_read_gbs"], peaks["hbm_copy_gbs"]) * 1e9
+    stages["cov_frac_measured_bf16"] = round(stages["cov_tflops"] / peaks["bf16_mfma_tflops"], 4)
+    stages["biip_frac_measured_copy"] = round(stages["biip_gbs"] * 1e6 / (peaks["hbm_copy_gbs"] * 1e9), 4)
+    stages["chol_frac_measured_fp32"] = round(stages["chol_tflops"] / peaks["fp32_mfma_tflops"], 4)
+    stages["gptaq_frac_measured_fp32"] = round(stages["gptaq_tflops"] / peaks["fp32_mfma_tflops"], 4)
+    cov_kernel["frac_measured"] = round(cov_kernel["achieved"] / peaks["bf16_mfma_tflops"], 4)
+    if trailing:
+        trailing["frac_measured"] = round(trailing["achieved"] / peaks["fp32_mfma_tflops"], 4)
+    del hbm
+
+
+def run_second_leg(workload, layer, steps, warmup, peaks, cpu_prefix=0):
+    """The whole path on a second layer shape (default: the LLaMA-3-70B
+    down_proj, W 8192 x 28672, 131072 bf16 tokens, 2-bit per channel),
+    device-resident inputs from the same generator, timed per stage. With
+    cpu_prefix > 0 the oracle is timed per stage on the same inputs
+    (covariances over that token prefix, scaled; the rest at full size,
+    several minutes of host time at this shape)."""
+    import torch
+
+    from synth import WORKLOADS, layer_specs, make_layer
+
+    torch.cuda.empty_cache()
+    spec = layer_specs(WORKLOADS[workload])[layer]
+    t0 = time.perf_counter()
+    data = make_layer(spec)
+    print(f"[bench] generated {spec.name} {spec.d_out}x{spec.d_in}, N={spec.n_tok} "
+          f"in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    g = run_gpu(spec, steps, warmup, data, extras=False)
+    torch.cuda.empty_cache()
+    cpu = None
+    if cpu_prefix:
+        cpu = cpu_baseline(spec, data, min(cpu_prefix, spec.n_tok))
+        print(f"[bench] {spec.name} cpu oracle stages (s): {json.dumps(cpu['stages_s'])}", file=sys.stderr,
+              flush=True)
+    del data
+    print(f"[bench] {spec.name} gpu stages (ms): {json.dumps(g['stage_ms'])}", file=sys.stderr, flush=True)
+    _, stages, cov_kernel, trailing = summarize(spec, g)
+    with_measured(stages, cov_kernel, trailing, peaks)
+    return {"workload": f"{workload}: {spec.name} W {spec.d_out}x{spec.d_in}, {spec.n_tok} {spec.dtype} "
+                        f"tokens, {spec.bits}-bit {'per-channel' if not spec.group else f'group {spec.group}'}",
+            "steps": steps, "warmup": warmup, "ms_per_layer": round(g["wall_s"] * 1e3 / steps, 3),
+            "stages": stages, "cov_kernel": cov_kernel, "trailing_gemm": trailing,
+            "sensitivity": g["sens"][2], "objective": g["obj"], "objective_rtn": g["obj_rtn"],
+            "cpu_oracle": cpu}
+
+
 def copy_calibration(mib):
     """One plain device-to-device copy of `mib` MiB (reads and writes that many bytes)."""
     import torch
@@ -407,13 +552,16 @@ def cpu_baseline(spec, data, prefix):
     t0 = time.perf_counter()
     HX, D, HG = oracle.covariances(data["x"][:prefix], data["xq"][:prefix], data["g"][:prefix])
     t["cov_prefix"] = time.perf_counter() - t0
+    print(f"[bench] oracle covariances over {prefix} tokens: {t['cov_prefix']:.1f} s", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     W2, HX2, D2, HG2, _, _ = oracle.biip(data["W"], HX, D, HG, data["sign_in"], data["sign_out"])
     t["biip"] = time.perf_counter() - t0
+    print(f"[bench] oracle BiIP: {t['biip']:.1f} s", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     oracle.sensitivity(HX2, HG2)
     U = oracle.inv_factor(HX2, spec.damp)
     t["chol"] = time.perf_counter() - t0
+    print(f"[bench] oracle factor: {t['chol']:.1f} s", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     P = oracle.form_p(D2, U)
     oracle.sweep(W2, U, P, spec.bits, spec.group, spec.block)
@@ -437,6 +585,13 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-prefix", type=int, default=4096)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the on-box peak microbenchmarks")
+    ap.add_argument("--second", default="llama3-70b-q-down:1", metavar="WORKLOAD:LAYER",
+                    help="a second layer timed per stage after the main one ('none' to skip)")
+    ap.add_argument("--second-steps", type=int, default=2)
+    ap.add_argument("--cpu-second-prefix", type=int, default=0, metavar="TOKENS",
+                    help="also time the oracle per stage on the second layer (covariances over this "
+                         "many tokens, scaled); 0 skips it")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this solver's path runs on a single MI355X "
@@ -454,7 +609,7 @@ def main():
         copy_calibration(args.copy_calib)
     g = run_gpu(spec, args.steps, args.warmup, data)
     print(f"[bench] gpu stages (ms): {json.dumps(g['stage_ms'])}", file=sys.stderr, flush=True)
-    costs = stage_costs(spec)
+    costs, stages, cov_kernel, trailing = summarize(spec, g)
     ms = g["wall_s"] * 1e3 / args.steps
     cov_ms = g["cov_kernel_ms"]
     achieved = costs["cov_flops"] / (cov_ms * 1e-3)
@@ -466,33 +621,17 @@ def main():
     roof = {"kernel": "cov_bf16_kernel", "kernel_ms": round(cov_ms, 4), "bound": "mfma",
             "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16, 4), "traffic": traffic}
-    st = g["stage_ms"]
-    stages = {
-        "cov_ms": round(st["cov"], 3),
-        "cov_tflops": round(costs["cov_flops"] / st["cov"] / 1e9, 1),
-        "biip_ms": round(st["biip"], 3),
-        "biip_gbs": round(costs["biip_bytes"] / st["biip"] / 1e6, 1),
-        "sens_ms": round(st["sens"], 3),
-        "chol_ms": round(st["chol"], 3),
-        "chol_tflops": round(costs["chol_flops"] / st["chol"] / 1e9, 2),
-        "gptaq_ms": round(st["gptaq"], 3),
-        "gptaq_tflops": round(costs["solve_flops"] / st["gptaq"] / 1e9, 2),
-        "no_cov_ms": round(sum(v for k, v in st.items() if k != "cov"), 3),
-    }
-    stages["cov_frac_bf16"] = round(costs["cov_flops"] / (st["cov"] * 1e-3) / PEAK_BF16, 4)
-    stages["biip_frac_hbm"] = round(costs["biip_bytes"] / (st["biip"] * 1e-3) / PEAK_HBM, 4)
-    stages["biip_frac_hbm_read_once"] = round(costs["biip_min_bytes"] / (st["biip"] * 1e-3) / PEAK_HBM, 4)
-    stages["chol_frac_fp32"] = round(costs["chol_flops"] / (st["chol"] * 1e-3) / PEAK_FP32_MFMA, 4)
-    stages["gptaq_frac_fp32"] = round(costs["solve_flops"] / (st["gptaq"] * 1e-3) / PEAK_FP32_MFMA, 4)
-    trailing = None
-    if g["trail_kernel_ms"]:
-        # the sweep's largest lazy GEMM: d_out x (d_in - 512) x 512, event-timed
-        tf = 2.0 * spec.d_out * (spec.d_in - 512) * 512
-        tms = g["trail_kernel_ms"]
-        trailing = {"kernel": "gemm_f32_kernel (first superblock's trailing update)",
-                    "shape": [spec.d_out, spec.d_in - 512, 512], "kernel_ms": round(tms, 4),
-                    "achieved": round(tf / (tms * 1e-3) / 1e12, 2), "peak": PEAK_FP32_MFMA / 1e12,
-                    "unit": "TFLOP/s", "frac": round(tf / (tms * 1e-3) / PEAK_FP32_MFMA, 4)}
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks()
+        print(f"[bench] measured peaks: {json.dumps(peaks)}", file=sys.stderr, flush=True)
+        roof["peak_measured"] = peaks["bf16_mfma_tflops"]
+        roof["frac_measured"] = round(achieved / 1e12 / peaks["bf16_mfma_tflops"], 4)
+    with_measured(stages, cov_kernel, trailing, peaks)
+    second = None
+    if args.second and args.second != "none":
+        wl, _, li = args.second.partition(":")
+        second = run_second_leg(wl, int(li or 0), args.second_steps, 1, peaks, args.cpu_second_prefix)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(spec, data, min(args.cpu_prefix, spec.n_tok))
@@ -511,6 +650,7 @@ def main():
                    "inputs": spec.dtype, "bits": spec.bits, "group": spec.group,
                    "block": spec.block, "damp": spec.damp},
         "roofline": roof,
+        "measured_peaks": peaks,
         "trailing_gemm": trailing,
         "stages": stages,
         "sensitivity": g["sens"][2],
@@ -519,6 +659,7 @@ def main():
         "inference": g["inference"],
         "streaming_covariances": g["streaming"],
         "output_feedback": g["output_feedback"],
+        "second_layer": second,
     }
     print(json.dumps(out))
 
