@@ -479,15 +479,13 @@ def with_measured(stages, cov_kernel, trailing, peaks):
     """Fractions of the measured ceilings beside the published ones."""
     if not peaks:
         return
-    hbm = max(peaks["hbm_read_gbs"], peaks["hbm_copy_gbs"]) * 1e9
     stages["cov_frac_measured_bf16"] = round(stages["cov_tflops"] / peaks["bf16_mfma_tflops"], 4)
-    stages["biip_frac_measured_copy"] = round(stages["biip_gbs"] * 1e6 / (peaks["hbm_copy_gbs"] * 1e9), 4)
+    stages["biip_frac_measured_copy"] = round(stages["biip_gbs"] / peaks["hbm_copy_gbs"], 4)
     stages["chol_frac_measured_fp32"] = round(stages["chol_tflops"] / peaks["fp32_mfma_tflops"], 4)
     stages["gptaq_frac_measured_fp32"] = round(stages["gptaq_tflops"] / peaks["fp32_mfma_tflops"], 4)
     cov_kernel["frac_measured"] = round(cov_kernel["achieved"] / peaks["bf16_mfma_tflops"], 4)
     if trailing:
         trailing["frac_measured"] = round(trailing["achieved"] / peaks["fp32_mfma_tflops"], 4)
-    del hbm
 
 
 def run_second_leg(workload, layer, steps, warmup, peaks, cpu_prefix=0):

@@ -20,9 +20,12 @@
  *    count. Token-major activations X (N x d_in) hold one token per row, so
  *    X^T X is the page's E[x x^T] up to 1/N.
  *  - Pointers are DEVICE pointers unless marked "host". The caller owns every
- *    buffer; the library allocates nothing and keeps no state between calls.
- *    Scratch memory is passed in as (ws, ws_bytes); kq_workspace_size gives
- *    the size each call needs.
+ *    buffer; the library allocates no device memory and creates no stream or
+ *    event. Scratch memory is passed in as (ws, ws_bytes); kq_workspace_size
+ *    gives the size each call needs. The only state kept between calls is the
+ *    measurement hook of kq_set_kernel_events (two caller-owned event handles
+ *    per thread, unset by default); nothing else carries over from one call
+ *    to the next.
  *  - Device work is enqueued on `stream` and is asynchronous, except calls
  *    that return host values (kq_sensitivity, kq_cholesky_inv,
  *    kq_layer_objective), which synchronize the stream before returning.
@@ -227,8 +230,8 @@ kq_status kq_gptaq_quantize(float* W, const float* U, const float* D,
  *   codes    d_out x d_in uint8;  scale, zero: d_out fp32.
  * Any d_out, d_in >= 1. Workspace from
  * kq_workspace_size(KQ_OP_YAQA_QUANTIZE, d_out, d_in, ...) (sized for a
- * non-NULL D). Synchronizes the stream (the call overlaps work on a second
- * stream of its own, which it releases before returning); fp32 arithmetic. */
+ * non-NULL D). Asynchronous: every launch is enqueued on `stream`, and the
+ * call creates no stream or event of its own; fp32 arithmetic. */
 kq_status kq_yaqa_quantize(float* W, const float* U_in, const float* U_out, const float* D,
                            int64_t d_out, int64_t d_in, const kq_quant_cfg* cfg,
                            uint8_t* codes, float* scale, float* zero,

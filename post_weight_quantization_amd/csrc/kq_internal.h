@@ -163,31 +163,4 @@ kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const 
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// A second stream (default priority) and two rings of events, for work that
-// overlaps a serial chain on the caller's stream; synchronized and released
-// when it goes out of scope (callers that use it synchronize their own
-// stream before returning).
-struct SideStream {
-  static constexpr int NE = 4;
-  hipStream_t st = nullptr;
-  hipEvent_t tiles[NE] = {};  // recorded on the caller's stream
-  hipEvent_t done[NE] = {};   // recorded on the side stream
-  kq_status open() {
-    KQ_HIP(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
-    for (int k = 0; k < NE; ++k) {
-      KQ_HIP(hipEventCreateWithFlags(&tiles[k], hipEventDisableTiming));
-      KQ_HIP(hipEventCreateWithFlags(&done[k], hipEventDisableTiming));
-    }
-    return KQ_OK;
-  }
-  ~SideStream() {
-    if (st) (void)hipStreamSynchronize(st);
-    for (int k = 0; k < NE; ++k) {
-      if (tiles[k]) (void)hipEventDestroy(tiles[k]);
-      if (done[k]) (void)hipEventDestroy(done[k]);
-    }
-    if (st) (void)hipStreamDestroy(st);
-  }
-};
-
 }  // namespace kq

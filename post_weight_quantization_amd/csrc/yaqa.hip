@@ -25,8 +25,8 @@
 // column blocks L < J. The feedback of its two neighbours finished one step
 // earlier (left: e_{I,J-1} U_I[J-1,J]; above: U_O[I-1,I]^T M_{I-1,J}) the tile
 // computes itself as MFMA products in LDS; everything farther away arrives
-// through batched fp32 MFMA GEMMs on a second stream, which carry the results
-// of step s to the tiles of steps >= s + 2 while the tiles of step s + 1 run:
+// through batched fp32 MFMA GEMMs enqueued after each step, which carry the
+// results of step s to the tiles of steps >= s + 2:
 // M[I, blocks >= J+2] += e_IJ U_I[J, .] and Wk[blocks >= I+2, J] -= U_O[I, .]^T M_IJ.
 //
 // Inside a tile, the four lanes of a quad hold one row (16 columns each) as
@@ -462,22 +462,18 @@ kq_status yaqa_run(float* W, const float* U_in, const float* U_out, const float*
   KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(yaqa_tile_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(YAQA_LDS)));
 
-  // The far feedback of step s (targets two or more tiles away) runs on a
-  // second stream while the tiles of step s + 1 run; step s + 2 waits for it.
-  SideStream side;
-  KQ_TRY(side.open());
+  // Everything runs in order on the caller's stream: the tiles of step s,
+  // then the far feedback of step s (targets two or more tiles away), which
+  // the tiles of step s + 2 are the first to need.
   const int nsteps = mt + nt - 1;
   for (int sidx = 0; sidx < nsteps; ++sidx) {
     const int I_lo = std::max(0, sidx - nt + 1), I_hi = std::min(sidx, mt - 1);
     const int cnt = I_hi - I_lo + 1;
     const int J_hi = sidx - I_lo;
-    if (sidx >= 2) KQ_HIP(hipStreamWaitEvent(s, side.done[(sidx - 2) % SideStream::NE], 0));
     st.s = sidx;
     st.I_lo = I_lo;
     yaqa_tile_kernel<<<unsigned(cnt), 256, YAQA_LDS, s>>>(st);
     KQ_HIP(hipGetLastError());
-    KQ_HIP(hipEventRecord(side.tiles[sidx % SideStream::NE], s));
-    KQ_HIP(hipStreamWaitEvent(side.st, side.tiles[sidx % SideStream::NE], 0));
     // M[I, blocks >= J + 2] += e_IJ U_I[J, same]
     GemmArgs gr = gemm_args(E + int64_t(I_lo) * YT * np + int64_t(J_hi) * YT, np,
                             UI + int64_t(J_hi) * YT * np, np, Mp + int64_t(I_lo) * YT * np, np, YT,
@@ -488,7 +484,7 @@ kq_status yaqa_run(float* W, const float* U_in, const float* U_out, const float*
     gr.strideC = int64_t(YT) * np;
     gr.ostart = int64_t(J_hi + 2) * YT;
     gr.ostart_ofs = -YT;
-    if (sidx - I_hi + 2 < nt) KQ_TRY(gemm_f32(gr, side.st));  // the smallest J has targets
+    if (sidx - I_hi + 2 < nt) KQ_TRY(gemm_f32(gr, s));  // the smallest J has targets
     // Wk[blocks >= I + 2, J] -= U_O[I, same]^T M_IJ
     GemmArgs gc = gemm_args(UO + int64_t(I_lo) * YT * mp, mp,
                             Mp + int64_t(I_lo) * YT * np + int64_t(J_hi) * YT, np,
@@ -500,11 +496,8 @@ kq_status yaqa_run(float* W, const float* U_in, const float* U_out, const float*
     gc.strideC = -int64_t(YT);
     gc.ostart = int64_t(I_lo + 2) * YT;
     gc.ostart_ofs = YT;
-    if (I_lo + 2 < mt) KQ_TRY(gemm_f32(gc, side.st));  // the smallest I has targets
-    KQ_HIP(hipEventRecord(side.done[sidx % SideStream::NE], side.st));
+    if (I_lo + 2 < mt) KQ_TRY(gemm_f32(gc, s));  // the smallest I has targets
   }
-  KQ_HIP(hipStreamWaitEvent(s, side.done[(nsteps - 1) % SideStream::NE], 0));
-  KQ_HIP(hipStreamSynchronize(s));
   return KQ_OK;
 }
 
