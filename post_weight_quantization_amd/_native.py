@@ -9,7 +9,7 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkq.so")
+LIB_PATH = os.environ.get("KQ_LIB_PATH") or os.path.join(HERE, "libkq.so")
 
 KQ_OK, KQ_ERR_ARG, KQ_ERR_SHAPE, KQ_ERR_NOT_PD, KQ_ERR_NONFINITE, KQ_ERR_WORKSPACE, KQ_ERR_HIP, \
     KQ_ERR_UNSUPPORTED = range(8)

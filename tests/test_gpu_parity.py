@@ -104,12 +104,22 @@ def test_cov_bf16_chunked_beta():
 # ------------------------------------------------------------------ stage 2
 
 
-@pytest.mark.parametrize("d_out,d_in,bo,bi", [(256, 256, 0, 0), (384, 512, 128, 0), (1024, 4096, 0, 64)])
+def _spd_large(rng, n, k=96):
+    """A cheap SPD matrix for large n: low-rank Gram matrix plus a spread diagonal."""
+    Z = rng.standard_normal((n, k))
+    return Z @ Z.T / k + np.diag(np.exp(rng.uniform(0, np.log(1e3), n)))
+
+
+# (4096, 4096) and (8192, 4096) take the two-pass transposing form (blocks of
+# 4096 and 8192 on both sides); the others the row and column passes
+@pytest.mark.parametrize("d_out,d_in,bo,bi", [(256, 256, 0, 0), (384, 512, 128, 0), (1024, 4096, 0, 64),
+                                              (4096, 4096, 0, 0), (8192, 4096, 0, 0)])
 def test_biip_against_oracle(d_out, d_in, bo, bi):
     rng = np.random.default_rng(d_out + d_in)
     sc = np.exp(rng.standard_normal(d_in))
-    HX = spd(rng, d_in, 1e3) * np.outer(sc, sc)  # SPD with diagonals spread over decades
-    HG = spd(rng, d_out, 1e4)
+    big = max(d_out, d_in) > 2048
+    HX = (_spd_large(rng, d_in) if big else spd(rng, d_in, 1e3)) * np.outer(sc, sc)  # diagonals over decades
+    HG = _spd_large(rng, d_out) if big else spd(rng, d_out, 1e4)
     D = 0.01 * rng.standard_normal((d_in, d_in))
     W = 0.02 * rng.standard_normal((d_out, d_in))
     si = rng.choice([-1, 1], d_in).astype(np.int8)
