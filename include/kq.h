@@ -294,6 +294,30 @@ kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* 
                              int64_t blk_out, const float* x, int64_t batch, int64_t d_out,
                              int64_t d_in, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of device scratch memory behind kq_apply_quantized_noalloc (one
+ * copy per GPU, held until the process ends). */
+#define KQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kq_apply_quantized for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, results and errors as kq_apply_quantized,
+ * without (ws, ws_bytes): the scratch memory is a fixed array of
+ * KQ_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, whose device
+ * address is looked up once per device on the first call made with that
+ * device current (the device of `stream` must be the current device). The
+ * call allocates nothing. Sizes whose workspace
+ * (kq_workspace_size(KQ_OP_APPLY_QUANTIZED, d_out, d_in, batch)) exceeds
+ * KQ_NOALLOC_SCRATCH_BYTES return KQ_ERR_WORKSPACE before any launch. Every
+ * call on a GPU shares that GPU's array: calls that may overlap on one GPU
+ * (two streams, two threads) race and must be ordered by the caller. No
+ * state of one call is read by the next (the array's contents are
+ * rewritten before use). Asynchronous. */
+kq_status kq_apply_quantized_noalloc(const uint32_t* packed, int32_t bits, const float* scale,
+                                     const float* zero, int32_t group, const float* s_x,
+                                     const float* s_g, const int8_t* sign_in, const int8_t* sign_out,
+                                     int64_t blk_in, int64_t blk_out, const float* x, int64_t batch,
+                                     int64_t d_out, int64_t d_in, float* y, hipStream_t stream);
+
 /* Weights and activations both quantized (the W2A4 setting; KronQ explainer,
  * gist.science, "Quantizzazione di Pesi e Attivazioni": activations follow
  * the QuaRot recipe). The rotated input x2 = V S_X^-1 x of each vector is

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     kq_allocate_bits,
     kq_apply_quantized,
     kq_apply_quantized_a4,
+    kq_apply_quantized_noalloc,
     kq_biip,
     kq_cholesky_inv,
     kq_form_p,

@@ -16,6 +16,7 @@ KQ_OK, KQ_ERR_ARG, KQ_ERR_SHAPE, KQ_ERR_NOT_PD, KQ_ERR_NONFINITE, KQ_ERR_WORKSPA
 STATUS_NAMES = {0: "KQ_OK", 1: "KQ_ERR_ARG", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_NOT_PD",
                 4: "KQ_ERR_NONFINITE", 5: "KQ_ERR_WORKSPACE", 6: "KQ_ERR_HIP", 7: "KQ_ERR_UNSUPPORTED"}
 KQ_BF16, KQ_F32 = 0, 1
+KQ_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/kq.h
 (KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_SENSITIVITY, KQ_OP_CHOLESKY_INV, KQ_OP_FORM_P,
  KQ_OP_GPTAQ_QUANTIZE, KQ_OP_LAYER_OBJECTIVE, KQ_OP_APPLY_QUANTIZED,
  KQ_OP_YAQA_QUANTIZE, KQ_OP_APPLY_QUANTIZED_A4) = range(10)
@@ -25,7 +26,7 @@ EXPORTS = ("kq_last_error", "kq_version", "kq_workspace_size", "kq_accumulate_co
            "kq_sensitivity", "kq_cholesky_inv", "kq_form_p", "kq_gptaq_quantize",
            "kq_allocate_bits", "kq_layer_objective", "kq_set_kernel_events",
            "kq_packed_row_words", "kq_pack_codes", "kq_apply_quantized", "kq_yaqa_quantize",
-           "kq_apply_quantized_a4")
+           "kq_apply_quantized_a4", "kq_apply_quantized_noalloc")
 
 
 class kq_quant_cfg(ctypes.Structure):
@@ -85,6 +86,8 @@ _sig("kq_packed_row_words", _st, _i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_i
 _sig("kq_pack_codes", _st, _p, _i64, _i64, ctypes.c_int32, _p, _p)
 _sig("kq_apply_quantized", _st, _p, ctypes.c_int32, _p, _p, ctypes.c_int32, _p, _p, _p, _p, _i64, _i64,
      _p, _i64, _i64, _i64, _p, _p, _sz, _p)
+_sig("kq_apply_quantized_noalloc", _st, _p, ctypes.c_int32, _p, _p, ctypes.c_int32, _p, _p, _p, _p, _i64,
+     _i64, _p, _i64, _i64, _i64, _p, _p)
 _sig("kq_apply_quantized_a4", _st, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _p, _i64, _i64, _i64,
      ctypes.c_float, _p, _p, _p, _p, _sz, _p)
 

@@ -318,6 +318,35 @@ def kq_apply_quantized(packed, bits: int, scale, zero, group: int, s_x, s_g, sig
     return y
 
 
+def kq_apply_quantized_noalloc(packed, bits: int, scale, zero, group: int, s_x, s_g, sign_in, sign_out,
+                               x, y, blk_in: int = 0, blk_out: int = 0, stream=None):
+    """kq_apply_quantized without a workspace: the library's fixed scratch
+    array serves instead (for callers that cannot allocate). y (batch x
+    d_out fp32) must be given: this call allocates nothing."""
+    batch, d_in = x.shape
+    d_out = packed.shape[0]
+    f32 = torch.float32
+    ng = -(-d_in // group) if group else 1
+    if y is None:
+        raise ValueError("y: expected an output tensor (this call allocates nothing)")
+    _expect(x, (batch, d_in), f32, "x")
+    _expect(packed, (d_out, kq_packed_row_words(d_in, bits)), packed.dtype, "packed")
+    if packed.element_size() != 4:
+        raise ValueError("packed: expected 32-bit words")
+    _expect(scale, (d_out, ng), f32, "scale")
+    _expect(zero, (d_out, ng), f32, "zero")
+    _expect(s_x, (d_in,), f32, "s_x")
+    _expect(s_g, (d_out,), f32, "s_g")
+    _expect(sign_in, (d_in,), torch.int8, "sign_in")
+    _expect(sign_out, (d_out,), torch.int8, "sign_out")
+    _expect(y, (batch, d_out), f32, "y")
+    _need_cuda(packed, scale, zero, s_x, s_g, sign_in, sign_out, x, y)
+    check(N.lib.kq_apply_quantized_noalloc(_ptr(packed), bits, _ptr(scale), _ptr(zero), group, _ptr(s_x),
+                                           _ptr(s_g), _ptr(sign_in), _ptr(sign_out), blk_in, blk_out,
+                                           _ptr(x), batch, d_out, d_in, _ptr(y), _stream(stream)))
+    return y
+
+
 def kq_apply_quantized_a4(packed, scale, zero, s_x, s_g, sign_in, sign_out, x, clip: float = 1.0,
                           blk_in: int = 0, blk_out: int = 0, y=None, act_codes=None, act_scale=None,
                           ws=None, stream=None):

@@ -6,6 +6,7 @@
 #include <cstring>
 #include <vector>
 #include <algorithm>
+#include <mutex>
 
 #include "kq_internal.h"
 
@@ -83,6 +84,61 @@ kq_status check_cfg(const kq_quant_cfg* cfg, int64_t d_in) {
 }  // namespace kq
 
 using namespace kq;
+
+// Scratch memory of kq_apply_quantized_noalloc: one copy per device, held
+// until the process ends. Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol); the device
+// address of each GPU's copy comes from hipGetSymbolAddress, called once per
+// device with that device current, and is kept in noalloc_ptr.
+static __device__ __align__(256) unsigned char scratch[KQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// argument checks shared by kq_apply_quantized and its no-allocation variant
+kq_status apply_validate(const uint32_t* packed, int32_t bits, const float* scale, const float* zero,
+                         int32_t group, const float* s_x, const float* s_g, const int8_t* sign_in,
+                         const int8_t* sign_out, int64_t blk_in, int64_t blk_out, const float* x,
+                         int64_t batch, int64_t d_out, int64_t d_in, float* y, int64_t* bi,
+                         int64_t* bo) {
+  if (!packed || !scale || !zero || !s_x || !s_g || !sign_in || !sign_out || !x || !y)
+    return fail(KQ_ERR_ARG, "apply_quantized: NULL argument");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(KQ_ERR_ARG, "apply_quantized: bits must be 2, 3, 4 or 8");
+  if (group != 0 && group != 128)
+    return fail(KQ_ERR_UNSUPPORTED, "apply_quantized: group must be 0 or 128");
+  if (d_out < 4 || d_out % 4 || batch < 1 || batch > 65536)
+    return fail(KQ_ERR_SHAPE, "apply_quantized: d_out must be a multiple of 4 and 1 <= batch <= 65536");
+  if (d_in < 32 || d_in % 32 || (group && d_in % group))
+    return fail(KQ_ERR_SHAPE, "apply_quantized: d_in must be a multiple of 32 (of the group size)");
+  KQ_TRY(resolve_block(d_in, blk_in, bi, "input"));
+  KQ_TRY(resolve_block(d_out, blk_out, bo, "output"));
+  const void* ptrs[4] = {packed, x, y, s_x};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(KQ_ERR_ARG, "apply_quantized: packed, x, y, s_x must be 16-byte aligned");
+  return KQ_OK;
+}
+
+constexpr int MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[MAX_DEVICES] = {};
+
+kq_status noalloc_scratch(void** out) {
+  int dev = -1;
+  KQ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(KQ_ERR_UNSUPPORTED, "apply_quantized_noalloc: device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void* p = nullptr;
+    KQ_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(KQ_ERR_HIP, "apply_quantized_noalloc: no device address for the scratch array");
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return KQ_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -374,24 +430,32 @@ kq_status kq_apply_quantized(const uint32_t* packed, int32_t bits, const float* 
                              int64_t blk_out, const float* x, int64_t batch, int64_t d_out,
                              int64_t d_in, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
-  if (!packed || !scale || !zero || !s_x || !s_g || !sign_in || !sign_out || !x || !y)
-    return fail(KQ_ERR_ARG, "apply_quantized: NULL argument");
-  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
-    return fail(KQ_ERR_ARG, "apply_quantized: bits must be 2, 3, 4 or 8");
-  if (group != 0 && group != 128)
-    return fail(KQ_ERR_UNSUPPORTED, "apply_quantized: group must be 0 or 128");
-  if (d_out < 4 || d_out % 4 || batch < 1 || batch > 65536)
-    return fail(KQ_ERR_SHAPE, "apply_quantized: d_out must be a multiple of 4 and 1 <= batch <= 65536");
-  if (d_in < 32 || d_in % 32 || (group && d_in % group))
-    return fail(KQ_ERR_SHAPE, "apply_quantized: d_in must be a multiple of 32 (of the group size)");
   int64_t bi = 0, bo = 0;
-  KQ_TRY(resolve_block(d_in, blk_in, &bi, "input"));
-  KQ_TRY(resolve_block(d_out, blk_out, &bo, "output"));
-  const void* ptrs[4] = {packed, x, y, s_x};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(KQ_ERR_ARG, "apply_quantized: packed, x, y, s_x must be 16-byte aligned");
+  KQ_TRY(apply_validate(packed, bits, scale, zero, group, s_x, s_g, sign_in, sign_out, blk_in, blk_out,
+                        x, batch, d_out, d_in, y, &bi, &bo));
   KQ_TRY(check_ws(ws, ws_bytes, apply_ws_bytes(d_out, d_in, batch), "apply_quantized"));
   Arena ar{static_cast<char*>(ws), ws_bytes, 0};
+  return apply_run(packed, bits, scale, zero, group, s_x, s_g, sign_in, sign_out, bi, bo, x, batch,
+                   d_out, d_in, y, ar, stream);
+}
+
+kq_status kq_apply_quantized_noalloc(const uint32_t* packed, int32_t bits, const float* scale,
+                                     const float* zero, int32_t group, const float* s_x,
+                                     const float* s_g, const int8_t* sign_in, const int8_t* sign_out,
+                                     int64_t blk_in, int64_t blk_out, const float* x, int64_t batch,
+                                     int64_t d_out, int64_t d_in, float* y, hipStream_t stream) {
+  clear_error();
+  int64_t bi = 0, bo = 0;
+  KQ_TRY(apply_validate(packed, bits, scale, zero, group, s_x, s_g, sign_in, sign_out, blk_in, blk_out,
+                        x, batch, d_out, d_in, y, &bi, &bo));
+  const size_t need = apply_ws_bytes(d_out, d_in, batch);
+  if (need > size_t(KQ_NOALLOC_SCRATCH_BYTES))
+    return fail(KQ_ERR_WORKSPACE,
+                "apply_quantized_noalloc: these sizes need %zu bytes of scratch, above the fixed %zu",
+                need, size_t(KQ_NOALLOC_SCRATCH_BYTES));
+  void* p = nullptr;
+  KQ_TRY(noalloc_scratch(&p));
+  Arena ar{static_cast<char*>(p), size_t(KQ_NOALLOC_SCRATCH_BYTES), 0};
   return apply_run(packed, bits, scale, zero, group, s_x, s_g, sign_in, sign_out, bi, bo, x, batch,
                    d_out, d_in, y, ar, stream);
 }
