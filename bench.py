@@ -584,6 +584,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-prefix", type=int, default=4096)
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-box peak microbenchmarks")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the legs after the layer step (inference, output feedback, streaming)")
     ap.add_argument("--second", default="llama3-70b-q-down:1", metavar="WORKLOAD:LAYER",
                     help="a second layer timed per stage after the main one ('none' to skip)")
     ap.add_argument("--second-steps", type=int, default=2)
@@ -605,7 +607,7 @@ def main():
           f"in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     if args.copy_calib:
         copy_calibration(args.copy_calib)
-    g = run_gpu(spec, args.steps, args.warmup, data)
+    g = run_gpu(spec, args.steps, args.warmup, data, extras=not args.no_extras)
     print(f"[bench] gpu stages (ms): {json.dumps(g['stage_ms'])}", file=sys.stderr, flush=True)
     costs, stages, cov_kernel, trailing = summarize(spec, g)
     ms = g["wall_s"] * 1e3 / args.steps

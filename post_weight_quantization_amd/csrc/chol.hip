@@ -10,11 +10,13 @@
 // library therefore:
 //   1. writes A = J (H + delta I) J (lower triangle) into U's buffer, with
 //      delta = damp * mean(diag H) computed on the device;
-//   2. factors A = L L^T in place, right-looking with 128-column blocks: a
-//      single-workgroup leaf factors the diagonal block and inverts it, the
-//      panel below is solved as a GEMM with that inverse (into a compact
-//      temporary, copied back), and the trailing lower triangle takes a
-//      rank-128 MFMA update from the compact copy;
+//   2. factors A = L L^T in place with 128-column blocks inside 512-column
+//      superblocks: a single-workgroup leaf factors the diagonal block and
+//      inverts it, the panel below is solved as a GEMM with that inverse
+//      (into a compact temporary, copied back), the superblock's remaining
+//      columns take a rank-128 MFMA update from the compact copy, and after
+//      each superblock the rest of the trailing lower triangle takes one
+//      rank-512 update;
 //   3. inverts L in place by bottom-up doubling with
 //      inv([[A,0],[B,C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]]: every level
 //      is two batched, triangle-aware fp32 MFMA GEMMs;
@@ -29,7 +31,8 @@ namespace kq {
 
 namespace {
 
-constexpr int NB = 128;
+constexpr int NB = 128;   // leaf (diagonal block) size
+constexpr int SB = 512;   // superblock: columns between two full trailing updates
 
 // A[i][j] = H[n-1-i][n-1-j] + delta [i == j] for i >= j (reads H's upper triangle)
 __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, const double* dsum,
@@ -46,26 +49,26 @@ __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, cons
 
 // ---------------------------------------------------------------- the leaf
 // Factor the NB x NB diagonal block at (k0, k0) of A (ld n) in place (lower,
-// zeros written above the diagonal) and write its inverse to Dinv (NB x NB,
-// zeros above the diagonal). One workgroup of 4 waves; the block lives in LDS.
-// Per 32-column panel:
-//  * wave 0 factors the 32 x 32 diagonal block and inverts it in registers
-//    (leaf_diag32), with no barrier or LDS access inside the 32 column steps;
-//  * the waves solve the rows below as a product with the inverse
-//    (L21 = A21 L11^-T) and take the rank-32 update of the trailing lower
-//    triangle, in 32 x 32 blocks on the matrix cores;
-// then the off-diagonal blocks of the inverse X_ip = -X_ii sum_k L_ik X_kp,
-// one block column per wave, also on the matrix cores.
+// zeros written above the diagonal) and write the inverse of the factor to
+// Dinv (NB x NB, zeros above the diagonal). One workgroup of 4 waves; the
+// block lives in LDS. Right-looking over eight 16-column panels p:
+//  * wave 0 factors the panel's 16 x 16 diagonal block in registers (DPP
+//    row broadcasts, no LDS access inside the 16 column steps);
+//  * the rows below solve for the panel's columns by forward substitution,
+//    one row per thread;
+//  * the trailing lower triangle takes the rank-16 update in 16 x 16 blocks
+//    on the matrix cores (v_mfma_f32_16x16x4f32), the blocks spread over the
+//    waves; wave 0 takes the next panel's diagonal block and factors it
+//    right away, so the next factorization overlaps the rest of the update.
+// The inverse X = L^-1 follows: the diagonal 16 x 16 blocks by forward
+// substitution, one column per thread, then the blocks below by
+// block-diagonals d = i - j = 1 .. 7, X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj,
+// on the matrix cores.
 constexpr int LS = NB + 4;  // LDS row stride (floats), keeps float4 alignment
+constexpr int PW = 16;      // panel width
+constexpr int NP = NB / PW;
 
-__device__ inline float lane_value(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-__device__ inline void wave_lds_fence() {
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Broadcast of lane J of each 16-lane row (DPP row_newbcast) to that row.
 template <int J>
@@ -77,48 +80,38 @@ __device__ inline float bc16(float v) {
 // x[J + 1 + K] += nmm * (entry (J + 1 + K, J): lane J + 1 + K's x[J], the
 // symmetric mirror of row J's entry), nmm = minus the row's multiplier
 template <int J, int... K>
-__device__ inline void chol16_upd_x(float (&x)[16], float nmm, std::integer_sequence<int, K...>) {
+__device__ inline void fac16_upd(float (&x)[16], float nmm, std::integer_sequence<int, K...>) {
   ((x[J + 1 + K] = __builtin_fmaf(bc16<J + 1 + K>(x[J]), nmm, x[J + 1 + K])), ...);
 }
 
-// y[K] += nmm * (row J of Y: lane J's y[K]), K <= J
-template <int J, int... K>
-__device__ inline void chol16_upd_y(float (&y)[16], float nmm, std::integer_sequence<int, K...>) {
-  ((y[K] = __builtin_fmaf(bc16<J>(y[K]), nmm, y[K])), ...);
-}
-
-// Step J of the 16 x 16 elimination: the pivot is lane J's x[J]; the rows
-// below take multipliers x_r[J] / piv, and the same row operations apply to
-// Y. Only the lower triangle of the block is ever read.
+// Step J of the 16 x 16 elimination A = L_u D L_u^T: the pivot is lane J's
+// x[J]; the rows below take multipliers x_r[J] / piv. Only the lower
+// triangle of the block is ever read.
 template <int J>
-struct Chol16 {
-  __device__ static void run(float (&x)[16], float (&y)[16], float (&dv)[16], int r, int col0,
-                             int* info) {
+struct Fac16 {
+  __device__ static void run(float (&x)[16], float (&dv)[16], int r, int col0, int* info) {
     float piv = bc16<J>(x[J]);
     if (!(piv > 0.f)) {  // non-positive or NaN pivot
       if ((threadIdx.x & 63) == 0) atomicMin(info, col0 + J + 1);
       piv = 1.f;
     }
-    const float nmm = r > J ? -(x[J] * __builtin_amdgcn_rcpf(piv)) : 0.f;  // minus the multiplier
-    chol16_upd_x<J>(x, nmm, std::make_integer_sequence<int, 15 - J>{});
-    chol16_upd_y<J>(y, nmm, std::make_integer_sequence<int, J + 1>{});
-    dv[J] = __builtin_amdgcn_sqrtf(piv);  // 1-ulp hardware square root
-    Chol16<J + 1>::run(x, y, dv, r, col0, info);
+    const float nmm = r > J ? -(x[J] * __builtin_amdgcn_rcpf(piv)) : 0.f;
+    fac16_upd<J>(x, nmm, std::make_integer_sequence<int, 15 - J>{});
+    dv[J] = piv;
+    Fac16<J + 1>::run(x, dv, r, col0, info);
   }
 };
 template <>
-struct Chol16<16> {
-  __device__ static void run(float (&)[16], float (&)[16], float (&)[16], int, int, int*) {}
+struct Fac16<16> {
+  __device__ static void run(float (&)[16], float (&)[16], int, int, int*) {}
 };
 
-// Cholesky and inverse of the 16 x 16 block at (R0, R0) of As (row stride
-// LS), one row per lane (lane r % 16 holds row r; the four 16-lane rows of
-// the wave hold copies): A = L_u D L_u^T by elimination with Y = L_u^-1,
-// then L[r][k] = x_r[k] / sqrt(piv_k) and L^-1 = D^(-1/2) Y. Lanes below 16
-// write L (zeros above the diagonal) to As and L^-1 to Xs.
-__device__ inline void chol16_block(float* As, float* Xs, int R0, int col0, int* info) {
+// Cholesky factor of the 16 x 16 block at (R0, R0) of As (row stride LS),
+// in place (zeros above the diagonal), by one wave: lane r % 16 holds row
+// r (the four 16-lane rows hold copies); L[r][k] = x_r[k] / sqrt(piv_k).
+__device__ inline void fac16_block(float* As, int R0, int col0, int* info) {
   const int r = threadIdx.x & 15;
-  float x[16], y[16], dv[16];
+  float x[16], dv[16];
   const float* row = As + (R0 + r) * LS + R0;
 #pragma unroll
   for (int k = 0; k < 16; k += 4) {
@@ -128,189 +121,56 @@ __device__ inline void chol16_block(float* As, float* Xs, int R0, int col0, int*
     x[k + 2] = v.z;
     x[k + 3] = v.w;
   }
-#pragma unroll
-  for (int k = 0; k < 16; ++k) y[k] = k == r ? 1.f : 0.f;
-  Chol16<0>::run(x, y, dv, r, col0, info);
-  float dr = dv[0];
-#pragma unroll
-  for (int k = 1; k < 16; ++k) dr = r == k ? dv[k] : dr;
-  const float idr = __builtin_amdgcn_rcpf(dr);
+  Fac16<0>::run(x, dv, r, col0, info);
   if ((threadIdx.x & 63) < 16) {
     float* lrow = As + (R0 + r) * LS + R0;
-    float* xrow = Xs + (R0 + r) * LS + R0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      lrow[k] = k < r ? x[k] * __builtin_amdgcn_rcpf(dv[k]) : (k == r ? dr : 0.f);
-      xrow[k] = k <= r ? y[k] * idr : 0.f;
+      const float sq = __builtin_amdgcn_sqrtf(dv[k]);  // 1-ulp hardware square root
+      lrow[k] = k < r ? x[k] * __builtin_amdgcn_rcpf(sq) : (k == r ? sq : 0.f);
     }
   }
 }
 
-// Cholesky of the 32 x 32 block at (C0, C0) of As and its inverse (wave 0):
-// two 16 x 16 factors with 16 x 16 products between them,
-//   L11 X11 = chol(A11), L21 = A21 X11^T, A22 -= L21 L21^T,
-//   L22 X22 = chol(A22), X21 = -X22 (L21 X11).
-// The products take lane l = (r, column group): row r = l % 16, columns
-// 4 (l / 16) .. + 3, reading their operands from LDS.
-__device__ void leaf_diag32(float* As, float* Xs, int64_t k0, int* info, int C0) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15, c0 = 4 * (lane >> 4);
-  const int col0 = int(k0) + C0;
-  chol16_block(As, Xs, C0, col0, info);
-  wave_lds_fence();
-  // L21[r][c] = sum_{k <= c} A21[r][k] X11[c][k]
-  float a[16];
-  {
-    const float* arow = As + (C0 + 16 + r) * LS + C0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) a[k] = arow[k];
-  }
-  float l21[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float* xr = Xs + (C0 + c0 + q) * LS + C0;
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) t = __builtin_fmaf(a[k], xr[k], t);  // X11 is zero above its diagonal
-    l21[q] = t;
-  }
-  wave_lds_fence();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) As[(C0 + 16 + r) * LS + C0 + c0 + q] = l21[q];
-  wave_lds_fence();
-  // A22[r][c] -= sum_k L21[r][k] L21[c][k] (lower triangle used)
-  {
-    float lr[16];
-    const float* lrow = As + (C0 + 16 + r) * LS + C0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) lr[k] = lrow[k];
-    float upd[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float* lc = As + (C0 + 16 + c0 + q) * LS + C0;
-      float t = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) t = __builtin_fmaf(lr[k], lc[k], t);
-      upd[q] = t;
-    }
-    wave_lds_fence();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) As[(C0 + 16 + r) * LS + C0 + 16 + c0 + q] -= upd[q];
-  }
-  wave_lds_fence();
-  chol16_block(As, Xs, C0 + 16, col0 + 16, info);
-  wave_lds_fence();
-  // T = L21 X11 (T[r][c] = sum_{k >= c} L21[r][k] X11[k][c]), then X21 = -X22 T
-  {
-    float lr[16];
-    const float* lrow = As + (C0 + 16 + r) * LS + C0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) lr[k] = lrow[k];
-    float t4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float t = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) t = __builtin_fmaf(lr[k], Xs[(C0 + k) * LS + C0 + c0 + q], t);
-      t4[q] = t;
-    }
-    // T goes to the unused upper-right block of Xs (rows 0..15, columns 16..31)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) Xs[(C0 + r) * LS + C0 + 16 + c0 + q] = t4[q];
-    wave_lds_fence();
-    float xr[16];
-    const float* x22 = Xs + (C0 + 16 + r) * LS + C0 + 16;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) xr[k] = x22[k];  // zero above the diagonal
-    float o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float t = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) t = __builtin_fmaf(xr[k], Xs[(C0 + k) * LS + C0 + 16 + c0 + q], t);
-      o[q] = -t;
-    }
-    wave_lds_fence();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      Xs[(C0 + 16 + r) * LS + C0 + c0 + q] = o[q];
-      Xs[(C0 + r) * LS + C0 + 16 + c0 + q] = 0.f;  // upper-right of X back to zero
-      As[(C0 + r) * LS + C0 + 16 + c0 + q] = 0.f;  // and of L
-    }
-  }
-}
-
-// ---- 32 x 32 block products on the matrix cores (one wave each).
-// v_mfma_f32_32x32x2_f32: lane l supplies A[l % 32][k + l / 32] and
-// B[k + l / 32][l % 32]; accumulator element r of lane l is
-// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// acc += sgn * A op(B): A is 32 x K (rows at ld LS); TB: B holds B[c][k]
-// (op = transpose), else B[k][c].
+// C (16 x 16 at rows/cols given by pointers with stride LS) += sgn * A B^T
+// over K = kn (a multiple of 4) with v_mfma_f32_16x16x4f32:
+//   A[i][k] = Ap[i * LS + k], B[j][k] = Bp[j * LS + k] (TB) or Bp[k * LS + j].
+// Lane l supplies A[l % 16][k + l / 16] and B(k + l / 16, l % 16); element
+// r of its accumulator is C[4 (l / 16) + r][l % 16].
+// The operands of each 16-deep chunk are read before its four MFMAs, so the
+// LDS reads of a chunk are in flight together.
 template <bool TB>
-__device__ inline void mma32(const float* A, const float* B, int K, float sgn, f32x16& acc) {
+__device__ inline void mma16(const float* Ap, const float* Bp, int kn, float sgn, f32x4& acc) {
   const int lane = threadIdx.x & 63;
-  const int lr = lane & 31, lk = lane >> 5;
-#pragma unroll 4
-  for (int k = 0; k < K; k += 2) {
-    const float a = sgn * A[lr * LS + k + lk];
-    const float bv = TB ? B[lr * LS + k + lk] : B[(k + lk) * LS + lr];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, acc, 0, 0, 0);
-  }
-}
-
-__device__ inline void acc_load(const float* C, f32x16& acc) {
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 31, lk = lane >> 5;
+  const int li = lane & 15, lk = lane >> 4;
+  for (int k0 = 0; k0 < kn; k0 += 16) {
+    float a[4], b[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = C[(8 * (r >> 2) + 4 * lk + (r & 3)) * LS + lr];
-}
-
-__device__ inline void acc_store(float* C, const f32x16& acc) {
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 31, lk = lane >> 5;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) C[(8 * (r >> 2) + 4 * lk + (r & 3)) * LS + lr] = acc[r];
-}
-
-__device__ inline void acc_zero(f32x16& acc) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-}
-
-// Rows C0 + 32 .. NB - 1 of panel columns C0 .. C0 + 31:
-// L21 = A21 L11^-T, i.e. L21[r][c] = sum_k A21[r][k] X11[c][k]. Wave w takes
-// block row w (in place: a wave reads only the rows it writes).
-__device__ void leaf_trsm_below(float* As, const float* Xs, int C0) {
-  const int w = threadIdx.x >> 6;
-  const int r0 = C0 + 32;
-  if (w >= (NB - r0) / 32) return;
-  f32x16 acc;
-  acc_zero(acc);
-  float* blk = As + (r0 + 32 * w) * LS + C0;
-  mma32<true>(blk, Xs + C0 * LS + C0, 32, 1.f, acc);
-  acc_store(blk, acc);
-}
-
-// Trailing lower triangle, rows and columns >= r0: As[r][c] -= sum_k
-// As[r][c0 + k] As[c][c0 + k] (k < 32), in 32 x 32 blocks over the waves.
-__device__ void leaf_syrk(float* As, int c0, int r0) {
-  const int w = threadIdx.x >> 6;
-  const int nb = (NB - r0) / 32;
-  for (int t = w, i = 0, j = 0, idx = 0; idx < nb * (nb + 1) / 2; ++idx) {
-    // block idx -> (i, j), j <= i, row by row
-    if (idx > 0) {
-      if (j < i) ++j;
-      else { ++i; j = 0; }
+    for (int q = 0; q < 4; ++q) {
+      const int k = k0 + 4 * q + lk;
+      a[q] = Ap[li * LS + k];
+      b[q] = TB ? Bp[li * LS + k] : Bp[k * LS + li];
     }
-    if (idx % 4 != t) continue;
-    f32x16 acc;
-    float* C = As + (r0 + 32 * i) * LS + r0 + 32 * j;
-    acc_load(C, acc);
-    mma32<true>(As + (r0 + 32 * i) * LS + c0, As + (r0 + 32 * j) * LS + c0, 32, -1.f, acc);
-    acc_store(C, acc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sgn * a[q], b[q], acc, 0, 0, 0);
   }
+}
+
+__device__ inline void acc16_load(const float* C, f32x4& acc) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = C[(4 * (lane >> 4) + r) * LS + (lane & 15)];
+}
+
+__device__ inline void acc16_store(float* C, const f32x4& acc) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) C[(4 * (lane >> 4) + r) * LS + (lane & 15)] = acc[r];
+}
+
+__device__ inline void wave_lds_fence() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t k0, float* Dinv,
@@ -338,38 +198,118 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
   }
   for (int e = t; e < NB * LS; e += 256) Xs[e] = 0.f;
   __syncthreads();
+  if (w == 0) fac16_block(As, 0, int(k0), info);
+  __syncthreads();
 
-  // ---- Cholesky and diagonal-block inverses, four panels
 #pragma unroll 1
-  for (int p = 0; p < 4; ++p) {
-    const int C0 = 32 * p;
-    if (w == 0) leaf_diag32(As, Xs, k0, info, C0);
-    __syncthreads();
-    if (p < 3) {
-      leaf_trsm_below(As, Xs, C0);
-      __syncthreads();
-      leaf_syrk(As, C0, C0 + 32);
-      __syncthreads();
+  for (int p = 0; p + 1 < NP; ++p) {
+    const int C0 = PW * p;
+    const int R0 = C0 + PW;   // first row (and column) below the panel
+    const int R = NB - R0;    // rows below
+    // ---- forward substitution: L[r][C0 + c] L[C0 + c][C0 + c] =
+    //      A[r][C0 + c] - sum_{m < c} L[r][C0 + m] L[C0 + c][C0 + m]
+    if (t < R) {
+      const int r = R0 + t;
+      float a[PW], l[PW][PW];
+      const float* arow = As + r * LS + C0;
+#pragma unroll
+      for (int c = 0; c < PW; c += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(arow + c);
+        a[c] = v.x;
+        a[c + 1] = v.y;
+        a[c + 2] = v.z;
+        a[c + 3] = v.w;
+      }
+      // the panel's diagonal block (same address for every thread: broadcast
+      // reads), all in flight before the substitution starts
+#pragma unroll
+      for (int c = 0; c < PW; ++c)
+#pragma unroll
+        for (int m = 0; m < PW; m += 4) {
+          if (m <= c) {
+            const float4 v = *reinterpret_cast<const float4*>(As + (C0 + c) * LS + C0 + m);
+            l[c][m] = v.x;
+            l[c][m + 1] = v.y;
+            l[c][m + 2] = v.z;
+            l[c][m + 3] = v.w;
+          }
+        }
+#pragma unroll
+      for (int c = 0; c < PW; ++c) {
+        float s = a[c];
+#pragma unroll
+        for (int m = 0; m < c; ++m) s = __builtin_fmaf(-a[m], l[c][m], s);
+        a[c] = s * __builtin_amdgcn_rcpf(l[c][c]);
+      }
+      float* orow = As + r * LS + C0;
+#pragma unroll
+      for (int c = 0; c < PW; c += 4)
+        *reinterpret_cast<float4*>(orow + c) = make_float4(a[c], a[c + 1], a[c + 2], a[c + 3]);
     }
+    __syncthreads();
+    // ---- trailing lower triangle -= L_panel L_panel^T, 16 x 16 blocks (bi >= bj);
+    // block (0, 0), the next panel's diagonal block, goes to wave 0, which
+    // then factors it; the other blocks go round-robin to waves 1..3
+    const int nb = R / PW;
+    if (w == 0) {
+      f32x4 acc;
+      float* Cb = As + R0 * LS + R0;
+      acc16_load(Cb, acc);
+      mma16<true>(As + R0 * LS + C0, As + R0 * LS + C0, PW, -1.f, acc);
+      acc16_store(Cb, acc);
+      wave_lds_fence();
+      fac16_block(As, R0, int(k0) + R0, info);
+    } else {
+      for (int idx = 1 + (w - 1); idx < nb * (nb + 1) / 2; idx += 3) {
+        // idx -> (bi, bj), bj <= bi, row by row
+        int bi = 0;
+        while ((bi + 1) * (bi + 2) / 2 <= idx) ++bi;
+        const int bj = idx - bi * (bi + 1) / 2;
+        f32x4 acc;
+        float* Cb = As + (R0 + PW * bi) * LS + R0 + PW * bj;
+        acc16_load(Cb, acc);
+        mma16<true>(As + (R0 + PW * bi) * LS + C0, As + (R0 + PW * bj) * LS + C0, PW, -1.f, acc);
+        acc16_store(Cb, acc);
+      }
+    }
+    __syncthreads();
   }
 
-  // ---- off-diagonal blocks: X_ip = -X_ii sum_{k=p}^{i-1} L_ik X_kp. Wave p
-  // owns block column p (i = p+1 .. 3 in order); the sum goes through the
-  // unused upper block (p, i) of Xs, zeroed again on the way out.
-  if (w < 3) {
-    const int p = w;
-    for (int i = p + 1; i < 4; ++i) {
-      f32x16 acc;
-      acc_zero(acc);
-      mma32<false>(As + (32 * i) * LS + 32 * p, Xs + (32 * p) * LS + 32 * p, 32 * (i - p), 1.f, acc);
-      float* Tb = Xs + (32 * p) * LS + 32 * i;
-      acc_store(Tb, acc);
-      acc_zero(acc);
-      mma32<false>(Xs + (32 * i) * LS + 32 * i, Tb, 32, -1.f, acc);
-      acc_store(Xs + (32 * i) * LS + 32 * p, acc);
+  // ---- inverse of the diagonal blocks: column c of block p solves
+  // L_pp x = e_c by forward substitution (one column per thread)
+  if (t < NB) {
+    const int P0 = PW * (t / PW), c = t % PW;
+    float x[PW];
+#pragma unroll
+    for (int r = 0; r < PW; ++r) {
+      const float* lr = As + (P0 + r) * LS + P0;
+      float s = r == c ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) s = __builtin_fmaf(-lr[m], x[m], s);
+      x[r] = r < c ? 0.f : s * __builtin_amdgcn_rcpf(lr[r]);
     }
+#pragma unroll
+    for (int r = 0; r < PW; ++r) Xs[(P0 + r) * LS + P0 + c] = x[r];
   }
   __syncthreads();
+  // ---- blocks below the diagonal by block-diagonals d: T = sum_k L_ik X_kj
+  // goes through the unused upper block (j, i) of Xs, then X_ij = -X_ii T
+#pragma unroll 1
+  for (int d = 1; d < NP; ++d) {
+    for (int j = w; j + d < NP; j += 4) {
+      const int i = j + d;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // T[r][c] = sum_{k in [16 j, 16 i)} L[16 i + r][k] X[k][16 j + c]
+      mma16<false>(As + (PW * i) * LS + PW * j, Xs + (PW * j) * LS + PW * j, PW * d, 1.f, acc);
+      float* Tb = Xs + (PW * j) * LS + PW * i;
+      acc16_store(Tb, acc);
+      wave_lds_fence();
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      mma16<false>(Xs + (PW * i) * LS + PW * i, Tb, PW, -1.f, o);
+      acc16_store(Xs + (PW * i) * LS + PW * j, o);
+    }
+    __syncthreads();
+  }
 
   // ---- write L (lower, zeros above) and its inverse
   for (int e = t; e < NB * NB / 4; e += 256) {
@@ -490,24 +430,44 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
 
   KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(leaf_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(LEAF_LDS)));
+  // Two levels of blocking: superblocks of SB columns, each factored
+  // right-looking in NB-column steps whose trailing updates stay inside the
+  // superblock's columns (all rows below); after the superblock one rank-SB
+  // update brings the rest of the trailing triangle up to date. The big
+  // update reads and writes the trailing triangle once per SB columns
+  // instead of once per NB, which keeps it compute-bound at large n.
   float* A = U;
-  for (int64_t k = 0; k < nb; ++k) {
-    const int64_t k0 = k * NB;
-    leaf_kernel<<<1, 256, LEAF_LDS, s>>>(A, n, k0, Dinv + k * NB * NB, dinfo);
-    KQ_HIP(hipGetLastError());
-    const int64_t m = n - k0 - NB;
-    if (m <= 0) break;
-    float* panel = A + (k0 + NB) * n + k0;
-    // L21 = panel * Dinv_k^T into the (still unused) inverse temporary, m x NB
-    // dense: out of place, so the product takes narrow tiles across N
-    GemmArgs gt = gemm_args(panel, n, Dinv + k * NB * NB, NB, T, NB, m, NB, NB, 1.f, 0.f, G_TRANS_B);
-    KQ_TRY(gemm_f32(gt, s));
-    // trailing lower triangle -= L21 L21^T, then L21 back into place
-    float* trail = A + (k0 + NB) * n + (k0 + NB);
-    GemmArgs gs = gemm_args(T, NB, T, NB, trail, n, m, m, NB, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
-    KQ_TRY(gemm_f32(gs, s));
-    KQ_HIP(hipMemcpy2DAsync(panel, size_t(n) * sizeof(float), T, NB * sizeof(float),
-                            NB * sizeof(float), size_t(m), hipMemcpyDeviceToDevice, s));
+  for (int64_t S0 = 0; S0 < n; S0 += SB) {
+    const int64_t S1 = std::min<int64_t>(S0 + SB, n);
+    for (int64_t k0 = S0; k0 < S1; k0 += NB) {
+      const int64_t k = k0 / NB;
+      leaf_kernel<<<1, 256, LEAF_LDS, s>>>(A, n, k0, Dinv + k * NB * NB, dinfo);
+      KQ_HIP(hipGetLastError());
+      const int64_t m = n - k0 - NB;  // rows below the block
+      if (m <= 0) break;
+      float* panel = A + (k0 + NB) * n + k0;
+      // L21 = panel * Dinv_k^T into the (still unused) inverse temporary, m x NB
+      // dense: out of place, so the product takes narrow tiles across N
+      GemmArgs gt = gemm_args(panel, n, Dinv + k * NB * NB, NB, T, NB, m, NB, NB, 1.f, 0.f, G_TRANS_B);
+      KQ_TRY(gemm_f32(gt, s));
+      // the superblock's remaining columns (all rows below) -= L21 L21^T
+      const int64_t w = S1 - k0 - NB;
+      if (w > 0) {
+        float* trail = A + (k0 + NB) * n + (k0 + NB);
+        GemmArgs gs = gemm_args(T, NB, T, NB, trail, n, m, w, NB, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
+        KQ_TRY(gemm_f32(gs, s));
+      }
+      KQ_HIP(hipMemcpy2DAsync(panel, size_t(n) * sizeof(float), T, NB * sizeof(float),
+                              NB * sizeof(float), size_t(m), hipMemcpyDeviceToDevice, s));
+    }
+    // the rest of the trailing lower triangle -= L_S L_S^T, L_S = A[S1:, S0:S1]
+    const int64_t mt = n - S1;
+    if (mt > 0) {
+      const float* LS = A + S1 * n + S0;
+      float* trail = A + S1 * n + S1;
+      GemmArgs gb = gemm_args(LS, n, LS, n, trail, n, mt, mt, S1 - S0, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
+      KQ_TRY(gemm_f32(gb, s));
+    }
   }
 
   // invert L in place

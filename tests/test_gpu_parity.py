@@ -110,8 +110,8 @@ def _spd_large(rng, n, k=96):
     return Z @ Z.T / k + np.diag(np.exp(rng.uniform(0, np.log(1e3), n)))
 
 
-# (4096, 4096) and (8192, 4096) take the two-pass transposing form (blocks of
-# 4096 and 8192 on both sides); the others the row and column passes
+# (4096, 4096) and (8192, 4096): the workloads' Hadamard blocks of 4096 and
+# 8192 on both sides (compile-time row passes, two column passes)
 @pytest.mark.parametrize("d_out,d_in,bo,bi", [(256, 256, 0, 0), (384, 512, 128, 0), (1024, 4096, 0, 64),
                                               (4096, 4096, 0, 0), (8192, 4096, 0, 0)])
 def test_biip_against_oracle(d_out, d_in, bo, bi):
