@@ -16,8 +16,8 @@
 // in-group part of W0 P must not yet be present at that moment: the grid is
 // taken from W_bar - Z with Z = W0 blockdiag_128(P) (a batched GEMM).
 //
-// Per 128-column block a panel kernel sweeps the block in registers (8 lanes
-// per row, 16 columns per lane, U's diagonal block in LDS) and writes codes,
+// Per 128-column block a panel kernel sweeps the block in registers (16 lanes
+// per row, 8 columns per lane, U's diagonal block in LDS) and writes codes,
 // W^ and the scaled errors E. The lazy update W_bar[:, >blk] -= E U_{blk,>blk}
 // runs as fp32 MFMA GEMMs, grouped in 512-column superblocks so the far part
 // of W_bar is read and written once per four panels.
@@ -59,20 +59,23 @@ __global__ __launch_bounds__(256) void grid_rows_kernel(const float* W, int64_t 
   }
 }
 
-// The column sweep of one 128-column block, for PR = 32 rows per workgroup.
-// Lane l of wave w: row row0 + 8 w + l / 8, position c = l % 8 in its group
-// of 8 lanes, holding columns blk0 + 16 c + j (j = 0..15) in registers. The
+// The column sweep of one 128-column block, for PR = 16 rows per workgroup.
+// Lane l of wave w: row row0 + 4 w + l / 16, position c = l % 16 in its group
+// of 16 lanes, holding columns blk0 + 8 c + j (j = 0..7) in registers. The
 // sweep runs an outer loop over the owning position c0 (not unrolled, which
-// keeps the code small enough for the instruction cache) and 16 unrolled
-// steps inside. Step p = 16 c0 + j0: every lane rounds its candidate w[j0];
-// the owner's scaled error reaches all 8 lanes of the row through a sum of
-// the masked errors with three DPP steps (quad_perm, quad_perm,
-// row_half_mirror), so the serial path has no LDS round trip; each lane then
+// keeps the code small enough for the instruction cache) and 8 unrolled steps
+// inside. Step p = 8 c0 + j0: every lane rounds its candidate w[j0]; the
+// owner's scaled error reaches all 16 lanes of the row through a sum of the
+// masked errors with four DPP steps (quad_perm, quad_perm, row_half_mirror,
+// row_mirror), so the serial path has no LDS round trip; each lane then
 // applies it to its columns with U row p from LDS (diagonal and below stored
-// as zeros, each lane's 16 entries at a 20-float stride: conflict-free).
-constexpr int PR = 32;
-constexpr int USEG = 20;            // floats per lane segment of a staged U row
-constexpr int UROW = 8 * USEG;      // floats per staged U row
+// as zeros, each lane's 8 entries as two float4). The owner keeps its errors
+// and codes in registers; every lane writes its 8 columns of W^, E and the
+// codes straight to memory at the end.
+constexpr int PR = 16;
+constexpr int NPOS = 16;            // lanes per row
+constexpr int CPL = BK / NPOS;      // columns per lane
+constexpr int UROW = BK;            // floats per staged U row
 
 // v + (v of another lane); with bound_ctrl set the move can fold into the
 // add as a DPP source operand (one instruction per level)
@@ -82,23 +85,21 @@ __device__ inline float dpp_add(float v, int ctrl_sel) {
       return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
     case 1:  // quad_perm [2,3,0,1]
       return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
-    default:  // row_half_mirror: lane i <-> 7 - i within each 8 lanes
+    case 2:  // row_half_mirror: lane i <-> 7 - i within each 8 lanes
       return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+    default:  // row_mirror: lane i <-> 15 - i within each 16 lanes
+      return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
   }
 }
 
-__device__ inline float group8_sum(float v) {
+__device__ inline float group16_sum(float v) {
   v = dpp_add(v, 0);
   v = dpp_add(v, 1);
-  return dpp_add(v, 2);
+  v = dpp_add(v, 2);
+  return dpp_add(v, 3);
 }
 
-// per-row strides of the staged errors (floats) and codes (bytes): padded so
-// the owners of one column in 8 rows write 8 different banks
-constexpr int ESTR = BK + 4;
-constexpr int CSTR = BK + 16;  // keeps 16-byte row alignment
-constexpr size_t PANEL_LDS =
-    sizeof(float) * (size_t(BK) * UROW + BK + PR * BK + PR * ESTR) + PR * CSTR;
+constexpr size_t PANEL_LDS = sizeof(float) * (size_t(BK) * UROW + BK);
 
 __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wbar,
                                                     const float* __restrict__ U,
@@ -108,11 +109,8 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
                                                     int64_t n, int64_t blk0, int ngroups,
                                                     int grouped, float maxq) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  float* Us = sm;                 // [p][c][j] = U[blk0 + p][blk0 + 16 c + j] if 16 c + j > p, else 0
+  float* Us = sm;                 // [p][m] = U[blk0 + p][blk0 + m] if m > p, else 0
   float* uinv = Us + BK * UROW;   // 1 / U_pp
-  float* Wo = uinv + BK;          // PR x BK staged W^
-  float* Eo = Wo + PR * BK;       // PR x BK staged errors (row stride ESTR)
-  uint8_t* Co = reinterpret_cast<uint8_t*>(Eo + PR * ESTR);  // PR x BK codes (row stride CSTR)
   const int t = threadIdx.x;
   {
     // U's diagonal block: 16 float4 loads per thread, all in flight together
@@ -134,21 +132,21 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
       x.y = m + 1 > p ? x.y : 0.f;
       x.z = m + 2 > p ? x.z : 0.f;
       x.w = m + 3 > p ? x.w : 0.f;
-      *reinterpret_cast<float4*>(Us + p * UROW + (m >> 4) * USEG + (m & 15)) = x;
+      *reinterpret_cast<float4*>(Us + p * UROW + m) = x;
     }
     if (t < BK) uinv[t] = 1.f / ud;
   }
 
   const int lane = t & 63;
-  const int c = lane & 7;
-  const int rloc = 8 * (t >> 6) + (lane >> 3);
+  const int c = lane & (NPOS - 1);
+  const int rloc = 4 * (t >> 6) + (lane >> 4);
   const int64_t row = int64_t(blockIdx.x) * PR + rloc;
   const bool valid = row < d_out;
   const int64_t rr = valid ? row : d_out - 1;
-  const float* wsrc = Wbar + rr * n + blk0 + 16 * c;
-  float w[16];
+  const float* wsrc = Wbar + rr * n + blk0 + CPL * c;
+  float w[CPL];
 #pragma unroll
-  for (int j = 0; j < 16; j += 4) {
+  for (int j = 0; j < CPL; j += 4) {
     const float4 v = *reinterpret_cast<const float4*>(wsrc + j);
     w[j] = v.x;
     w[j + 1] = v.y;
@@ -161,14 +159,14 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
     // grid of this group from the working values minus the in-group P terms
     float lo = 0.f, hi = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < CPL; ++j) {
       float v = w[j];
-      if (Z) v -= Z[rr * n + blk0 + 16 * c + j];
+      if (Z) v -= Z[rr * n + blk0 + CPL * c + j];
       lo = fminf(lo, v);
       hi = fmaxf(hi, v);
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
+    for (int o = 1; o < NPOS; o <<= 1) {
       lo = fminf(lo, __shfl_xor(lo, o));
       hi = fmaxf(hi, __shfl_xor(hi, o));
     }
@@ -190,26 +188,26 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
   const float isc = 1.f / sc;
   __syncthreads();
 
-  // 1 / U_pp and the superdiagonal U_{p,p+1} of this lane's own 16 columns:
+  // 1 / U_pp and the superdiagonal U_{p,p+1} of this lane's own 8 columns:
   // only the lane owning column p uses them, and they stay in registers so
   // the dependent chain of a step (quantize -> scaled error -> row sum ->
   // next candidate) never waits for LDS
-  float uiv[16], sup[15];
+  float uiv[CPL], sup[CPL - 1];
 #pragma unroll
-  for (int j = 0; j < 16; j += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(uinv + 16 * c + j);
+  for (int j = 0; j < CPL; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(uinv + CPL * c + j);
     uiv[j] = v.x;
     uiv[j + 1] = v.y;
     uiv[j + 2] = v.z;
     uiv[j + 3] = v.w;
   }
 #pragma unroll
-  for (int j = 0; j < 15; ++j) sup[j] = Us[(16 * c + j) * UROW + c * USEG + j + 1];
-  // U row p for this lane (16 entries), fetched one step ahead
-  auto fetch = [&](int p, float (&u)[16]) {
-    const float* up = Us + p * UROW + c * USEG;
+  for (int j = 0; j < CPL - 1; ++j) sup[j] = Us[(CPL * c + j) * UROW + CPL * c + j + 1];
+  // U row p for this lane (8 entries), fetched one step ahead
+  auto fetch = [&](int p, float (&u)[CPL]) {
+    const float* up = Us + p * UROW + CPL * c;
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
+    for (int k4 = 0; k4 < CPL / 4; ++k4) {
       const float4 v = *reinterpret_cast<const float4*>(up + 4 * k4);
       u[4 * k4] = v.x;
       u[4 * k4 + 1] = v.y;
@@ -217,18 +215,18 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
       u[4 * k4 + 3] = v.w;
     }
   };
-  float ua[16], ub[16];
+  float ua[CPL], ub[CPL];
+  float eown[CPL];     // this lane's scaled errors (set when it owns the column)
+  uint32_t qown[2] = {0u, 0u};  // this lane's 8 codes, 4 per word
   fetch(0, ua);
-  float* erow = Eo + rloc * ESTR;
-  uint8_t* crow = Co + rloc * CSTR;
 #pragma unroll 1
-  for (int c0 = 0; c0 < 8; ++c0) {
+  for (int c0 = 0; c0 < NPOS; ++c0) {
     const bool own = c == c0;
 #pragma unroll
-    for (int j0 = 0; j0 < 16; ++j0) {
-      const int p = 16 * c0 + j0;
-      float(&ucur)[16] = (j0 & 1) ? ub : ua;
-      float(&unxt)[16] = (j0 & 1) ? ua : ub;
+    for (int j0 = 0; j0 < CPL; ++j0) {
+      const int p = CPL * c0 + j0;
+      float(&ucur)[CPL] = (j0 & 1) ? ub : ua;
+      float(&unxt)[CPL] = (j0 & 1) ? ua : ub;
       // zero on the lanes not owning column p, so their scaled error is 0
       // without a select on the dependent chain
       const float ui = own ? uiv[j0] : 0.f;
@@ -237,41 +235,32 @@ __global__ __launch_bounds__(256) void panel_kernel(const float* __restrict__ Wb
       const float q = __builtin_amdgcn_fmed3f(rintf(x * isc) + zr, 0.f, maxq);
       const float wq = sc * (q - zr);
       const float el = (x - wq) * ui;
-      const float e = group8_sum(el);
+      const float e = group16_sum(el);
       if (own) {
         w[j0] = wq;
-        erow[p] = el;
-        crow[p] = uint8_t(q);
+        eown[j0] = el;
+        qown[j0 >> 2] |= uint32_t(q) << (8 * (j0 & 3));
       }
       // the owner's next candidate from the register superdiagonal, then
       // the rest of the row from the LDS copy of U row p
-      if (j0 + 1 < 16) w[j0 + 1] -= e * (own ? sup[j0] : 0.f);
+      if (j0 + 1 < CPL) w[j0 + 1] -= e * (own ? sup[j0] : 0.f);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < CPL; ++j) {
         if (j == j0 + 1) w[j] -= e * (own ? 0.f : ucur[j]);
         else w[j] -= e * ucur[j];
       }
     }
   }
+  // every lane owned its 8 columns once: W^, E and the codes go straight out
+  if (valid) {
+    float* wo = Wout + row * n + blk0 + CPL * c;
+    float* eo = E + row * ldE + CPL * c;
 #pragma unroll
-  for (int j = 0; j < 16; j += 4)
-    *reinterpret_cast<float4*>(Wo + rloc * BK + 16 * c + j) = make_float4(w[j], w[j + 1], w[j + 2], w[j + 3]);
-  __syncthreads();
-  const int64_t rows_here = min<int64_t>(PR, d_out - int64_t(blockIdx.x) * PR);
-  for (int e = t; e < PR * BK / 4; e += 256) {
-    const int r = e >> 5, col = (e & 31) * 4;
-    if (r >= rows_here) continue;
-    const int64_t grow = int64_t(blockIdx.x) * PR + r;
-    *reinterpret_cast<float4*>(Wout + grow * n + blk0 + col) =
-        *reinterpret_cast<const float4*>(Wo + r * BK + col);
-    *reinterpret_cast<float4*>(E + grow * ldE + col) = *reinterpret_cast<const float4*>(Eo + r * ESTR + col);
-  }
-  for (int e = t; e < PR * BK / 16; e += 256) {
-    const int r = e >> 3, col = (e & 7) * 16;
-    if (r >= rows_here) continue;
-    const int64_t grow = int64_t(blockIdx.x) * PR + r;
-    *reinterpret_cast<uint4*>(codes + grow * n + blk0 + col) =
-        *reinterpret_cast<const uint4*>(Co + r * CSTR + col);
+    for (int j = 0; j < CPL; j += 4) {
+      *reinterpret_cast<float4*>(wo + j) = make_float4(w[j], w[j + 1], w[j + 2], w[j + 3]);
+      *reinterpret_cast<float4*>(eo + j) = make_float4(eown[j], eown[j + 1], eown[j + 2], eown[j + 3]);
+    }
+    *reinterpret_cast<uint2*>(codes + row * n + blk0 + CPL * c) = make_uint2(qown[0], qown[1]);
   }
 }
 
