@@ -11,8 +11,10 @@
 //   1. writes A = J (H + delta I) J (lower triangle) into U's buffer, with
 //      delta = damp * mean(diag H) computed on the device;
 //   2. factors A = L L^T in place with 128-column blocks inside 512-column
-//      superblocks: a single-workgroup leaf factors the diagonal block and
-//      inverts it, the panel below is solved as a GEMM with that inverse
+//      superblocks: a single-workgroup leaf factors the diagonal block in
+//      LDS and writes only the inverse of its factor (the diagonal blocks of
+//      L itself are never needed again), the panel below is solved as a GEMM
+//      with that inverse
 //      (into a compact temporary, copied back), the superblock's remaining
 //      columns take a rank-128 MFMA update from the compact copy, and after
 //      each superblock the rest of the trailing lower triangle takes one
@@ -48,20 +50,22 @@ __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, cons
 }
 
 // ---------------------------------------------------------------- the leaf
-// Factor the NB x NB diagonal block at (k0, k0) of A (ld n) in place (lower,
-// zeros written above the diagonal) and write the inverse of the factor to
-// Dinv (NB x NB, zeros above the diagonal). One workgroup of 4 waves; the
-// block lives in LDS. Right-looking over eight 16-column panels p:
+// Factor the NB x NB diagonal block at (k0, k0) of A (ld n) in LDS and write
+// the inverse of its factor to Dinv (NB x NB, zeros above the diagonal). The
+// factor itself is not written back: only its inverse is used afterwards
+// (for the panel solve and as the diagonal blocks of the inverse). One
+// workgroup of 4 waves. Right-looking over eight 16-column panels p:
 //  * wave 0 factors the panel's 16 x 16 diagonal block in registers (DPP
-//    row broadcasts, no LDS access inside the 16 column steps);
+//    row broadcasts, no LDS access inside the 16 column steps) and keeps the
+//    reciprocals of its diagonal;
 //  * the rows below solve for the panel's columns by forward substitution,
-//    one row per thread;
+//    one row per thread, while wave 2 inverts the panel's diagonal block
+//    (one column per thread);
 //  * the trailing lower triangle takes the rank-16 update in 16 x 16 blocks
-//    on the matrix cores (v_mfma_f32_16x16x4f32), the blocks spread over the
-//    waves; wave 0 takes the next panel's diagonal block and factors it
-//    right away, so the next factorization overlaps the rest of the update.
-// The inverse X = L^-1 follows: the diagonal 16 x 16 blocks by forward
-// substitution, one column per thread, then the blocks below by
+//    on the matrix cores (v_mfma_f32_16x16x4f32), two blocks at a time per
+//    wave; wave 0 takes the next panel's diagonal block and factors it right
+//    away, so the next factorization overlaps the rest of the update.
+// The blocks of the inverse X = L^-1 below the diagonal follow by
 // block-diagonals d = i - j = 1 .. 7, X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj,
 // on the matrix cores.
 constexpr int LS = NB + 4;  // LDS row stride (floats), keeps float4 alignment
@@ -77,42 +81,43 @@ __device__ inline float bc16(float v) {
                                                             0xF, 0xF, true));
 }
 
-// x[J + 1 + K] += nmm * (entry (J + 1 + K, J): lane J + 1 + K's x[J], the
-// symmetric mirror of row J's entry), nmm = minus the row's multiplier
+// x[J + 1 + K] += nl * L[J + 1 + K][J] (lane J + 1 + K's x[J]), nl = -L[r][J]
 template <int J, int... K>
-__device__ inline void fac16_upd(float (&x)[16], float nmm, std::integer_sequence<int, K...>) {
-  ((x[J + 1 + K] = __builtin_fmaf(bc16<J + 1 + K>(x[J]), nmm, x[J + 1 + K])), ...);
+__device__ inline void fac16_upd(float (&x)[16], float nl, std::integer_sequence<int, K...>) {
+  ((x[J + 1 + K] = __builtin_fmaf(bc16<J + 1 + K>(x[J]), nl, x[J + 1 + K])), ...);
 }
 
-// Step J of the 16 x 16 elimination A = L_u D L_u^T: the pivot is lane J's
-// x[J]; the rows below take multipliers x_r[J] / piv. Only the lower
-// triangle of the block is ever read.
+// Column J of the 16 x 16 Cholesky factor: the pivot is lane J's x[J];
+// every row scales its x[J] by the pivot's reciprocal square root (row J
+// gets sqrt(pivot)), then the columns right of J take the rank-1 update.
+// Only the lower triangle of the block is ever read; a non-positive (or
+// NaN) pivot is kept in dv for the caller and replaced by 1.
 template <int J>
 struct Fac16 {
-  __device__ static void run(float (&x)[16], float (&dv)[16], int r, int col0, int* info) {
-    float piv = bc16<J>(x[J]);
-    if (!(piv > 0.f)) {  // non-positive or NaN pivot
-      if ((threadIdx.x & 63) == 0) atomicMin(info, col0 + J + 1);
-      piv = 1.f;
-    }
-    const float nmm = r > J ? -(x[J] * __builtin_amdgcn_rcpf(piv)) : 0.f;
-    fac16_upd<J>(x, nmm, std::make_integer_sequence<int, 15 - J>{});
+  __device__ static void run(float (&x)[16], float (&dv)[16], float (&rv)[16]) {
+    const float piv = bc16<J>(x[J]);
     dv[J] = piv;
-    Fac16<J + 1>::run(x, dv, r, col0, info);
+    const float rs = __builtin_amdgcn_rsqf(piv > 0.f ? piv : 1.f);
+    rv[J] = rs;
+    x[J] *= rs;
+    fac16_upd<J>(x, -x[J], std::make_integer_sequence<int, 15 - J>{});
+    Fac16<J + 1>::run(x, dv, rv);
   }
 };
 template <>
 struct Fac16<16> {
-  __device__ static void run(float (&)[16], float (&)[16], int, int, int*) {}
+  __device__ static void run(float (&)[16], float (&)[16], float (&)[16]) {}
 };
 
 // Cholesky factor of the 16 x 16 block at (R0, R0) of As (row stride LS),
-// in place (zeros above the diagonal), by one wave: lane r % 16 holds row
-// r (the four 16-lane rows hold copies); L[r][k] = x_r[k] / sqrt(piv_k).
-__device__ inline void fac16_block(float* As, int R0, int col0, int* info) {
-  const int r = threadIdx.x & 15;
-  float x[16], dv[16];
-  const float* row = As + (R0 + r) * LS + R0;
+// in place (its upper triangle left undefined), by one wave: lane r % 16
+// holds row r (the four 16-lane rows hold copies). The reciprocals of the
+// factor's diagonal go to invd[R0 ..]; the first bad pivot to info.
+__device__ inline void fac16_block(float* As, float* invd, int R0, int col0, int* info) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  float x[16], dv[16], rv[16];
+  float* row = As + (R0 + r) * LS + R0;
 #pragma unroll
   for (int k = 0; k < 16; k += 4) {
     const float4 v = *reinterpret_cast<const float4*>(row + k);
@@ -121,38 +126,100 @@ __device__ inline void fac16_block(float* As, int R0, int col0, int* info) {
     x[k + 2] = v.z;
     x[k + 3] = v.w;
   }
-  Fac16<0>::run(x, dv, r, col0, info);
-  if ((threadIdx.x & 63) < 16) {
-    float* lrow = As + (R0 + r) * LS + R0;
+  Fac16<0>::run(x, dv, rv);
+  if (lane < 16) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float sq = __builtin_amdgcn_sqrtf(dv[k]);  // 1-ulp hardware square root
-      lrow[k] = k < r ? x[k] * __builtin_amdgcn_rcpf(sq) : (k == r ? sq : 0.f);
-    }
+    for (int k = 0; k < 16; k += 4)
+      *reinterpret_cast<float4*>(row + k) = make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 16; k += 4)
+      *reinterpret_cast<float4*>(invd + R0 + k) = make_float4(rv[k], rv[k + 1], rv[k + 2], rv[k + 3]);
+    for (int k = 0; k < 16; ++k)
+      if (!(dv[k] > 0.f)) {
+        atomicMin(info, col0 + k + 1);
+        break;
+      }
   }
 }
 
-// C (16 x 16 at rows/cols given by pointers with stride LS) += sgn * A B^T
-// over K = kn (a multiple of 4) with v_mfma_f32_16x16x4f32:
-//   A[i][k] = Ap[i * LS + k], B[j][k] = Bp[j * LS + k] (TB) or Bp[k * LS + j].
-// Lane l supplies A[l % 16][k + l / 16] and B(k + l / 16, l % 16); element
-// r of its accumulator is C[4 (l / 16) + r][l % 16].
-// The operands of each 16-deep chunk are read before its four MFMAs, so the
-// LDS reads of a chunk are in flight together.
-template <bool TB>
-__device__ inline void mma16(const float* Ap, const float* Bp, int kn, float sgn, f32x4& acc) {
-  const int lane = threadIdx.x & 63;
-  const int li = lane & 15, lk = lane >> 4;
-  for (int k0 = 0; k0 < kn; k0 += 16) {
-    float a[4], b[4];
+// Rows 0..15 of a 16 x 16 lower block at (P0, P0) of As into registers
+// (l[c][m] for m < c, broadcast reads, all in flight together) and the
+// reciprocals of its diagonal.
+__device__ inline void load_diag16(const float* As, const float* invd, int P0, float (&l)[PW][PW],
+                                   float (&iv)[PW]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = k0 + 4 * q + lk;
-      a[q] = Ap[li * LS + k];
-      b[q] = TB ? Bp[li * LS + k] : Bp[k * LS + li];
+  for (int c = 0; c < PW; ++c)
+#pragma unroll
+    for (int m = 0; m < PW; m += 4) {
+      if (m < c) {
+        const float4 v = *reinterpret_cast<const float4*>(As + (P0 + c) * LS + P0 + m);
+        l[c][m] = v.x;
+        l[c][m + 1] = v.y;
+        l[c][m + 2] = v.z;
+        l[c][m + 3] = v.w;
+      }
     }
 #pragma unroll
+  for (int m = 0; m < PW; m += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(invd + P0 + m);
+    iv[m] = v.x;
+    iv[m + 1] = v.y;
+    iv[m + 2] = v.z;
+    iv[m + 3] = v.w;
+  }
+}
+
+// Column c of the inverse of the 16 x 16 lower block at (P0, P0): L x = e_c
+// by forward substitution, into Xs.
+__device__ inline void inv16_col(const float* As, const float* invd, float* Xs, int P0, int c) {
+  float l[PW][PW], iv[PW], x[PW];
+  load_diag16(As, invd, P0, l, iv);
+#pragma unroll
+  for (int r = 0; r < PW; ++r) {
+    float s = r == c ? 1.f : 0.f;
+#pragma unroll
+    for (int m = 0; m < r; ++m) s = __builtin_fmaf(-l[r][m], x[m], s);
+    x[r] = r < c ? 0.f : s * iv[r];
+  }
+#pragma unroll
+  for (int r = 0; r < PW; ++r) Xs[(P0 + r) * LS + P0 + c] = x[r];
+}
+
+// Lane l supplies A[l % 16][k + l / 16] and B(k + l / 16, l % 16) to
+// v_mfma_f32_16x16x4f32; element r of its accumulator is
+// C[4 (l / 16) + r][l % 16].
+template <bool TB>
+__device__ inline void chunk16(const float* Ap, const float* Bp, int k0, float (&a)[4], float (&b)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k = k0 + 4 * q + lk;
+    a[q] = Ap[li * LS + k];
+    b[q] = TB ? Bp[li * LS + k] : Bp[k * LS + li];
+  }
+}
+
+// C (16 x 16, rows/cols given by pointers with stride LS) += sgn * A B^T
+// over K = kn (a multiple of 16):
+//   A[i][k] = Ap[i * LS + k], B[j][k] = Bp[j * LS + k] (TB) or Bp[k * LS + j].
+// The next 16-deep chunk is read while the current one's MFMAs run.
+template <bool TB>
+__device__ inline void mma16(const float* Ap, const float* Bp, int kn, float sgn, f32x4& acc) {
+  float a[4], b[4];
+  chunk16<TB>(Ap, Bp, 0, a, b);
+  for (int k0 = 0; k0 < kn; k0 += 16) {
+    float an[4], bn[4];
+    chunk16<TB>(Ap, Bp, k0 + 16 < kn ? k0 + 16 : k0, an, bn);
+#pragma unroll
     for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sgn * a[q], b[q], acc, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[q] = an[q];
+      b[q] = bn[q];
+    }
   }
 }
 
@@ -173,16 +240,56 @@ __device__ inline void wave_lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-__global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t k0, float* Dinv,
-                                                   int* info) {
+// block index idx of a lower triangle of 16 x 16 blocks, row by row -> (bi, bj)
+__device__ inline void tri_block(int idx, int& bi, int& bj) {
+  bi = 0;
+  while ((bi + 1) * (bi + 2) / 2 <= idx) ++bi;
+  bj = idx - bi * (bi + 1) / 2;
+}
+
+// C_b -= P_bi P_bj^T for two blocks at once (K = 16): both blocks' reads
+// are in flight together
+__device__ inline void syrk16_pair(float* As, int R0, int C0, int bi0, int bj0, int bi1, int bj1) {
+  float* C0p = As + (R0 + PW * bi0) * LS + R0 + PW * bj0;
+  float* C1p = As + (R0 + PW * bi1) * LS + R0 + PW * bj1;
+  f32x4 acc0, acc1;
+  acc16_load(C0p, acc0);
+  acc16_load(C1p, acc1);
+  float a0[4], b0[4], a1[4], b1[4];
+  chunk16<true>(As + (R0 + PW * bi0) * LS + C0, As + (R0 + PW * bj0) * LS + C0, 0, a0, b0);
+  chunk16<true>(As + (R0 + PW * bi1) * LS + C0, As + (R0 + PW * bj1) * LS + C0, 0, a1, b1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(-a0[q], b0[q], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(-a1[q], b1[q], acc1, 0, 0, 0);
+  }
+  acc16_store(C0p, acc0);
+  acc16_store(C1p, acc1);
+}
+
+// C_b -= P_bi P_bj^T for one block (K = 16)
+__device__ inline void syrk16_one(float* As, int R0, int C0, int bi, int bj) {
+  float* Cp = As + (R0 + PW * bi) * LS + R0 + PW * bj;
+  f32x4 acc;
+  acc16_load(Cp, acc);
+  float a[4], b[4];
+  chunk16<true>(As + (R0 + PW * bi) * LS + C0, As + (R0 + PW * bj) * LS + C0, 0, a, b);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-a[q], b[q], acc, 0, 0, 0);
+  acc16_store(Cp, acc);
+}
+
+__global__ __launch_bounds__(256) void leaf_kernel(const float* A, int64_t n, int64_t k0,
+                                                   float* Dinv, int* info) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   float* As = sm;                    // NB x LS: the block, then L
-  float* Xs = sm + NB * LS;          // NB x LS: the inverse
+  float* Xs = sm + NB * LS;          // NB x LS: the inverse (upper blocks: scratch)
+  float* invd = Xs + NB * LS;        // NB: reciprocals of L's diagonal
   const int t = threadIdx.x;
   const int w = t >> 6;
-  float* base = A + k0 * n + k0;
   {
     // the diagonal block: 16 float4 loads per thread, all in flight together
+    const float* base = A + k0 * n + k0;
     constexpr int NV = NB * NB / 4 / 256;
     float4 v[NV];
 #pragma unroll
@@ -196,9 +303,8 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
       *reinterpret_cast<float4*>(As + (e >> 5) * LS + (e & 31) * 4) = v[k];
     }
   }
-  for (int e = t; e < NB * LS; e += 256) Xs[e] = 0.f;
   __syncthreads();
-  if (w == 0) fac16_block(As, 0, int(k0), info);
+  if (w == 0) fac16_block(As, invd, 0, int(k0), info);
   __syncthreads();
 
 #pragma unroll 1
@@ -210,8 +316,8 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
     //      A[r][C0 + c] - sum_{m < c} L[r][C0 + m] L[C0 + c][C0 + m]
     if (t < R) {
       const int r = R0 + t;
-      float a[PW], l[PW][PW];
-      const float* arow = As + r * LS + C0;
+      float a[PW], l[PW][PW], iv[PW];
+      float* arow = As + r * LS + C0;
 #pragma unroll
       for (int c = 0; c < PW; c += 4) {
         const float4 v = *reinterpret_cast<const float4*>(arow + c);
@@ -220,78 +326,48 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
         a[c + 2] = v.z;
         a[c + 3] = v.w;
       }
-      // the panel's diagonal block (same address for every thread: broadcast
-      // reads), all in flight before the substitution starts
-#pragma unroll
-      for (int c = 0; c < PW; ++c)
-#pragma unroll
-        for (int m = 0; m < PW; m += 4) {
-          if (m <= c) {
-            const float4 v = *reinterpret_cast<const float4*>(As + (C0 + c) * LS + C0 + m);
-            l[c][m] = v.x;
-            l[c][m + 1] = v.y;
-            l[c][m + 2] = v.z;
-            l[c][m + 3] = v.w;
-          }
-        }
+      load_diag16(As, invd, C0, l, iv);
 #pragma unroll
       for (int c = 0; c < PW; ++c) {
         float s = a[c];
 #pragma unroll
         for (int m = 0; m < c; ++m) s = __builtin_fmaf(-a[m], l[c][m], s);
-        a[c] = s * __builtin_amdgcn_rcpf(l[c][c]);
+        a[c] = s * iv[c];
       }
-      float* orow = As + r * LS + C0;
 #pragma unroll
       for (int c = 0; c < PW; c += 4)
-        *reinterpret_cast<float4*>(orow + c) = make_float4(a[c], a[c + 1], a[c + 2], a[c + 3]);
+        *reinterpret_cast<float4*>(arow + c) = make_float4(a[c], a[c + 1], a[c + 2], a[c + 3]);
+    } else if (t >= 128 && t < 128 + PW) {
+      inv16_col(As, invd, Xs, C0, t - 128);
     }
     __syncthreads();
     // ---- trailing lower triangle -= L_panel L_panel^T, 16 x 16 blocks (bi >= bj);
     // block (0, 0), the next panel's diagonal block, goes to wave 0, which
-    // then factors it; the other blocks go round-robin to waves 1..3
+    // then factors it; the other blocks go to waves 1..3 in pairs
     const int nb = R / PW;
     if (w == 0) {
-      f32x4 acc;
-      float* Cb = As + R0 * LS + R0;
-      acc16_load(Cb, acc);
-      mma16<true>(As + R0 * LS + C0, As + R0 * LS + C0, PW, -1.f, acc);
-      acc16_store(Cb, acc);
+      syrk16_one(As, R0, C0, 0, 0);
       wave_lds_fence();
-      fac16_block(As, R0, int(k0) + R0, info);
+      fac16_block(As, invd, R0, int(k0) + R0, info);
     } else {
-      for (int idx = 1 + (w - 1); idx < nb * (nb + 1) / 2; idx += 3) {
-        // idx -> (bi, bj), bj <= bi, row by row
-        int bi = 0;
-        while ((bi + 1) * (bi + 2) / 2 <= idx) ++bi;
-        const int bj = idx - bi * (bi + 1) / 2;
-        f32x4 acc;
-        float* Cb = As + (R0 + PW * bi) * LS + R0 + PW * bj;
-        acc16_load(Cb, acc);
-        mma16<true>(As + (R0 + PW * bi) * LS + C0, As + (R0 + PW * bj) * LS + C0, PW, -1.f, acc);
-        acc16_store(Cb, acc);
+      const int nblk = nb * (nb + 1) / 2;
+      for (int idx = w; idx < nblk; idx += 6) {
+        int bi0, bj0, bi1, bj1;
+        tri_block(idx, bi0, bj0);
+        if (idx + 3 < nblk) {
+          tri_block(idx + 3, bi1, bj1);
+          syrk16_pair(As, R0, C0, bi0, bj0, bi1, bj1);
+        } else {
+          syrk16_one(As, R0, C0, bi0, bj0);
+        }
       }
     }
     __syncthreads();
   }
-
-  // ---- inverse of the diagonal blocks: column c of block p solves
-  // L_pp x = e_c by forward substitution (one column per thread)
-  if (t < NB) {
-    const int P0 = PW * (t / PW), c = t % PW;
-    float x[PW];
-#pragma unroll
-    for (int r = 0; r < PW; ++r) {
-      const float* lr = As + (P0 + r) * LS + P0;
-      float s = r == c ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < r; ++m) s = __builtin_fmaf(-lr[m], x[m], s);
-      x[r] = r < c ? 0.f : s * __builtin_amdgcn_rcpf(lr[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < PW; ++r) Xs[(P0 + r) * LS + P0 + c] = x[r];
-  }
+  // the last panel's diagonal block
+  if (t < PW) inv16_col(As, invd, Xs, NB - PW, t);
   __syncthreads();
+
   // ---- blocks below the diagonal by block-diagonals d: T = sum_k L_ik X_kj
   // goes through the unused upper block (j, i) of Xs, then X_ij = -X_ii T
 #pragma unroll 1
@@ -311,22 +387,17 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* A, int64_t n, int64_t 
     __syncthreads();
   }
 
-  // ---- write L (lower, zeros above) and its inverse
+  // ---- write the inverse (zeros above the diagonal)
   for (int e = t; e < NB * NB / 4; e += 256) {
     const int r = e >> 5, c = (e & 31) * 4;
-    const float4 l = *reinterpret_cast<const float4*>(As + r * LS + c);
     const float4 x = *reinterpret_cast<const float4*>(Xs + r * LS + c);
-    // zero the strictly upper part (columns c..c+3 against row r)
-    const float4 lo = make_float4(c > r ? 0.f : l.x, c + 1 > r ? 0.f : l.y, c + 2 > r ? 0.f : l.z,
-                                  c + 3 > r ? 0.f : l.w);
     const float4 xo = make_float4(c > r ? 0.f : x.x, c + 1 > r ? 0.f : x.y, c + 2 > r ? 0.f : x.z,
                                   c + 3 > r ? 0.f : x.w);
-    *reinterpret_cast<float4*>(base + r * n + c) = lo;
     *reinterpret_cast<float4*>(Dinv + r * NB + c) = xo;
   }
 }
 
-constexpr size_t LEAF_LDS = sizeof(float) * (size_t(NB) * LS * 2);
+constexpr size_t LEAF_LDS = sizeof(float) * (size_t(NB) * LS * 2 + NB);
 
 // Copy the inverted diagonal blocks into place (block b at (b*NB, b*NB)).
 __global__ void place_diag_kernel(const float* __restrict__ Dinv, int64_t nblk, float* A,
