@@ -442,7 +442,7 @@ kq_status trtri_levels(float* L, int64_t n, float* T, hipStream_t s) {
     const int64_t pair = 2 * sz;
     const int64_t nfull = n / pair;
     if (nfull > 0) {
-      GemmArgs g1 = gemm_args(L + sz * n, n, L, n, T, sz, sz, sz, sz, 1.f, 0.f, G_B_LOWER);
+      GemmArgs g1 = gemm_args(L + sz * n, n, L, n, T, sz, sz, sz, sz, 1.f, 0.f, G_B_LOWER | G_ORDER_NASC);
       g1.batch = int(nfull);
       g1.strideA = pair * n + pair;
       g1.strideB = pair * n + pair;
@@ -464,7 +464,7 @@ kq_status trtri_levels(float* L, int64_t n, float* T, hipStream_t s) {
       float* X11 = L + r * n + r;
       float* L21 = L + (r + sz) * n + r;
       float* X22 = L + (r + sz) * n + r + sz;
-      KQ_TRY(gemm_f32(gemm_args(L21, n, X11, n, T, sz, s2, sz, sz, 1.f, 0.f, G_B_LOWER), s));
+      KQ_TRY(gemm_f32(gemm_args(L21, n, X11, n, T, sz, s2, sz, sz, 1.f, 0.f, G_B_LOWER | G_ORDER_NASC), s));
       GemmArgs g2 = gemm_args(X22, n, T, sz, L21, n, s2, sz, s2, -1.f, 0.f, G_A_LOWER | G_ORDER_MDESC);
       g2.Cin = nullptr;
       KQ_TRY(gemm_f32(g2, s));

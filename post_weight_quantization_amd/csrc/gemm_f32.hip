@@ -13,6 +13,15 @@
 // so the MFMA operand reads (32 consecutive m or n per k) are conflict-free.
 // Global loads are float4; all callers pass 16-byte aligned pointers and
 // leading dimensions that are multiples of 4.
+//
+// Tile schedule: the grid is one-dimensional and holds only the tiles that
+// write output (a lower or upper triangle of tiles when the output is), so
+// no workgroup slot goes to a tile that returns at once. The order flags
+// sort the tiles by K range, longest first. Workgroup b runs on XCD b % 8 and
+// shares a CU with b + 256, b + 512, ... while they are resident together;
+// when the K range varies from tile to tile, every other round of 256 tiles
+// is reversed (a "snake"), so a CU that gets one of the longest tiles of a
+// round gets one of the shortest of the next.
 #include "kq_internal.h"
 
 namespace kq {
@@ -31,43 +40,132 @@ struct Stage {
 
 __device__ inline float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
+constexpr uint32_t G_SNAKE = 1u << 31;  // set by the launcher: K range varies by tile
+constexpr int ROUND = 256;              // workgroups per round: one per CU
+
+// largest k with k (k + 1) / 2 <= x (x < 2^31: every count here fits 32 bits)
+__device__ inline int tri_root(int x) {
+  int k = int((sqrtf(8.f * float(x) + 1.f) - 1.f) * 0.5f);
+  while (k > 0 && k * (k + 1) / 2 > x) --k;
+  while ((k + 1) * (k + 2) / 2 <= x) ++k;
+  return k;
+}
+
+// (local index) -> (row, column) in a lower triangle of tiles (column <= row)
+// of p x q tiles, row by row; with q < p the rows from q on are full
+__device__ inline void lower_tile(int loc, int p, int q, int& r, int& c) {
+  const int s = min(p, q), t0 = s * (s + 1) / 2;
+  if (loc < t0) {
+    const int k = tri_root(loc);
+    r = k;
+    c = loc - k * (k + 1) / 2;
+  } else {
+    r = s + (loc - t0) / q;
+    c = (loc - t0) % q;
+  }
+}
+
+// tiles of one batch that write output
+__host__ __device__ inline int64_t tiles_per_batch(uint32_t fl, int64_t ntm, int64_t ntn) {
+  if (fl & G_OUT_LOWER) {
+    const int64_t s = ntm < ntn ? ntm : ntn;
+    return s * (s + 1) / 2 + (ntm - s) * ntn;
+  }
+  if (fl & (G_OUT_UPPER | G_OUT_SUPPER)) {
+    const int64_t s = ntm < ntn ? ntm : ntn;
+    return s * (s + 1) / 2 + (ntn - s) * ntm;
+  }
+  return ntm * ntn;
+}
+
+// blockIdx.x -> (batch, row tile, column tile); the launcher keeps the grid
+// below 2^31 tiles
+__device__ inline void tile_of(uint32_t fl, int ntm, int ntn, int nb, int& z, int& tm, int& tn) {
+  int lin = int(blockIdx.x);
+  if (fl & G_SNAKE) {
+    const int total = int(gridDim.x);
+    const int r = lin / ROUND, o = lin % ROUND;
+    const int len = min(ROUND, total - r * ROUND);
+    if (r & 1) lin = r * ROUND + (len - 1 - o);
+  }
+  if (fl & G_OUT_LOWER) {
+    const int tpb = int(tiles_per_batch(fl, ntm, ntn));
+    z = lin / tpb;
+    lower_tile(lin % tpb, ntm, ntn, tm, tn);
+    return;
+  }
+  if (fl & (G_OUT_UPPER | G_OUT_SUPPER)) {
+    const int tpb = int(tiles_per_batch(fl, ntm, ntn));
+    z = lin / tpb;
+    const int loc = lin % tpb;
+    if (fl & G_ORDER_DIAG) {
+      // diagonals e = tn - tm from ntn - 1 down to 0
+      if (ntm == ntn) {
+        const int j = tri_root(loc);
+        tm = loc - j * (j + 1) / 2;
+        tn = tm + (ntn - 1 - j);
+      } else {
+        int rem = loc;
+        int e = ntn - 1;
+        for (;; --e) {
+          const int len = min(ntn - e, ntm);
+          if (rem < len) break;
+          rem -= len;
+        }
+        tm = rem;
+        tn = tm + e;
+      }
+    } else {
+      // column by column, ascending
+      lower_tile(loc, ntn, ntm, tn, tm);
+    }
+    return;
+  }
+  if (fl & (G_ORDER_NDESC | G_ORDER_NASC)) {
+    const int per = ntm * nb;
+    const int c = lin / per;
+    tn = (fl & G_ORDER_NDESC) ? ntn - 1 - c : c;
+    z = (lin % per) / ntm;
+    tm = lin % ntm;
+  } else if (fl & G_ORDER_MDESC) {
+    const int per = ntn * nb;
+    tm = ntm - 1 - lin / per;
+    z = (lin % per) / ntn;
+    tn = lin % ntn;
+  } else if (fl & G_ORDER_DIAG) {
+    // diagonals e = tn - tm from ntn - 1 down to -(ntm - 1)
+    const int tpb = ntm * ntn;
+    z = lin / tpb;
+    int rem = lin % tpb;
+    int e = ntn - 1;
+    for (;; --e) {
+      const int len = min(ntn - max(e, 0), ntm - max(-e, 0));
+      if (rem < len) break;
+      rem -= len;
+    }
+    tm = max(-e, 0) + rem;
+    tn = tm + e;
+  } else {
+    const int tpb = ntm * ntn;
+    z = lin / tpb;
+    tm = (lin % tpb) / ntn;
+    tn = lin % ntn;
+  }
+}
+
 template <bool TA, bool TB, int T>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int TM = T, TN = T;
   constexpr int LDSP = T + 4;   // padded LDS row (floats)
   constexpr int H = T / 64;     // float4 loads per operand per thread per stage
   constexpr int FD = T / 64;    // 32 x 32 MFMA blocks per wave and dimension
-  const int z = blockIdx.z;
+  const uint32_t fl = g.flags;
+  int z, tm, tn;
+  tile_of(fl, int(cdiv(g.M, TM)), int(cdiv(g.N, TN)), g.batch > 0 ? g.batch : 1, z, tm, tn);
   const float* __restrict__ A = g.A + z * g.strideA;
   const float* __restrict__ B = g.B + z * g.strideB;
   float* C = g.C + z * g.strideC;
   const float* Cin = g.Cin ? g.Cin + z * g.strideC : nullptr;
-  const uint32_t fl = g.flags;
-  // tile coordinates: dispatch order is blockIdx.x fastest; optionally remap so
-  // that the tiles with the longest K range start first
-  const int ntn = gridDim.x, ntm = gridDim.y;
-  int tn = blockIdx.x, tm = blockIdx.y;
-  if (fl & (G_ORDER_NDESC | G_ORDER_MDESC | G_ORDER_DIAG)) {
-    const int lin = blockIdx.y * ntn + blockIdx.x;
-    if (fl & G_ORDER_NDESC) {
-      tn = ntn - 1 - lin / ntm;
-      tm = lin % ntm;
-    } else if (fl & G_ORDER_MDESC) {
-      tm = ntm - 1 - lin / ntn;
-      tn = lin % ntn;
-    } else {
-      // diagonals e = tn - tm from ntn - 1 down to -(ntm - 1)
-      int rem = lin;
-      int e = ntn - 1;
-      for (;; --e) {
-        const int len = min(ntn - max(e, 0), ntm - max(-e, 0));
-        if (rem < len) break;
-        rem -= len;
-      }
-      tm = max(-e, 0) + rem;
-      tn = tm + e;
-    }
-  }
   const int64_t m0 = int64_t(tm) * TM;
   const int64_t n0 = int64_t(tn) * TN;
 
@@ -325,18 +423,22 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   // where an in-place product needs one tile across N
   const bool small = !((g.flags & G_C_ALIASES_A) && g.N > 64);
   const int T = small ? 64 : 128;
-  dim3 grid(unsigned(cdiv(g.N, T)), unsigned(cdiv(g.M, T)), unsigned(nb));
+  GemmArgs ga = g;
+  if (g.flags & (G_A_UPPER | G_A_SUPPER | G_A_LOWER | G_B_UPPER | G_B_LOWER)) ga.flags |= G_SNAKE;
+  const int64_t tiles = tiles_per_batch(g.flags, cdiv(g.M, T), cdiv(g.N, T)) * nb;
+  if (tiles > INT32_MAX) return fail(KQ_ERR_SHAPE, "internal gemm: too many tiles");
+  const dim3 grid(static_cast<unsigned>(tiles), 1, 1);
   const bool ta = g.flags & G_TRANS_A, tb = g.flags & G_TRANS_B;
   if (small) {
-    if (!ta && !tb) gemm_f32_kernel<false, false, 64><<<grid, 256, 0, s>>>(g);
-    else if (!ta && tb) gemm_f32_kernel<false, true, 64><<<grid, 256, 0, s>>>(g);
-    else if (ta && !tb) gemm_f32_kernel<true, false, 64><<<grid, 256, 0, s>>>(g);
-    else gemm_f32_kernel<true, true, 64><<<grid, 256, 0, s>>>(g);
+    if (!ta && !tb) gemm_f32_kernel<false, false, 64><<<grid, 256, 0, s>>>(ga);
+    else if (!ta && tb) gemm_f32_kernel<false, true, 64><<<grid, 256, 0, s>>>(ga);
+    else if (ta && !tb) gemm_f32_kernel<true, false, 64><<<grid, 256, 0, s>>>(ga);
+    else gemm_f32_kernel<true, true, 64><<<grid, 256, 0, s>>>(ga);
   } else {
-    if (!ta && !tb) gemm_f32_kernel<false, false, 128><<<grid, 256, 0, s>>>(g);
-    else if (!ta && tb) gemm_f32_kernel<false, true, 128><<<grid, 256, 0, s>>>(g);
-    else if (ta && !tb) gemm_f32_kernel<true, false, 128><<<grid, 256, 0, s>>>(g);
-    else gemm_f32_kernel<true, true, 128><<<grid, 256, 0, s>>>(g);
+    if (!ta && !tb) gemm_f32_kernel<false, false, 128><<<grid, 256, 0, s>>>(ga);
+    else if (!ta && tb) gemm_f32_kernel<false, true, 128><<<grid, 256, 0, s>>>(ga);
+    else if (ta && !tb) gemm_f32_kernel<true, false, 128><<<grid, 256, 0, s>>>(ga);
+    else gemm_f32_kernel<true, true, 128><<<grid, 256, 0, s>>>(ga);
   }
   KQ_HIP(hipGetLastError());
   return KQ_OK;

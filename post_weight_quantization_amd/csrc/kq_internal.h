@@ -66,6 +66,7 @@ enum GemmFlag : uint32_t {
   G_ORDER_NDESC = 1u << 12,  // column tiles in descending order
   G_ORDER_MDESC = 1u << 13,  // row tiles in descending order
   G_ORDER_DIAG = 1u << 14,   // by (column tile - row tile), descending
+  G_ORDER_NASC = 1u << 18,   // column tiles in ascending order
   // C aliases A (in place): every tile must span all N columns so that it
   // reads its rows of A before any tile writes them (requires N <= 128)
   G_C_ALIASES_A = 1u << 15,
@@ -161,6 +162,6 @@ kq_status apply_run(const uint32_t* packed, int bits, const float* scale, const 
                     const int8_t* so, int64_t bi, int64_t bo, const float* x, int64_t batch,
                     int64_t d_out, int64_t d_in, float* y, Arena& ws, hipStream_t s);
 
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace kq
