@@ -158,13 +158,15 @@ __device__ inline void tile_loop(const uint16_t* srcA, const uint16_t* srcB, int
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
-  // interleave: one MFMA, one LDS read, sixteen times
+  // interleave: the next k-step's sixteen LDS reads two per MFMA over the
+  // first eight MFMAs, so they have landed before the next group starts
   auto interleave = [&]() {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 8; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   // ---- DMA addressing: wave w fills rows 8w..8w+7 of each operand stage with
