@@ -14,11 +14,11 @@
 //      superblocks: a single-workgroup leaf factors the diagonal block in
 //      LDS and writes only the inverse of its factor (the diagonal blocks of
 //      L itself are never needed again), the panel below is solved as a GEMM
-//      with that inverse
-//      (into a compact temporary, copied back), the superblock's remaining
-//      columns take a rank-128 MFMA update from the compact copy, and after
-//      each superblock the rest of the trailing lower triangle takes one
-//      rank-512 update;
+//      with that inverse into a compact copy of the superblock's panels, the
+//      superblock's remaining columns take a rank-128 MFMA update from it,
+//      and after each superblock the rest of the trailing lower triangle
+//      takes one rank-512 update from it before one copy puts the
+//      superblock's panels in place;
 //   3. inverts L in place by bottom-up doubling with
 //      inv([[A,0],[B,C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]]: every level
 //      is two batched, triangle-aware fp32 MFMA GEMMs;
@@ -475,10 +475,18 @@ kq_status trtri_levels(float* L, int64_t n, float* T, hipStream_t s) {
 
 }  // namespace
 
+// The temporary holds one superblock's solved panels (rows below its first
+// leaf, SB columns) during the factorization and the products of the
+// triangular inverse (n^2 / 4) afterwards.
+static size_t chol_tmp_floats(int64_t n) {
+  const size_t panels = size_t(std::max<int64_t>(n - NB, 0)) * size_t(std::min<int64_t>(SB, n));
+  return std::max(panels, size_t(n) * n / 4) + 4;
+}
+
 size_t chol_ws_bytes(int64_t n) {
   Arena ar{nullptr, 0, 0};
   ar.take<float>(size_t(n) * NB);               // inverted diagonal blocks
-  ar.take<float>(size_t(n) * n / 4 + 4);        // triangular-inverse temporary
+  ar.take<float>(chol_tmp_floats(n));          // superblock panels, then the inverse temporary
   ar.take<double>(1);
   ar.take<int>(1);
   return ar.used;
@@ -488,7 +496,7 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
                        Arena& ws, hipStream_t s) {
   const int64_t nb = n / NB;
   float* Dinv = ws.take<float>(size_t(n) * NB);
-  float* T = ws.take<float>(size_t(n) * n / 4 + 4);
+  float* T = ws.take<float>(chol_tmp_floats(n));
   double* dsum = ws.take<double>(1);
   int* dinfo = ws.take<int>(1);
   if (!Dinv || !T || !dsum || !dinfo) return fail(KQ_ERR_WORKSPACE, "cholesky_inv: workspace too small");
@@ -510,35 +518,46 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
   float* A = U;
   for (int64_t S0 = 0; S0 < n; S0 += SB) {
     const int64_t S1 = std::min<int64_t>(S0 + SB, n);
+    const int64_t sw = S1 - S0;
+    // TS: the superblock's solved panels, row r >= S0 + NB of column c in
+    // [S0, S1) at TS[(r - S0 - NB) sw + (c - S0)]
+    float* TS = T;
     for (int64_t k0 = S0; k0 < S1; k0 += NB) {
       const int64_t k = k0 / NB;
       leaf_kernel<<<1, 256, LEAF_LDS, s>>>(A, n, k0, Dinv + k * NB * NB, dinfo);
       KQ_HIP(hipGetLastError());
       const int64_t m = n - k0 - NB;  // rows below the block
       if (m <= 0) break;
-      float* panel = A + (k0 + NB) * n + k0;
-      // L21 = panel * Dinv_k^T into the (still unused) inverse temporary, m x NB
-      // dense: out of place, so the product takes narrow tiles across N
-      GemmArgs gt = gemm_args(panel, n, Dinv + k * NB * NB, NB, T, NB, m, NB, NB, 1.f, 0.f, G_TRANS_B);
+      const float* panel = A + (k0 + NB) * n + k0;
+      float* Tk = TS + (k0 - S0) * sw + (k0 - S0);
+      // L21 = panel * Dinv_k^T (Dinv_k lower: op(B)[k][j] = 0 for k > j),
+      // out of place into TS, so the product takes narrow tiles across N
+      GemmArgs gt = gemm_args(panel, n, Dinv + k * NB * NB, NB, Tk, sw, m, NB, NB, 1.f, 0.f,
+                              G_TRANS_B | G_B_UPPER);
       KQ_TRY(gemm_f32(gt, s));
       // the superblock's remaining columns (all rows below) -= L21 L21^T
       const int64_t w = S1 - k0 - NB;
       if (w > 0) {
         float* trail = A + (k0 + NB) * n + (k0 + NB);
-        GemmArgs gs = gemm_args(T, NB, T, NB, trail, n, m, w, NB, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
+        GemmArgs gs = gemm_args(Tk, sw, Tk, sw, trail, n, m, w, NB, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
         KQ_TRY(gemm_f32(gs, s));
       }
-      KQ_HIP(hipMemcpy2DAsync(panel, size_t(n) * sizeof(float), T, NB * sizeof(float),
-                              NB * sizeof(float), size_t(m), hipMemcpyDeviceToDevice, s));
     }
-    // the rest of the trailing lower triangle -= L_S L_S^T, L_S = A[S1:, S0:S1]
+    const int64_t rows = n - S0 - NB;
+    if (rows <= 0) continue;
+    // the rest of the trailing lower triangle -= L_S L_S^T, L_S = TS rows from S1
     const int64_t mt = n - S1;
     if (mt > 0) {
-      const float* LS = A + S1 * n + S0;
+      const float* LS = TS + (S1 - S0 - NB) * sw;
       float* trail = A + S1 * n + S1;
-      GemmArgs gb = gemm_args(LS, n, LS, n, trail, n, mt, mt, S1 - S0, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
+      GemmArgs gb = gemm_args(LS, sw, LS, sw, trail, n, mt, mt, sw, -1.f, 1.f, G_TRANS_B | G_OUT_LOWER);
       KQ_TRY(gemm_f32(gb, s));
     }
+    // the panels back into place in one copy: the entries of TS above each
+    // panel were never written and land in the diagonal blocks or the upper
+    // triangle, which the inverse overwrites and never reads
+    KQ_HIP(hipMemcpy2DAsync(A + (S0 + NB) * n + S0, size_t(n) * sizeof(float), TS, size_t(sw) * sizeof(float),
+                            size_t(sw) * sizeof(float), size_t(rows), hipMemcpyDeviceToDevice, s));
   }
 
   // invert L in place
