@@ -24,8 +24,9 @@
  *    event. Scratch memory is passed in as (ws, ws_bytes); kq_workspace_size
  *    gives the size each call needs. The only state kept between calls is the
  *    measurement hook of kq_set_kernel_events (two caller-owned event handles
- *    per thread, unset by default); nothing else carries over from one call
- *    to the next.
+ *    per thread, unset by default) and the testing knob of kq_set_gemm_tile
+ *    (per thread, automatic by default); nothing else carries over from one
+ *    call to the next.
  *  - Device work is enqueued on `stream` and is asynchronous, except calls
  *    that return host values (kq_sensitivity, kq_cholesky_inv,
  *    kq_layer_objective), which synchronize the stream before returning.
@@ -113,6 +114,21 @@ const char* kq_version(void);
  * Errors: KQ_ERR_UNSUPPORTED for other ops, KQ_ERR_ARG if exactly one event
  * is NULL. */
 kq_status kq_set_kernel_events(kq_op op, hipEvent_t start, hipEvent_t stop);
+
+/* Testing knob; not part of the method and not needed to use it.
+ * The library's fp32 matrix products (factorization updates, triangular
+ * inverse, P, the fold and the sweep's lazy updates) run on a 64-, 128- or
+ * 256-wide output tile, chosen per product from its shape. After
+ * kq_set_gemm_tile(tile), later calls made from this thread use:
+ *   tile   0: the choice by shape (the default);
+ *          64: the 64-wide tile everywhere;
+ *          128 or 256: that tile wherever a product allows it (a product
+ *          computed in place, and the output-start-masked products of
+ *          kq_yaqa_quantize, always take the 64-wide tile).
+ * Every tile computes each output from the same operands with fp32
+ * accumulation; results differ only in summation order.
+ * Errors: KQ_ERR_ARG for any other value. */
+kq_status kq_set_gemm_tile(int tile);
 
 /* Bytes of scratch memory `op` needs for the given sizes (host output).
  * n_tok and dtype matter for KQ_OP_ACCUMULATE_COV only; cfg for

@@ -26,5 +26,6 @@ from .api import (  # noqa: F401
     kq_packed_row_words,
     kq_sensitivity,
     kq_set_kernel_events,
+    kq_set_gemm_tile,
     kq_workspace_size,
 )

@@ -26,7 +26,7 @@ EXPORTS = ("kq_last_error", "kq_version", "kq_workspace_size", "kq_accumulate_co
            "kq_sensitivity", "kq_cholesky_inv", "kq_form_p", "kq_gptaq_quantize",
            "kq_allocate_bits", "kq_layer_objective", "kq_set_kernel_events",
            "kq_packed_row_words", "kq_pack_codes", "kq_apply_quantized", "kq_yaqa_quantize",
-           "kq_apply_quantized_a4", "kq_apply_quantized_noalloc")
+           "kq_apply_quantized_a4", "kq_apply_quantized_noalloc", "kq_set_gemm_tile")
 
 
 class kq_quant_cfg(ctypes.Structure):
@@ -82,6 +82,7 @@ _sig("kq_layer_objective", _st, _p, _p, _p, _p, _p, _i64, _i64, ctypes.POINTER(c
 
 
 _sig("kq_set_kernel_events", _st, ctypes.c_int, _p, _p)
+_sig("kq_set_gemm_tile", _st, ctypes.c_int)
 _sig("kq_packed_row_words", _st, _i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64))
 _sig("kq_pack_codes", _st, _p, _i64, _i64, ctypes.c_int32, _p, _p)
 _sig("kq_apply_quantized", _st, _p, ctypes.c_int32, _p, _p, ctypes.c_int32, _p, _p, _p, _p, _i64, _i64,

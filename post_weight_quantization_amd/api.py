@@ -269,6 +269,13 @@ def kq_set_kernel_events(op: int, start=None, stop=None, stream=None):
                                       ctypes.c_void_p(stop.cuda_event)))
 
 
+def kq_set_gemm_tile(tile: int) -> None:
+    """Force the fp32 product tile of later calls on this thread: 0 chooses by
+    shape (the default), 64, 128 or 256 force one kernel where the product
+    allows it. A testing knob."""
+    check(N.lib.kq_set_gemm_tile(int(tile)))
+
+
 def kq_packed_row_words(d_in: int, bits: int) -> int:
     out = ctypes.c_int64(0)
     check(N.lib.kq_packed_row_words(d_in, bits, ctypes.byref(out)))

@@ -373,6 +373,299 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       }
 }
 
+// ------------------------------------------------------------ large tiles
+// A 256 x 256 output tile per workgroup of 8 waves (2 x 4); each wave holds
+// 128 x 64 as 8 x 4 accumulators of v_mfma_f32_16x16x4f32 (128 AGPRs), so
+// two waves share a SIMD. K advances 32 per stage through double-buffered
+// LDS, loaded through registers one stage ahead. Per stage a wave issues 256
+// MFMAs (8192 cycles of matrix-core work) against 12-48 LDS reads, so the
+// stage's loads, stores and barrier are a small fraction of its time.
+// An operand whose K index is contiguous in memory (A untransposed, B
+// transposed) keeps that layout in LDS ([row][k], row stride 36 floats) and
+// is read as one float4 per 16-row block and 16-deep chunk: lane l supplies
+// k = 4 (l / 16) + e to the chunk's MFMA e, and the other operand supplies
+// the same k. An operand with M or N contiguous keeps [k][row] (row stride
+// 260 floats) and is read as one float per MFMA. Masks and bounds are
+// applied when a stage is stored to LDS.
+// The same design also runs 128 x 128 tiles with 4 waves of 64 x 64 (about
+// 74 KB of LDS: two workgroups per CU, whose prologues and epilogues overlap
+// each other's K loops).
+constexpr int BK = 32;
+constexpr int KC_LD = BK + 4;
+template <int BT>
+struct BigCfg {
+  static constexpr int NT = BT == 256 ? 512 : 256;        // threads
+  static constexpr int WXN = NT / 128;                     // waves across N (2 rows of waves)
+  static constexpr int WM = BT / 2, WN = BT / WXN;         // wave tile (WN = 64)
+  static constexpr int NBM = WM / 16, NBN = WN / 16;       // 16 x 16 accumulators per wave
+  static constexpr int MC_LD = BT + 4;
+  static constexpr int OP_FLOATS = BT * KC_LD > BK * MC_LD ? BT * KC_LD : BK * MC_LD;
+  static constexpr size_t LDS = sizeof(float) * size_t(4 * OP_FLOATS);  // 2 operands x 2 buffers
+  static constexpr int RSTEP = NT / 8;                     // K-contiguous rows per h step
+  static constexpr int Q4 = BT / 4;                        // float4 per M/N-contiguous k-row
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool TA, bool TB, int BT>
+__global__ __launch_bounds__(BigCfg<BT>::NT) void gemm_big_kernel(GemmArgs g) {
+  using Cf = BigCfg<BT>;
+  constexpr int MC_LD = Cf::MC_LD, OP_FLOATS = Cf::OP_FLOATS, NBM = Cf::NBM, NBN = Cf::NBN;
+  constexpr int WM = Cf::WM, WN = Cf::WN, RSTEP = Cf::RSTEP, Q4 = Cf::Q4, NT = Cf::NT;
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const uint32_t fl = g.flags;
+  int z, tm, tn;
+  tile_of(fl, int(cdiv(g.M, BT)), int(cdiv(g.N, BT)), g.batch > 0 ? g.batch : 1, z, tm, tn);
+  const float* __restrict__ A = g.A + z * g.strideA;
+  const float* __restrict__ B = g.B + z * g.strideB;
+  float* C = g.C + z * g.strideC;
+  const float* Cin = g.Cin ? g.Cin + z * g.strideC : nullptr;
+  const int64_t m0 = int64_t(tm) * BT;
+  const int64_t n0 = int64_t(tn) * BT;
+
+  if ((fl & G_OUT_LOWER) && n0 > m0 + BT - 1) return;
+  if ((fl & G_OUT_UPPER) && m0 > n0 + BT - 1) return;
+  if ((fl & G_OUT_SUPPER) && m0 >= n0 + BT - 1) return;
+  if ((fl & G_OUT_NSTART) && n0 < g.ostart + z * g.ostart_ofs) return;
+  if ((fl & G_OUT_MSTART) && m0 < g.ostart + z * g.ostart_ofs) return;
+
+  const int64_t ko = g.kbase + z * g.kofs;
+  int64_t klo = 0, khi = g.K;
+  if (fl & G_A_UPPER) klo = max(klo, m0 - ko);
+  if (fl & G_A_SUPPER) klo = max(klo, m0 + 1 - ko);
+  if (fl & G_A_LOWER) khi = min(khi, m0 + BT - ko);
+  if (fl & G_B_UPPER) khi = min(khi, n0 + BT - ko);
+  if (fl & G_B_LOWER) klo = max(klo, n0 - ko);
+  klo = max<int64_t>(0, klo) & ~int64_t(3);
+  if (klo >= khi && g.beta == 1.f && Cin == C) return;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int wy = w / Cf::WXN, wx = w % Cf::WXN;  // wave rows WM wy, columns WN wx
+  const int li = lane & 15, lq = lane >> 4;
+  const bool amask = fl & (G_A_UPPER | G_A_LOWER | G_A_SUPPER);
+  const bool bmask = fl & (G_B_UPPER | G_B_LOWER);
+  auto mask_a = [&](int64_t m, int64_t kg, float v) -> float {
+    if ((fl & G_A_UPPER) && kg < m) return 0.f;
+    if ((fl & G_A_SUPPER) && kg <= m) return 0.f;
+    if ((fl & G_A_LOWER) && kg > m) return 0.f;
+    return v;
+  };
+  auto mask_b = [&](int64_t kg, int64_t n, float v) -> float {
+    if ((fl & G_B_UPPER) && kg > n) return 0.f;
+    if ((fl & G_B_LOWER) && kg < n) return 0.f;
+    return v;
+  };
+
+  // staging: four float4 per operand per thread and stage, h = 0..3.
+  // K-contiguous operand: row (t / 8) + RSTEP h, k 4 (t % 8); M/N-contiguous:
+  // k t / Q4 + 8 h, row 4 (t % Q4). Offsets are 32-bit from the uniform
+  // tile origin (a tile's rows times the leading dimension fit in 32 bits).
+  const int kq_c = 4 * (t & 7), r_c = t >> 3;        // K-contiguous: k, first row
+  const int k_m = t / Q4, r_m = 4 * (t % Q4);        // M/N-contiguous: first k, row
+  const int Mrem = int(min<int64_t>(g.M - m0, BT)), Nrem = int(min<int64_t>(g.N - n0, BT));
+  const int lda = int(g.lda), ldb = int(g.ldb);
+  float4 sa[4], sb[4];
+  auto load = [&](int k0) {
+    const int krem = int(khi) - k0;
+    const float* Ak = TA ? A + int64_t(k0) * g.lda + m0 : A + m0 * g.lda + k0;
+    const float* Bk = TB ? B + n0 * g.ldb + k0 : B + int64_t(k0) * g.ldb + n0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float4 va = make_float4(0.f, 0.f, 0.f, 0.f), vb = va;
+      if (!TA) {
+        if (r_c + RSTEP * h < Mrem && kq_c < krem) va = ld4(Ak + (r_c + RSTEP * h) * lda + kq_c);
+      } else {
+        if (r_m < Mrem && k_m + 8 * h < krem) va = ld4(Ak + (k_m + 8 * h) * lda + r_m);
+      }
+      if (TB) {
+        if (r_c + RSTEP * h < Nrem && kq_c < krem) vb = ld4(Bk + (r_c + RSTEP * h) * ldb + kq_c);
+      } else {
+        if (r_m < Nrem && k_m + 8 * h < krem) vb = ld4(Bk + (k_m + 8 * h) * ldb + r_m);
+      }
+      sa[h] = va;
+      sb[h] = vb;
+    }
+  };
+  auto store = [&](int k0, int buf) {
+    float* As = lds + (2 * buf) * OP_FLOATS;
+    float* Bs = As + OP_FLOATS;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float e[4] = {sa[h].x, sa[h].y, sa[h].z, sa[h].w};
+      if (!TA) {
+        const int r = r_c + RSTEP * h;
+        if (amask) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = mask_a(m0 + r, k0 + kq_c + q + ko, e[q]);
+        }
+        *reinterpret_cast<float4*>(As + r * KC_LD + kq_c) = make_float4(e[0], e[1], e[2], e[3]);
+      } else {
+        const int kr = k_m + 8 * h;
+        if (amask) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = mask_a(m0 + r_m + q, k0 + kr + ko, e[q]);
+        }
+        *reinterpret_cast<float4*>(As + kr * MC_LD + r_m) = make_float4(e[0], e[1], e[2], e[3]);
+      }
+      float f[4] = {sb[h].x, sb[h].y, sb[h].z, sb[h].w};
+      if (TB) {
+        const int r = r_c + RSTEP * h;
+        if (bmask) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) f[q] = mask_b(k0 + kq_c + q + ko, n0 + r, f[q]);
+        }
+        *reinterpret_cast<float4*>(Bs + r * KC_LD + kq_c) = make_float4(f[0], f[1], f[2], f[3]);
+      } else {
+        const int kr = k_m + 8 * h;
+        if (bmask) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) f[q] = mask_b(k0 + kr + ko, n0 + r_m + q, f[q]);
+        }
+        *reinterpret_cast<float4*>(Bs + kr * MC_LD + r_m) = make_float4(f[0], f[1], f[2], f[3]);
+      }
+    }
+  };
+
+  f32x4 acc[NBM][NBN];
+#pragma unroll
+  for (int i = 0; i < NBM; ++i)
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+    const float* As = lds + (2 * buf) * OP_FLOATS;
+    const float* Bs = As + OP_FLOATS;
+    // one 16-deep chunk at a time keeps the operands of one chunk live
+#pragma unroll 1
+    for (int kc = 0; kc < BK; kc += 16) {
+      float a[NBM][4], b[NBN][4];
+#pragma unroll
+      for (int i = 0; i < NBM; ++i) {
+        const int r = WM * wy + 16 * i + li;
+        if (!TA) {
+          const float4 v = *reinterpret_cast<const float4*>(As + r * KC_LD + kc + 4 * lq);
+          a[i][0] = v.x;
+          a[i][1] = v.y;
+          a[i][2] = v.z;
+          a[i][3] = v.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[i][e] = As[(kc + 4 * lq + e) * MC_LD + r];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NBN; ++j) {
+        const int c = WN * wx + 16 * j + li;
+        if (TB) {
+          const float4 v = *reinterpret_cast<const float4*>(Bs + c * KC_LD + kc + 4 * lq);
+          b[j][0] = v.x;
+          b[j][1] = v.y;
+          b[j][2] = v.z;
+          b[j][3] = v.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[j][e] = Bs[(kc + 4 * lq + e) * MC_LD + c];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < NBM; ++i)
+#pragma unroll
+          for (int j = 0; j < NBN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if (klo < khi) {
+    const int k_lo = int(klo), k_hi = int(khi);
+    load(k_lo);
+    store(k_lo, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = k_lo; k0 < k_hi; k0 += BK) {
+      const bool more = k0 + BK < k_hi;
+      if (more) load(k0 + BK);
+      compute(buf);
+      if (more) store(k0 + BK, buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // epilogue through LDS, one half of the tile's rows (one row of waves) at a
+  // time: the waves holding that half write their accumulators (acc[i][j][r]
+  // is element (WM wy + 16 i + 4 lq + r, WN wx + 16 j + li)), then every
+  // thread handles its float4 of it with coalesced, batched reads of C and
+  // writes.
+  const float alpha = g.alpha, beta = g.beta;
+  constexpr int ELD = BT + 4;  // conflict-free column writes, 16-byte rows
+  constexpr int PER = WM * BT / 4 / NT;  // float4 per thread per half
+  constexpr int BATCH = PER < 8 ? PER : 8;
+  auto writes = [&](int64_t m, int64_t n) {
+    if (m >= g.M || n >= g.N) return false;
+    if ((fl & G_OUT_LOWER) && n > m) return false;
+    if ((fl & G_OUT_UPPER) && n < m) return false;
+    if ((fl & G_OUT_SUPPER) && n <= m) return false;
+    return true;
+  };
+  const bool vec = ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(Cin ? Cin : C)) & 15) == 0;
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    if (wy == half) {
+#pragma unroll
+      for (int i = 0; i < NBM; ++i)
+#pragma unroll
+        for (int j = 0; j < NBN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) lds[(16 * i + 4 * lq + r) * ELD + WN * wx + 16 * j + li] = acc[i][j][r];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int q0 = 0; q0 < PER; q0 += BATCH) {
+      float4 cv[BATCH];
+      if (beta != 0.f) {
+#pragma unroll
+        for (int q = 0; q < BATCH; ++q) {
+          const int idx = t + NT * (q0 + q);
+          const int64_t m = m0 + WM * half + idx / Q4, n = n0 + 4 * (idx % Q4);
+          cv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (vec && m < g.M && n + 3 < g.N) cv[q] = ld4(Cin + m * g.ldc + n);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        const int idx = t + NT * (q0 + q);
+        const int row = idx / Q4, c4 = 4 * (idx % Q4);
+        const int64_t m = m0 + WM * half + row, n = n0 + c4;
+        const float4 a4 = *reinterpret_cast<const float4*>(lds + row * ELD + c4);
+        float v[4] = {alpha * a4.x, alpha * a4.y, alpha * a4.z, alpha * a4.w};
+        const bool all = vec && writes(m, n) && writes(m, n + 3) && writes(m, n + 1) && writes(m, n + 2);
+        if (all) {
+          if (beta != 0.f) {
+            v[0] += beta * cv[q].x;
+            v[1] += beta * cv[q].y;
+            v[2] += beta * cv[q].z;
+            v[3] += beta * cv[q].w;
+          }
+          *reinterpret_cast<float4*>(C + m * g.ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (!writes(m, n + e)) continue;
+            float o = v[e];
+            if (beta != 0.f) o += beta * Cin[m * g.ldc + n + e];
+            C[m * g.ldc + n + e] = o;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 __global__ void fill_kernel(float* p, int64_t n, float v) {
   int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t step = int64_t(gridDim.x) * blockDim.x;
@@ -408,6 +701,74 @@ GemmArgs gemm_args(const float* A, int64_t lda, const float* B, int64_t ldb, flo
   return g;
 }
 
+// Tile choice. A round of 256-wide tiles is one per CU (256 CUs); of
+// 128-wide tiles two per CU. Measured on the solver's shapes, the 256-wide
+// kernel runs a tile's K loop at about 0.86 of a CU's fp32 MFMA peak plus
+// about 30 us of prologue and epilogue per tile; the 128-wide kernel its two
+// tiles per CU at about 0.80 together plus about 10 us; the 64-wide kernel
+// sustains about 0.62 of the chip's peak overall. With a uniform K range the
+// estimated times are compared; with K ranges that vary by tile the larger
+// tiles need at least four rounds to balance.
+// set_gemm_tile(64, 128 or 256) forces one kernel where it applies (tests).
+thread_local int t_forced_tile = 0;
+
+int choose_tile(const GemmArgs& g, int64_t nb) {
+  // in-place products need one tile across N; output starts are given in
+  // multiples of the 64-wide tile
+  if (g.flags & (G_C_ALIASES_A | G_OUT_NSTART | G_OUT_MSTART)) return 64;
+  if (t_forced_tile) return t_forced_tile;
+  if (g.K < 256) return 64;
+  const int64_t t256 = tiles_per_batch(g.flags, cdiv(g.M, 256), cdiv(g.N, 256)) * nb;
+  const int64_t t128 = tiles_per_batch(g.flags, cdiv(g.M, 128), cdiv(g.N, 128)) * nb;
+  const int64_t t64 = tiles_per_batch(g.flags, cdiv(g.M, 64), cdiv(g.N, 64)) * nb;
+  if (g.flags & (G_A_UPPER | G_A_SUPPER | G_A_LOWER | G_B_UPPER | G_B_LOWER)) {
+    if (t256 >= 4 * 256) return 256;
+    if (t128 >= 4 * 512) return 128;
+    return 64;
+  }
+  constexpr double cu_peak = 157.3e12 / 256, chip_peak = 157.3e12;
+  const double K = double(g.K);
+  const double e256 = double(cdiv(t256, 256)) * (2.0 * 256 * 256 * K / (0.86 * cu_peak) + 30e-6);
+  const double e128 = double(cdiv(t128, 512)) * (2.0 * 2 * 128 * 128 * K / (0.80 * cu_peak) + 10e-6);
+  const double e64 = 2.0 * double(t64) * 64.0 * 64.0 * K / (0.62 * chip_peak);
+  if (e256 <= e128 && e256 <= e64) return 256;
+  return e128 <= e64 ? 128 : 64;
+}
+
+template <int BT>
+kq_status launch_big(const GemmArgs& ga, int64_t nb, hipStream_t s) {
+  // the LDS limit is a per-device function attribute: set it once per device
+  static bool attr_set[64] = {};
+  int dev = 0;
+  KQ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    const int lds = int(BigCfg<BT>::LDS);
+    KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<false, false, BT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<false, true, BT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<true, false, BT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<true, true, BT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
+  }
+  const int64_t tiles = tiles_per_batch(ga.flags, cdiv(ga.M, BT), cdiv(ga.N, BT)) * nb;
+  if (tiles > INT32_MAX) return fail(KQ_ERR_SHAPE, "internal gemm: too many tiles");
+  const dim3 grid(static_cast<unsigned>(tiles), 1, 1);
+  constexpr int nt = BigCfg<BT>::NT;
+  constexpr size_t lds = BigCfg<BT>::LDS;
+  const bool ta = ga.flags & G_TRANS_A, tb = ga.flags & G_TRANS_B;
+  if (!ta && !tb) gemm_big_kernel<false, false, BT><<<grid, nt, lds, s>>>(ga);
+  else if (!ta && tb) gemm_big_kernel<false, true, BT><<<grid, nt, lds, s>>>(ga);
+  else if (ta && !tb) gemm_big_kernel<true, false, BT><<<grid, nt, lds, s>>>(ga);
+  else gemm_big_kernel<true, true, BT><<<grid, nt, lds, s>>>(ga);
+  KQ_HIP(hipGetLastError());
+  return KQ_OK;
+}
+
+void set_gemm_tile(int tile) { t_forced_tile = tile; }
+
 kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return KQ_OK;
   if ((g.lda | g.ldb | g.ldc | g.K) & 3)
@@ -417,14 +778,15 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   const int64_t nb = g.batch > 0 ? g.batch : 1;
   if ((g.flags & G_C_ALIASES_A) && g.N > 128)
     return fail(KQ_ERR_SHAPE, "internal gemm: an in-place product needs N <= 128");
-  // 64-wide tiles: at 5 waves per SIMD they hide latency better than the
-  // 128-wide tiles (2 waves per SIMD), also on large dense products, and
-  // shorten the longest tile of triangular products; 128-wide tiles only
-  // where an in-place product needs one tile across N
-  const bool small = !((g.flags & G_C_ALIASES_A) && g.N > 64);
-  const int T = small ? 64 : 128;
   GemmArgs ga = g;
   if (g.flags & (G_A_UPPER | G_A_SUPPER | G_A_LOWER | G_B_UPPER | G_B_LOWER)) ga.flags |= G_SNAKE;
+  const int tile = choose_tile(g, nb);
+  if (tile == 256) return launch_big<256>(ga, nb, s);
+  if (tile == 128) return launch_big<128>(ga, nb, s);
+  // the 64-wide kernel; its 128-wide form only where an in-place product
+  // needs one tile across N
+  const bool small = !((g.flags & G_C_ALIASES_A) && g.N > 64);
+  const int T = small ? 64 : 128;
   const int64_t tiles = tiles_per_batch(g.flags, cdiv(g.M, T), cdiv(g.N, T)) * nb;
   if (tiles > INT32_MAX) return fail(KQ_ERR_SHAPE, "internal gemm: too many tiles");
   const dim3 grid(static_cast<unsigned>(tiles), 1, 1);

@@ -146,6 +146,14 @@ const char* kq_last_error(void) { return g_err; }
 
 const char* kq_version(void) { return "kq 0.1 gfx950"; }
 
+kq_status kq_set_gemm_tile(int tile) {
+  clear_error();
+  if (tile != 0 && tile != 64 && tile != 128 && tile != 256)
+    return fail(KQ_ERR_ARG, "set_gemm_tile: tile must be 0 (by shape), 64, 128 or 256");
+  set_gemm_tile(tile);
+  return KQ_OK;
+}
+
 kq_status kq_set_kernel_events(kq_op op, hipEvent_t start, hipEvent_t stop) {
   clear_error();
   if (op != KQ_OP_ACCUMULATE_COV && op != KQ_OP_GPTAQ_QUANTIZE && op != KQ_OP_APPLY_QUANTIZED &&

@@ -93,6 +93,8 @@ struct GemmArgs {
 };
 
 kq_status gemm_f32(const GemmArgs& g, hipStream_t s);
+// tile of later gemm_f32 calls on this thread: 0 by shape, 64, 128 or 256 forced
+void set_gemm_tile(int tile);
 GemmArgs gemm_args(const float* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                    int64_t M, int64_t N, int64_t K, float alpha, float beta, uint32_t flags);
 

@@ -76,6 +76,13 @@ def test_kernel_event_hook_validation():
     assert N.lib.kq_set_kernel_events(N.KQ_OP_YAQA_QUANTIZE, None, None) == N.KQ_ERR_UNSUPPORTED
 
 
+def test_gemm_tile_knob_validation():
+    for bad in (1, 32, 96, 512, -64):
+        assert N.lib.kq_set_gemm_tile(bad) == N.KQ_ERR_ARG
+    for ok in (64, 128, 256, 0):
+        assert N.lib.kq_set_gemm_tile(ok) == N.KQ_OK
+
+
 def test_inference_entry_points_validate_on_host():
     from oracle import deploy
     out = ctypes.c_int64()
