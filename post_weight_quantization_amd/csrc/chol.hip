@@ -61,13 +61,13 @@ __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, cons
 //  * the rows below solve for the panel's columns by forward substitution,
 //    one row per thread, while wave 2 inverts the panel's diagonal block
 //    (one column per thread);
-//  * the trailing lower triangle takes the rank-16 update in 16 x 16 blocks
-//    on the matrix cores (v_mfma_f32_16x16x4f32), two blocks at a time per
-//    wave; wave 0 takes the next panel's diagonal block and factors it right
-//    away, so the next factorization overlaps the rest of the update.
-// The blocks of the inverse X = L^-1 below the diagonal follow by
-// block-diagonals d = i - j = 1 .. 7, X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj,
-// on the matrix cores.
+//  * wave 0 applies the panel to the next diagonal block and factors it
+//    right away; waves 1..3 bring the next block column below the diagonal
+//    up to date in one product over all panels so far (left-looking) and
+//    apply the panel to the later diagonal blocks, all in 16 x 16 blocks on
+//    the matrix cores (v_mfma_f32_16x16x4f32).
+// The blocks of the inverse X = L^-1 below the diagonal follow by doubling,
+// X21 = -X22 (L21 X11) over 16 -> 32 -> 64 -> 128, on the matrix cores.
 constexpr int LS = NB + 4;  // LDS row stride (floats), keeps float4 alignment
 constexpr int PW = 16;      // panel width
 constexpr int NP = NB / PW;
@@ -240,33 +240,6 @@ __device__ inline void wave_lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// block index idx of a lower triangle of 16 x 16 blocks, row by row -> (bi, bj)
-__device__ inline void tri_block(int idx, int& bi, int& bj) {
-  bi = 0;
-  while ((bi + 1) * (bi + 2) / 2 <= idx) ++bi;
-  bj = idx - bi * (bi + 1) / 2;
-}
-
-// C_b -= P_bi P_bj^T for two blocks at once (K = 16): both blocks' reads
-// are in flight together
-__device__ inline void syrk16_pair(float* As, int R0, int C0, int bi0, int bj0, int bi1, int bj1) {
-  float* C0p = As + (R0 + PW * bi0) * LS + R0 + PW * bj0;
-  float* C1p = As + (R0 + PW * bi1) * LS + R0 + PW * bj1;
-  f32x4 acc0, acc1;
-  acc16_load(C0p, acc0);
-  acc16_load(C1p, acc1);
-  float a0[4], b0[4], a1[4], b1[4];
-  chunk16<true>(As + (R0 + PW * bi0) * LS + C0, As + (R0 + PW * bj0) * LS + C0, 0, a0, b0);
-  chunk16<true>(As + (R0 + PW * bi1) * LS + C0, As + (R0 + PW * bj1) * LS + C0, 0, a1, b1);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(-a0[q], b0[q], acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(-a1[q], b1[q], acc1, 0, 0, 0);
-  }
-  acc16_store(C0p, acc0);
-  acc16_store(C1p, acc1);
-}
-
 // C_b -= P_bi P_bj^T for one block (K = 16)
 __device__ inline void syrk16_one(float* As, int R0, int C0, int bi, int bj) {
   float* Cp = As + (R0 + PW * bi) * LS + R0 + PW * bj;
@@ -341,24 +314,32 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* A, int64_t n, in
       inv16_col(As, invd, Xs, C0, t - 128);
     }
     __syncthreads();
-    // ---- trailing lower triangle -= L_panel L_panel^T, 16 x 16 blocks (bi >= bj);
-    // block (0, 0), the next panel's diagonal block, goes to wave 0, which
-    // then factors it; the other blocks go to waves 1..3 in pairs
-    const int nb = R / PW;
+    // ---- updates. Wave 0 applies the panel to the next diagonal block and
+    // factors it. Waves 1..3 bring the next block column below the diagonal
+    // up to date in one product over all panels so far (its blocks are
+    // untouched until then: left-looking), and apply the panel to the later
+    // diagonal blocks (right-looking), so each phase carries about the same
+    // work instead of the whole trailing triangle at the first panels.
     if (w == 0) {
       syrk16_one(As, R0, C0, 0, 0);
       wave_lds_fence();
       fac16_block(As, invd, R0, int(k0) + R0, info);
     } else {
-      const int nblk = nb * (nb + 1) / 2;
-      for (int idx = w; idx < nblk; idx += 6) {
-        int bi0, bj0, bi1, bj1;
-        tri_block(idx, bi0, bj0);
-        if (idx + 3 < nblk) {
-          tri_block(idx + 3, bi1, bj1);
-          syrk16_pair(As, R0, C0, bi0, bj0, bi1, bj1);
+      const int nxt = p + 1;              // the next block column
+      const int ntask = 2 * (NP - 1 - nxt);
+      for (int task = w - 1; task < ntask; task += 3) {
+        if (task < NP - 1 - nxt) {
+          // block (i, nxt) -= sum over panels 0..p of L_i,c L_nxt,c^T
+          const int i = nxt + 1 + task;
+          float* Cb = As + (PW * i) * LS + PW * nxt;
+          f32x4 acc;
+          acc16_load(Cb, acc);
+          mma16<true>(As + (PW * i) * LS, As + (PW * nxt) * LS, PW * nxt, -1.f, acc);
+          acc16_store(Cb, acc);
         } else {
-          syrk16_one(As, R0, C0, bi0, bj0);
+          // diagonal block (j, j) -= L_j,p L_j,p^T
+          const int j = nxt + 1 + (task - (NP - 1 - nxt));
+          syrk16_one(As, R0, C0, j - nxt, j - nxt);
         }
       }
     }
@@ -368,24 +349,65 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* A, int64_t n, in
   if (t < PW) inv16_col(As, invd, Xs, NB - PW, t);
   __syncthreads();
 
-  // ---- blocks below the diagonal by block-diagonals d: T = sum_k L_ik X_kj
-  // goes through the unused upper block (j, i) of Xs, then X_ij = -X_ii T
-#pragma unroll 1
-  for (int d = 1; d < NP; ++d) {
-    for (int j = w; j + d < NP; j += 4) {
-      const int i = j + d;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      // T[r][c] = sum_{k in [16 j, 16 i)} L[16 i + r][k] X[k][16 j + c]
-      mma16<false>(As + (PW * i) * LS + PW * j, Xs + (PW * j) * LS + PW * j, PW * d, 1.f, acc);
-      float* Tb = Xs + (PW * j) * LS + PW * i;
-      acc16_store(Tb, acc);
-      wave_lds_fence();
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-      mma16<false>(Xs + (PW * i) * LS + PW * i, Tb, PW, -1.f, o);
-      acc16_store(Xs + (PW * i) * LS + PW * j, o);
-    }
-    __syncthreads();
+  // ---- the blocks of the inverse below the diagonal, by doubling: merge
+  // adjacent inverted blocks with X21 = -X22 (L21 X11), 16 -> 32 -> 64 -> 128.
+  // In a merge the product T = L21 X11 goes, one block column b at a time,
+  // to an unused upper part of Xs (rows of the first half, columns of the
+  // second: a k-major slab), and the wave that computed T's column b also
+  // computes X21's column b from it, so only the levels need barriers.
+  {
+    // level 1: wave w merges blocks 2w and 2w + 1
+    const int a0 = 2 * w;
+    f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+    mma16<false>(As + (PW * (a0 + 1)) * LS + PW * a0, Xs + (PW * a0) * LS + PW * a0, PW, 1.f, tacc);
+    float* Tb = Xs + (PW * a0) * LS + PW * (a0 + 1);
+    acc16_store(Tb, tacc);
+    wave_lds_fence();
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    mma16<false>(Xs + (PW * (a0 + 1)) * LS + PW * (a0 + 1), Tb, PW, -1.f, o);
+    acc16_store(Xs + (PW * (a0 + 1)) * LS + PW * a0, o);
   }
+  __syncthreads();
+  {
+    // level 2: merge q = w / 2 joins blocks {4q, 4q+1} and {4q+2, 4q+3};
+    // this wave takes block column b = w % 2 of T and of X21
+    const int q0 = 4 * (w >> 1), b = w & 1, c0 = q0 + 2;
+    float* slab = Xs + (PW * q0) * LS + PW * (c0 + b);  // T[c][b] at block (q0 + c, c0 + b)
+#pragma unroll 1
+    for (int a = 0; a < 2; ++a) {
+      f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+      mma16<false>(As + (PW * (c0 + a)) * LS + PW * (q0 + b), Xs + (PW * (q0 + b)) * LS + PW * (q0 + b),
+                   PW * (2 - b), 1.f, tacc);
+      acc16_store(slab + (PW * a) * LS, tacc);
+    }
+    wave_lds_fence();
+#pragma unroll 1
+    for (int a = 0; a < 2; ++a) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      mma16<false>(Xs + (PW * (c0 + a)) * LS + PW * c0, slab, PW * (a + 1), -1.f, o);
+      acc16_store(Xs + (PW * (c0 + a)) * LS + PW * (q0 + b), o);
+    }
+  }
+  __syncthreads();
+  {
+    // level 3: blocks 0..3 and 4..7; this wave takes block column b = w
+    const int b = w;
+    float* slab = Xs + PW * (4 + b);  // T[c][b] at block (c, 4 + b)
+#pragma unroll 1
+    for (int a = 0; a < 4; ++a) {
+      f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+      mma16<false>(As + (PW * (4 + a)) * LS + PW * b, Xs + (PW * b) * LS + PW * b, PW * (4 - b), 1.f, tacc);
+      acc16_store(slab + (PW * a) * LS, tacc);
+    }
+    wave_lds_fence();
+#pragma unroll 1
+    for (int a = 0; a < 4; ++a) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      mma16<false>(Xs + (PW * (4 + a)) * LS + PW * 4, slab, PW * (a + 1), -1.f, o);
+      acc16_store(Xs + (PW * (4 + a)) * LS + PW * b, o);
+    }
+  }
+  __syncthreads();
 
   // ---- write the inverse (zeros above the diagonal)
   for (int e = t; e < NB * NB / 4; e += 256) {
