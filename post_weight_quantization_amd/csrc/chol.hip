@@ -176,12 +176,15 @@ __device__ inline void load_diag16(const float* As, const float* invd, int P0, f
 __device__ inline void inv16_col(const float* As, const float* invd, float* Xs, int P0, int c) {
   float l[PW][PW], iv[PW], x[PW];
   load_diag16(As, invd, P0, l, iv);
+  // right-looking: once x[r] is final it updates every later entry, so the
+  // dependent chain is one multiply and one FMA per row
+#pragma unroll
+  for (int r = 0; r < PW; ++r) x[r] = r == c ? 1.f : 0.f;
 #pragma unroll
   for (int r = 0; r < PW; ++r) {
-    float s = r == c ? 1.f : 0.f;
+    x[r] *= iv[r];
 #pragma unroll
-    for (int m = 0; m < r; ++m) s = __builtin_fmaf(-l[r][m], x[m], s);
-    x[r] = r < c ? 0.f : s * iv[r];
+    for (int m = r + 1; m < PW; ++m) x[m] = __builtin_fmaf(-l[m][r], x[r], x[m]);
   }
 #pragma unroll
   for (int r = 0; r < PW; ++r) Xs[(P0 + r) * LS + P0 + c] = x[r];
@@ -286,7 +289,8 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* A, int64_t n, in
     const int R0 = C0 + PW;   // first row (and column) below the panel
     const int R = NB - R0;    // rows below
     // ---- forward substitution: L[r][C0 + c] L[C0 + c][C0 + c] =
-    //      A[r][C0 + c] - sum_{m < c} L[r][C0 + m] L[C0 + c][C0 + m]
+    //      A[r][C0 + c] - sum_{m < c} L[r][C0 + m] L[C0 + c][C0 + m],
+    //      each term subtracted as soon as L[r][C0 + m] is known
     if (t < R) {
       const int r = R0 + t;
       float a[PW], l[PW][PW], iv[PW];
@@ -300,12 +304,12 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* A, int64_t n, in
         a[c + 3] = v.w;
       }
       load_diag16(As, invd, C0, l, iv);
+      // right-looking: a[c] final, then it updates every later column
 #pragma unroll
       for (int c = 0; c < PW; ++c) {
-        float s = a[c];
+        a[c] *= iv[c];
 #pragma unroll
-        for (int m = 0; m < c; ++m) s = __builtin_fmaf(-a[m], l[c][m], s);
-        a[c] = s * iv[c];
+        for (int m = c + 1; m < PW; ++m) a[m] = __builtin_fmaf(-a[c], l[m][c], a[m]);
       }
 #pragma unroll
       for (int c = 0; c < PW; c += 4)
@@ -351,10 +355,11 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* A, int64_t n, in
 
   // ---- the blocks of the inverse below the diagonal, by doubling: merge
   // adjacent inverted blocks with X21 = -X22 (L21 X11), 16 -> 32 -> 64 -> 128.
-  // In a merge the product T = L21 X11 goes, one block column b at a time,
-  // to an unused upper part of Xs (rows of the first half, columns of the
-  // second: a k-major slab), and the wave that computed T's column b also
-  // computes X21's column b from it, so only the levels need barriers.
+  // In a merge the product T = L21 X11 goes to an unused upper part of Xs
+  // (rows of the first half, columns of the second: each block column of T
+  // a k-major slab). In the first two levels the wave that computes T's
+  // column b also computes X21's column b from it; the last level splits T
+  // by rows and X21 by columns, with a barrier between.
   {
     // level 1: wave w merges blocks 2w and 2w + 1
     const int a0 = 2 * w;
@@ -390,16 +395,22 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* A, int64_t n, in
   }
   __syncthreads();
   {
-    // level 3: blocks 0..3 and 4..7; this wave takes block column b = w
-    const int b = w;
-    float* slab = Xs + PW * (4 + b);  // T[c][b] at block (c, 4 + b)
+    // level 3: blocks 0..3 and 4..7. T's blocks have K = 16 (4 - b) and
+    // X21's K = 16 (a + 1), so T goes by block rows (wave a) and X21 by block
+    // columns (wave b) after a barrier: ten 16-deep chunks per wave in each
+    // half. T[a][b] sits at block (a, 4 + b): column b of T is a k-major slab.
+    const int a = w;
 #pragma unroll 1
-    for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 4; ++b) {
       f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
       mma16<false>(As + (PW * (4 + a)) * LS + PW * b, Xs + (PW * b) * LS + PW * b, PW * (4 - b), 1.f, tacc);
-      acc16_store(slab + (PW * a) * LS, tacc);
+      acc16_store(Xs + (PW * a) * LS + PW * (4 + b), tacc);
     }
-    wave_lds_fence();
+  }
+  __syncthreads();
+  {
+    const int b = w;
+    const float* slab = Xs + PW * (4 + b);
 #pragma unroll 1
     for (int a = 0; a < 4; ++a) {
       f32x4 o = {0.f, 0.f, 0.f, 0.f};

@@ -702,11 +702,13 @@ GemmArgs gemm_args(const float* A, int64_t lda, const float* B, int64_t ldb, flo
 }
 
 // Tile choice. A round of 256-wide tiles is one per CU (256 CUs); of
-// 128-wide tiles two per CU. Measured on the solver's shapes, the 256-wide
-// kernel runs a tile's K loop at about 0.86 of a CU's fp32 MFMA peak plus
-// about 30 us of prologue and epilogue per tile; the 128-wide kernel its two
-// tiles per CU at about 0.80 together plus about 10 us; the 64-wide kernel
-// sustains about 0.62 of the chip's peak overall. With a uniform K range the
+// 128-wide tiles two per CU. Measured on the solver's shapes (matrix cores
+// busy 0.80-0.85 of the launch for the 256-wide tile, 0.67 for the 128-wide
+// one on the same 8192 x 28672 layer), the 256-wide kernel runs a tile's K
+// loop at about 0.86 of a CU's fp32 MFMA peak plus about 30 us of prologue
+// and epilogue per tile; the 128-wide kernel its two tiles per CU at about
+// 0.68 together plus about 10 us; the 64-wide kernel sustains about 0.62 of
+// the chip's peak overall. With a uniform K range the
 // estimated times are compared; with K ranges that vary by tile the larger
 // tiles need at least four rounds to balance.
 // set_gemm_tile(64, 128 or 256) forces one kernel where it applies (tests).
@@ -729,7 +731,7 @@ int choose_tile(const GemmArgs& g, int64_t nb) {
   constexpr double cu_peak = 157.3e12 / 256, chip_peak = 157.3e12;
   const double K = double(g.K);
   const double e256 = double(cdiv(t256, 256)) * (2.0 * 256 * 256 * K / (0.86 * cu_peak) + 30e-6);
-  const double e128 = double(cdiv(t128, 512)) * (2.0 * 2 * 128 * 128 * K / (0.80 * cu_peak) + 10e-6);
+  const double e128 = double(cdiv(t128, 512)) * (2.0 * 2 * 128 * 128 * K / (0.68 * cu_peak) + 10e-6);
   const double e64 = 2.0 * double(t64) * 64.0 * 64.0 * K / (0.62 * chip_peak);
   if (e256 <= e128 && e256 <= e64) return 256;
   return e128 <= e64 ? 128 : 64;
