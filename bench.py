@@ -41,8 +41,8 @@ PEAK_HBM = 8.0e12       # bytes/s
 # workload (4096 x 4096, 131072 bf16 tokens), from FETCH_SIZE and WRITE_SIZE
 # counter passes scaled by the same counters on a copy of known size. Valid
 # only for the kernel source it was measured on (sha256 of cov.hip).
-COV_TRAFFIC = {"cov_sha256": "e965d565bae46d873946a446fad0ccc8860d0f7a8f9e970fddc01fe905a78287",
-               "bytes": 17105681408}
+COV_TRAFFIC = {"cov_sha256": "8bd196031121dda4e32fead7ae7177dd9880f94cad1ffa5a445445be7dc564e2",
+               "bytes": 17109835776}
 
 
 def stage_costs(spec):

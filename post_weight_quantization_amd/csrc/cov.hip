@@ -382,7 +382,9 @@ __global__ __launch_bounds__(256) void drift_bf16_kernel(const uint4* __restrict
 
 // Sum the pool slots of one tile in slot order, apply alpha/beta, write the
 // tile and, for off-diagonal tiles of H_X and H_G, its transpose. One
-// workgroup per 64 x 64 sub-block of a 256 x 256 tile.
+// workgroup per 64 x 64 sub-block of a 256 x 256 tile; each thread sums four
+// float4 of it, with the loads of four slots in flight together (the sum of
+// every element still runs over the slots in order: deterministic).
 __global__ __launch_bounds__(256) void cov_pool_reduce_kernel(const CovRed* __restrict__ reds,
                                                               const float* __restrict__ pool,
                                                               float* HX, float* D, float* HG,
@@ -394,25 +396,55 @@ __global__ __launch_bounds__(256) void cov_pool_reduce_kernel(const CovRed* __re
   float* C = rd.kind == K_HX ? HX : rd.kind == K_D ? D : HG;
   const int64_t dim = rd.kind == K_HG ? d_out : d_in;
   const int lr0 = (sub >> 2) * 64, lc0 = (sub & 3) * 64;
-  const int tx = threadIdx.x & 63;
-  const int ty = threadIdx.x >> 6;  // 0..3
-  const int64_t c = int64_t(rd.J) * CT + lc0 + tx;
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int64_t r = int64_t(rd.I) * CT + lr0 + rr;
-    const float* src = pool + rd.slot0 * int64_t(CT * CT) + (lr0 + rr) * CT + lc0 + tx;
-    float s = 0.f;
-    for (int k = 0; k < rd.count; ++k) s += src[int64_t(k) * CT * CT];
-    s *= alpha;
-    if (r < dim && c < dim) {
-      float o = s;
-      if (beta != 0.f) o += beta * C[r * dim + c];
-      C[r * dim + c] = o;
+  const int t = threadIdx.x;
+  const int c4 = 4 * (t & 15);  // column within the sub-block
+  const int rq = t >> 4;        // rows rq + 16 h
+  const float* base = pool + rd.slot0 * int64_t(CT * CT) + lr0 * CT + lc0 + c4;
+  float4 acc[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < rd.count; k0 += 4) {
+    float4 v[4][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        v[kk][h] = k0 + kk < rd.count
+                       ? *reinterpret_cast<const float4*>(base + int64_t(k0 + kk) * CT * CT + (rq + 16 * h) * CT)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (k0 + kk >= rd.count) break;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc[h].x += v[kk][h].x;
+        acc[h].y += v[kk][h].y;
+        acc[h].z += v[kk][h].z;
+        acc[h].w += v[kk][h].w;
+      }
     }
-    tileT[rr][tx] = s;
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int rr = rq + 16 * h;
+    const int64_t r = int64_t(rd.I) * CT + lr0 + rr;
+    const float sv[4] = {alpha * acc[h].x, alpha * acc[h].y, alpha * acc[h].z, alpha * acc[h].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t c = int64_t(rd.J) * CT + lc0 + c4 + e;
+      if (r < dim && c < dim) {
+        float o = sv[e];
+        if (beta != 0.f) o += beta * C[r * dim + c];
+        C[r * dim + c] = o;
+      }
+      tileT[rr][c4 + e] = sv[e];
+    }
   }
   if (rd.kind == K_D || rd.I == rd.J) return;
   __syncthreads();
   // transpose: element (J*CT + lc0 + rr, I*CT + lr0 + tx) = tile[tx][rr]
+  const int tx = t & 63;
+  const int ty = t >> 6;  // 0..3
   const int64_t c2 = int64_t(rd.I) * CT + lr0 + tx;
   for (int rr = ty; rr < 64; rr += 4) {
     const int64_t r2 = int64_t(rd.J) * CT + lc0 + rr;
