@@ -25,9 +25,11 @@
 // column blocks L < J. The feedback of its two neighbours finished one step
 // earlier (left: e_{I,J-1} U_I[J-1,J]; above: U_O[I-1,I]^T M_{I-1,J}) the tile
 // computes itself as MFMA products in LDS; everything farther away arrives
-// through batched fp32 MFMA GEMMs enqueued after each step, which carry the
-// results of step s to the tiles of steps >= s + 2:
+// through 64 x 64 x 64 fp32 MFMA products that carry the results of step s to
+// the tiles of steps >= s + 2:
 // M[I, blocks >= J+2] += e_IJ U_I[J, .] and Wk[blocks >= I+2, J] -= U_O[I, .]^T M_IJ.
+// They run in the launch of step s + 1, on the workgroups after its tiles
+// (the CUs the tiles leave free), so one launch per step carries all of it.
 //
 // Inside a tile, the four lanes of a quad hold one row (16 columns each) as
 // v = Z0 - (column feedback received) and t = sum_{l<j} e_il U_I[l,j], so
@@ -57,7 +59,7 @@ constexpr size_t YAQA_LDS = sizeof(float) * (8 * YT * YP + YT + 4 * YT) + YT * Y
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct YaqaStep {
-  const float* Wk;  // m_p x n_p working input (column feedback applied)
+  float* Wk;        // m_p x n_p working input (column feedback applied)
   float* Mp;        // m_p x n_p row-feedback accumulator; a finished tile holds its complete M
   float* E;         // m_p x n_p scaled errors
   int64_t ld;       // n_p
@@ -71,6 +73,12 @@ struct YaqaStep {
   const float* zero;
   float maxq;
   int s, I_lo;
+  int ntile;        // workgroups [0, ntile) are this step's tiles
+  // the far feedback of the previous step (tiles (I, ps - I), I in
+  // [p_I_lo, p_I_lo + p_cnt)), spread over the workgroups from ntile on:
+  // p_qr (p_qc) target blocks per tile at most for the row (column) kind
+  int ps, p_I_lo, p_cnt, p_qr, p_qc, nfar;
+  int mt, nt;       // tile counts of the padded matrices
 };
 
 // acc += op(A) B with K = YT for this wave's 32 x 32 block at (wm, wn), both
@@ -87,6 +95,132 @@ __device__ inline void mfma_k64(const float (*Ap)[YP], const float (*Bp)[YP], f3
   }
 }
 
+// The far feedback of the previous step's tiles, as 64 x 64 x 64 products on
+// the CUs that this step's tiles leave free:
+//   row kind:    M[I, c] += e_IJ U_I[J, c]        for column blocks c >= J + 2
+//   column kind: Wk[r, J] -= U_O[I, r]^T M_IJ     for row blocks r >= I + 2
+// Task q of tile b targets block J + 2 + q (row kind) or I + 2 + q (column
+// kind); tasks past the matrix are skipped. Nothing here touches what this
+// step's tiles read or write: their blocks lie on the anti-diagonal
+// I + J = ps + 1, the targets at least one block beyond it. The next task's
+// operands are loaded while the current one multiplies.
+__device__ inline bool far_valid(const YaqaStep& a, int idx, int nrow) {
+  if (idx < nrow) {
+    const int b = idx / a.p_qr, q = idx % a.p_qr;
+    const int J = a.ps - (a.p_I_lo + b);
+    return J + 2 + q < a.nt;
+  }
+  const int b = (idx - nrow) / a.p_qc, q = (idx - nrow) % a.p_qc;
+  return a.p_I_lo + b + 2 + q < a.mt;
+}
+
+struct FarOps {
+  const float* A;  // row kind [m][k], column kind [k][m]
+  const float* B;  // [k][n]
+  float* C;        // output block, row stride ld
+  int64_t lda, ldb;
+};
+
+__device__ inline FarOps far_ops(const YaqaStep& a, int idx, int nrow) {
+  FarOps o;
+  if (idx < nrow) {
+    const int b = idx / a.p_qr, q = idx % a.p_qr;
+    const int I = a.p_I_lo + b, J = a.ps - I, c = J + 2 + q;
+    o.A = a.E + int64_t(I) * YT * a.ld + int64_t(J) * YT;
+    o.lda = a.ld;
+    o.B = a.UI + int64_t(J) * YT * a.ldI + int64_t(c) * YT;
+    o.ldb = a.ldI;
+    o.C = a.Mp + int64_t(I) * YT * a.ld + int64_t(c) * YT;
+  } else {
+    const int b = (idx - nrow) / a.p_qc, q = (idx - nrow) % a.p_qc;
+    const int I = a.p_I_lo + b, J = a.ps - I, r = I + 2 + q;
+    o.A = a.UO + int64_t(I) * YT * a.ldO + int64_t(r) * YT;
+    o.lda = a.ldO;
+    o.B = a.Mp + int64_t(I) * YT * a.ld + int64_t(J) * YT;
+    o.ldb = a.ld;
+    o.C = a.Wk + int64_t(r) * YT * a.ld + int64_t(J) * YT;
+  }
+  return o;
+}
+
+__device__ inline int far_next(const YaqaStep& a, int idx, int nrow, int ntot) {
+  while (idx < ntot && !far_valid(a, idx, nrow)) idx += a.nfar;
+  return idx;
+}
+
+constexpr int FNV = YT * YT / 4 / 256;  // float4 per thread and block
+
+static_assert(FNV == 4, "far-task operand registers are written out for 4 float4 per block");
+
+// 4 float4 of each operand block per thread, as named registers (arrays of
+// them carried around the task loop were placed in scratch memory)
+struct FarRegs {
+  float4 a0, a1, a2, a3, b0, b1, b2, b3;
+};
+
+__device__ inline FarRegs far_load(const FarOps& o) {
+  const int t = threadIdx.x;
+  const int row = t / (YT / 4), col = 4 * (t % (YT / 4));  // element t; t + 256 h is 16 h rows down
+  const float* pa = o.A + row * o.lda + col;
+  const float* pb = o.B + row * o.ldb + col;
+  FarRegs v;
+  v.a0 = *reinterpret_cast<const float4*>(pa);
+  v.a1 = *reinterpret_cast<const float4*>(pa + 16 * o.lda);
+  v.a2 = *reinterpret_cast<const float4*>(pa + 32 * o.lda);
+  v.a3 = *reinterpret_cast<const float4*>(pa + 48 * o.lda);
+  v.b0 = *reinterpret_cast<const float4*>(pb);
+  v.b1 = *reinterpret_cast<const float4*>(pb + 16 * o.ldb);
+  v.b2 = *reinterpret_cast<const float4*>(pb + 32 * o.ldb);
+  v.b3 = *reinterpret_cast<const float4*>(pb + 48 * o.ldb);
+  return v;
+}
+
+__device__ __attribute__((always_inline)) inline void far_tasks(const YaqaStep& a, int f, float* sm) {
+  float(*As)[YP] = reinterpret_cast<float(*)[YP]>(sm);
+  float(*Bs)[YP] = reinterpret_cast<float(*)[YP]>(sm + YT * YP);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
+  const int nrow = a.p_cnt * a.p_qr;
+  const int ntot = nrow + a.p_cnt * a.p_qc;
+  int idx = far_next(a, f, nrow, ntot);
+  if (idx >= ntot) return;
+  FarRegs v = far_load(far_ops(a, idx, nrow));
+  while (idx < ntot) {
+    __syncthreads();  // the previous task's LDS reads are done
+    {
+      const int row = t / (YT / 4), col = 4 * (t % (YT / 4));
+      *reinterpret_cast<float4*>(&As[row][col]) = v.a0;
+      *reinterpret_cast<float4*>(&As[row + 16][col]) = v.a1;
+      *reinterpret_cast<float4*>(&As[row + 32][col]) = v.a2;
+      *reinterpret_cast<float4*>(&As[row + 48][col]) = v.a3;
+      *reinterpret_cast<float4*>(&Bs[row][col]) = v.b0;
+      *reinterpret_cast<float4*>(&Bs[row + 16][col]) = v.b1;
+      *reinterpret_cast<float4*>(&Bs[row + 32][col]) = v.b2;
+      *reinterpret_cast<float4*>(&Bs[row + 48][col]) = v.b3;
+    }
+    __syncthreads();
+    const bool rowk = idx < nrow;
+    float* C = far_ops(a, idx, nrow).C;
+    float cv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cv[r] = C[(wm + 8 * (r >> 2) + 4 * lk + (r & 3)) * a.ld + wn + lr];
+    const int nidx = far_next(a, idx + a.nfar, nrow, ntot);
+    // after the last task this reloads the current one (unused)
+    v = far_load(far_ops(a, nidx < ntot ? nidx : idx, nrow));
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    if (rowk) mfma_k64<true>(As, Bs, acc, wm, wn, lr, lk);
+    else mfma_k64<false>(As, Bs, acc, wm, wn, lr, lk);
+    const float alpha = rowk ? 1.f : -1.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      C[(wm + 8 * (r >> 2) + 4 * lk + (r & 3)) * a.ld + wn + lr] = cv[r] + alpha * acc[r];
+    idx = nidx;
+  }
+}
+
 // One tile (I, J) of the wavefront. Besides the far feedback already in Wk
 // and Mp it takes the near feedback of its two finished neighbours itself:
 //   P2 = e_{I,J-1} U_I[J-1, J]           (completes Mpart_IJ)
@@ -97,6 +231,10 @@ __device__ inline void mfma_k64(const float (*Ap)[YP], const float (*Bp)[YP], f3
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void yaqa_tile_kernel(
     YaqaStep a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
+  if (int(blockIdx.x) >= a.ntile) {
+    far_tasks(a, int(blockIdx.x) - a.ntile, sm);
+    return;
+  }
   float(*UIs)[YP] = reinterpret_cast<float(*)[YP]>(sm);               // U_I[l][c], 0 for c < l
   float(*UOt)[YP] = reinterpret_cast<float(*)[YP]>(sm + YT * YP);     // U_O[k][i] at [i][k], 0 for k > i
   float(*Ms)[YP] = reinterpret_cast<float(*)[YP]>(sm + 2 * YT * YP);  // Mpart (+ P2)
@@ -462,41 +600,41 @@ kq_status yaqa_run(float* W, const float* U_in, const float* U_out, const float*
   KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(yaqa_tile_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(YAQA_LDS)));
 
-  // Everything runs in order on the caller's stream: the tiles of step s,
-  // then the far feedback of step s (targets two or more tiles away), which
-  // the tiles of step s + 2 are the first to need.
+  // One launch per step, on the caller's stream: the tiles of step s, and on
+  // the CUs they leave free the far feedback of step s - 1, which the tiles
+  // of step s + 1 are the first to need.
+  int ncu = 0;
+  {
+    int dev = 0;
+    KQ_HIP(hipGetDevice(&dev));
+    KQ_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  }
+  st.mt = mt;
+  st.nt = nt;
   const int nsteps = mt + nt - 1;
   for (int sidx = 0; sidx < nsteps; ++sidx) {
     const int I_lo = std::max(0, sidx - nt + 1), I_hi = std::min(sidx, mt - 1);
     const int cnt = I_hi - I_lo + 1;
-    const int J_hi = sidx - I_lo;
     st.s = sidx;
     st.I_lo = I_lo;
-    yaqa_tile_kernel<<<unsigned(cnt), 256, YAQA_LDS, s>>>(st);
+    st.ntile = cnt;
+    st.nfar = 0;
+    st.p_cnt = 0;
+    if (sidx > 0) {
+      const int ps = sidx - 1;
+      const int pI_lo = std::max(0, ps - nt + 1), pI_hi = std::min(ps, mt - 1);
+      st.ps = ps;
+      st.p_I_lo = pI_lo;
+      st.p_cnt = pI_hi - pI_lo + 1;
+      // the tile with the smallest J (the largest I) has the most row-kind
+      // targets, the one with the smallest I the most column-kind targets
+      st.p_qr = std::max(0, nt - 2 - (ps - pI_hi));
+      st.p_qc = std::max(0, mt - 2 - pI_lo);
+      const int64_t space = int64_t(st.p_cnt) * (st.p_qr + st.p_qc);
+      if (space > 0) st.nfar = int(std::min<int64_t>(space, std::max(64, ncu - cnt)));
+    }
+    yaqa_tile_kernel<<<unsigned(cnt + st.nfar), 256, YAQA_LDS, s>>>(st);
     KQ_HIP(hipGetLastError());
-    // M[I, blocks >= J + 2] += e_IJ U_I[J, same]
-    GemmArgs gr = gemm_args(E + int64_t(I_lo) * YT * np + int64_t(J_hi) * YT, np,
-                            UI + int64_t(J_hi) * YT * np, np, Mp + int64_t(I_lo) * YT * np, np, YT,
-                            np, YT, 1.f, 1.f, G_OUT_NSTART);
-    gr.batch = cnt;
-    gr.strideA = int64_t(YT) * np - YT;
-    gr.strideB = -int64_t(YT) * np;
-    gr.strideC = int64_t(YT) * np;
-    gr.ostart = int64_t(J_hi + 2) * YT;
-    gr.ostart_ofs = -YT;
-    if (sidx - I_hi + 2 < nt) KQ_TRY(gemm_f32(gr, s));  // the smallest J has targets
-    // Wk[blocks >= I + 2, J] -= U_O[I, same]^T M_IJ
-    GemmArgs gc = gemm_args(UO + int64_t(I_lo) * YT * mp, mp,
-                            Mp + int64_t(I_lo) * YT * np + int64_t(J_hi) * YT, np,
-                            Wk + int64_t(J_hi) * YT, np, mp, YT, YT, -1.f, 1.f,
-                            G_TRANS_A | G_OUT_MSTART);
-    gc.batch = cnt;
-    gc.strideA = int64_t(YT) * mp;
-    gc.strideB = int64_t(YT) * np - YT;
-    gc.strideC = -int64_t(YT);
-    gc.ostart = int64_t(I_lo + 2) * YT;
-    gc.ostart_ofs = YT;
-    if (I_lo + 2 < mt) KQ_TRY(gemm_f32(gc, s));  // the smallest I has targets
   }
   return KQ_OK;
 }
