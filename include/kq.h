@@ -24,12 +24,19 @@
  *    event. Scratch memory is passed in as (ws, ws_bytes); kq_workspace_size
  *    gives the size each call needs. The only state kept between calls is the
  *    measurement hook of kq_set_kernel_events (two caller-owned event handles
- *    per thread, unset by default) and the testing knob of kq_set_gemm_tile
- *    (per thread, automatic by default); nothing else carries over from one
- *    call to the next.
+ *    per thread, unset by default), the testing knob of kq_set_gemm_tile
+ *    (per thread, automatic by default), a 64-byte pinned host buffer
+ *    per calling thread (hipHostMalloc on first use, kept until the process
+ *    ends) through which the calls below read their host results, and the
+ *    host copy of the last launch schedule kq_accumulate_cov built on the
+ *    thread (rebuilt when the shapes or the requested outputs change);
+ *    nothing else carries over from one call to the next.
  *  - Device work is enqueued on `stream` and is asynchronous, except calls
- *    that return host values (kq_sensitivity, kq_cholesky_inv,
- *    kq_layer_objective), which synchronize the stream before returning.
+ *    that return host values: kq_sensitivity and kq_layer_objective wait
+ *    until the stream is idle before returning; kq_cholesky_inv waits for
+ *    its factorization (to report a non-positive pivot) and returns with the
+ *    inverse still enqueued. These waits poll the stream (the calling
+ *    thread spins) rather than block.
  *  - Arguments are validated on the host before anything is launched;
  *    errors return a kq_status and kq_last_error() gives a message (per
  *    thread). Calls on disjoint buffers may run concurrently.
@@ -191,7 +198,10 @@ kq_status kq_sensitivity(const float* HX, const float* HG, int64_t d_in, int64_t
  * receives 0, or k+1 where k is the original column index of the first
  * non-positive pivot (the factorisation proceeds from the last column to the
  * first); that case returns KQ_ERR_NOT_PD and leaves U undefined.
- * Synchronizes the stream. */
+ * Waits for the factorization before returning (the pivot status is read on
+ * the host); the triangular inverse that completes U is enqueued on the
+ * stream after that check, so U is ready when the stream's work before the
+ * next synchronization point has run, as for the asynchronous calls. */
 kq_status kq_cholesky_inv(const float* H, int64_t n, float damp, float* U, int32_t* info,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 

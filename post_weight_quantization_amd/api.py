@@ -59,10 +59,17 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
-def _ws(nbytes: int, device, ws):
+def _ws(nbytes: int, device, ws, stream=None):
+    """The caller's workspace, or a new one. A new one is freed when the
+    binding returns, possibly with the call's kernels still queued: on a
+    stream other than the current one it is recorded there, so the caching
+    allocator does not hand it out again before that stream's work is done."""
     if ws is not None:
         return ws
-    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    t = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+    return t
 
 
 def kq_accumulate_cov(X, Xq, G, alpha: float, beta: float, HX=None, D=None, HG=None,
@@ -98,7 +105,7 @@ def kq_accumulate_cov(X, Xq, G, alpha: float, beta: float, HX=None, D=None, HG=N
         HG = torch.empty(d_out, d_out, dtype=torch.float32, device=dev)
     if ws is None:
         need = kq_workspace_size(N.KQ_OP_ACCUMULATE_COV, d_out, d_in, n_tok, dt)
-        ws = _ws(need, dev, None)
+        ws = _ws(need, dev, None, stream)
     check(N.lib.kq_accumulate_cov(_ptr(X), _ptr(Xq), _ptr(G), dt, n_tok, d_in, d_out, alpha, beta,
                                   _ptr(HX), _ptr(D), _ptr(HG), _ptr(ws), _nbytes(ws), _stream(stream)))
     return HX, D, HG
@@ -123,7 +130,7 @@ def kq_biip(W, HX, D, HG, sign_in, sign_out, blk_in: int = 0, blk_out: int = 0, 
         s_x = torch.empty(d_in, dtype=torch.float32, device=dev)
     if s_g is None:
         s_g = torch.empty(d_out, dtype=torch.float32, device=dev)
-    ws = _ws(kq_workspace_size(N.KQ_OP_BIIP, d_out, d_in), dev, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_BIIP, d_out, d_in), dev, ws, stream)
     check(N.lib.kq_biip(_ptr(W), _ptr(HX), _ptr(D), _ptr(HG), d_out, d_in, _ptr(sign_in),
                         _ptr(sign_out), blk_in, blk_out, _ptr(s_x), _ptr(s_g), _ptr(ws), _nbytes(ws),
                         _stream(stream)))
@@ -135,7 +142,7 @@ def kq_sensitivity(HX, HG, ws=None, stream=None):
     _expect(HX, (HX.shape[0], HX.shape[0]), torch.float32, "HX")
     _expect(HG, (HG.shape[0], HG.shape[0]), torch.float32, "HG")
     _need_cuda(HX, HG, ws)
-    ws = _ws(kq_workspace_size(N.KQ_OP_SENSITIVITY, HG.shape[0], HX.shape[0]), HX.device, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_SENSITIVITY, HG.shape[0], HX.shape[0]), HX.device, ws, stream)
     tx, tg, s = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
     check(N.lib.kq_sensitivity(_ptr(HX), _ptr(HG), HX.shape[0], HG.shape[0], ctypes.byref(tx),
                                ctypes.byref(tg), ctypes.byref(s), _ptr(ws), _nbytes(ws),
@@ -144,14 +151,16 @@ def kq_sensitivity(HX, HG, ws=None, stream=None):
 
 
 def kq_cholesky_inv(H, damp: float, U=None, ws=None, stream=None):
-    """Upper U with U^T U = (H + damp*mean(diag H) I)^-1 (synchronizes the stream)."""
+    """Upper U with U^T U = (H + damp*mean(diag H) I)^-1. Waits for the
+    factorization (a non-positive pivot raises); the inverse is left queued
+    on the stream."""
     n = H.shape[0]
     _expect(H, (n, n), torch.float32, "H")
     _expect(U, (n, n), torch.float32, "U")
     _need_cuda(H, U, ws)
     if U is None:
         U = torch.empty_like(H)
-    ws = _ws(kq_workspace_size(N.KQ_OP_CHOLESKY_INV, n, n), H.device, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_CHOLESKY_INV, n, n), H.device, ws, stream)
     info = ctypes.c_int32(0)
     st = N.lib.kq_cholesky_inv(_ptr(H), n, damp, _ptr(U), ctypes.byref(info), _ptr(ws), _nbytes(ws),
                                _stream(stream))
@@ -166,7 +175,7 @@ def kq_form_p(D, U, P=None, ws=None, stream=None):
     _need_cuda(D, U, P, ws)
     if P is None:
         P = torch.empty_like(D)
-    ws = _ws(kq_workspace_size(N.KQ_OP_FORM_P, n, n), D.device, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_FORM_P, n, n), D.device, ws, stream)
     check(N.lib.kq_form_p(_ptr(D), _ptr(U), n, _ptr(P), _ptr(ws), _nbytes(ws), _stream(stream)))
     return P
 
@@ -192,7 +201,7 @@ def kq_gptaq_quantize(W, U, D, bits: int, group: int = 0, block: int = 128, code
         scale = torch.empty(d_out, ng, dtype=torch.float32, device=dev)
     if zero is None:
         zero = torch.empty(d_out, ng, dtype=torch.float32, device=dev)
-    ws = _ws(kq_workspace_size(N.KQ_OP_GPTAQ_QUANTIZE, d_out, d_in, cfg=cfg), dev, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_GPTAQ_QUANTIZE, d_out, d_in, cfg=cfg), dev, ws, stream)
     check(N.lib.kq_gptaq_quantize(_ptr(W), _ptr(U), _ptr(D), d_out, d_in, ctypes.byref(cfg),
                                   _ptr(codes), _ptr(scale), _ptr(zero), _ptr(ws), _nbytes(ws),
                                   _stream(stream)))
@@ -221,7 +230,7 @@ def kq_yaqa_quantize(W, U_in, U_out, D, bits: int, codes=None, scale=None, zero=
         scale = torch.empty(d_out, 1, dtype=torch.float32, device=dev)
     if zero is None:
         zero = torch.empty(d_out, 1, dtype=torch.float32, device=dev)
-    ws = _ws(kq_workspace_size(N.KQ_OP_YAQA_QUANTIZE, d_out, d_in, cfg=cfg), dev, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_YAQA_QUANTIZE, d_out, d_in, cfg=cfg), dev, ws, stream)
     check(N.lib.kq_yaqa_quantize(_ptr(W), _ptr(U_in), _ptr(U_out), _ptr(D), d_out, d_in,
                                  ctypes.byref(cfg), _ptr(codes), _ptr(scale), _ptr(zero), _ptr(ws),
                                  _nbytes(ws), _stream(stream)))
@@ -247,7 +256,7 @@ def kq_layer_objective(W0, What, HX, D, HG, ws=None, stream=None) -> float:
     _expect(D, (d_in, d_in), f32, "D")
     _expect(HG, (d_out, d_out), f32, "HG")
     _need_cuda(W0, What, HX, D, HG, ws)
-    ws = _ws(kq_workspace_size(N.KQ_OP_LAYER_OBJECTIVE, d_out, d_in), W0.device, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_LAYER_OBJECTIVE, d_out, d_in), W0.device, ws, stream)
     obj = ctypes.c_double()
     check(N.lib.kq_layer_objective(_ptr(W0), _ptr(What), _ptr(HX), _ptr(D), _ptr(HG), d_out, d_in,
                                    ctypes.byref(obj), _ptr(ws), _nbytes(ws), _stream(stream)))
@@ -318,7 +327,7 @@ def kq_apply_quantized(packed, bits: int, scale, zero, group: int, s_x, s_g, sig
     _need_cuda(packed, scale, zero, s_x, s_g, sign_in, sign_out, x, y, ws)
     if y is None:
         y = torch.empty(batch, d_out, dtype=torch.float32, device=x.device)
-    ws = _ws(kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED, d_out, d_in, batch), x.device, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED, d_out, d_in, batch), x.device, ws, stream)
     check(N.lib.kq_apply_quantized(_ptr(packed), bits, _ptr(scale), _ptr(zero), group, _ptr(s_x),
                                    _ptr(s_g), _ptr(sign_in), _ptr(sign_out), blk_in, blk_out, _ptr(x),
                                    batch, d_out, d_in, _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)))
@@ -379,7 +388,7 @@ def kq_apply_quantized_a4(packed, scale, zero, s_x, s_g, sign_in, sign_out, x, c
     _need_cuda(packed, scale, zero, s_x, s_g, sign_in, sign_out, x, y, act_codes, act_scale, ws)
     if y is None:
         y = torch.empty(batch, d_out, dtype=torch.float32, device=x.device)
-    ws = _ws(kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED_A4, d_out, d_in, batch), x.device, ws)
+    ws = _ws(kq_workspace_size(N.KQ_OP_APPLY_QUANTIZED_A4, d_out, d_in, batch), x.device, ws, stream)
     check(N.lib.kq_apply_quantized_a4(_ptr(packed), _ptr(scale), _ptr(zero), _ptr(s_x), _ptr(s_g),
                                       _ptr(sign_in), _ptr(sign_out), blk_in, blk_out, _ptr(x), batch,
                                       d_out, d_in, float(clip), _ptr(y), _ptr(act_codes),

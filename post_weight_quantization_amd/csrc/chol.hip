@@ -593,16 +593,12 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
                             size_t(sw) * sizeof(float), size_t(rows), hipMemcpyDeviceToDevice, s));
   }
 
-  // invert L in place
-  place_diag_kernel<<<dim3(NB, unsigned(nb)), NB, 0, s>>>(Dinv, nb, A, n);
-  KQ_HIP(hipGetLastError());
-  KQ_TRY(trtri_levels(A, n, T, s));
-  reverse_out_kernel<<<dim3(unsigned(cdiv(n, 256)), unsigned(n)), 256, 0, s>>>(A, n);
-  KQ_HIP(hipGetLastError());
-
+  // The pivot status is final once the last leaf has run. Reading it here,
+  // before the inverse is enqueued, leaves the inverse and the index reversal
+  // (about a fifth of the stage) queued when the call returns, so the
+  // caller's next launches reach the stream before it drains.
   int hinfo = INT_MAX;
-  KQ_HIP(hipMemcpyAsync(&hinfo, dinfo, sizeof(int), hipMemcpyDeviceToHost, s));
-  KQ_HIP(hipStreamSynchronize(s));
+  KQ_TRY(read_to_host(&hinfo, dinfo, sizeof(int), s));
   int32_t out = 0;
   if (hinfo != INT_MAX) {
     // reversed index k (0-based) = hinfo - 1  ->  original column n-1-k
@@ -610,6 +606,13 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
   }
   if (info) *info = out;
   if (out) return fail(KQ_ERR_NOT_PD, "cholesky_inv: matrix is not positive definite (column %d)", out - 1);
+
+  // invert L in place
+  place_diag_kernel<<<dim3(NB, unsigned(nb)), NB, 0, s>>>(Dinv, nb, A, n);
+  KQ_HIP(hipGetLastError());
+  KQ_TRY(trtri_levels(A, n, T, s));
+  reverse_out_kernel<<<dim3(unsigned(cdiv(n, 256)), unsigned(n)), 256, 0, s>>>(A, n);
+  KQ_HIP(hipGetLastError());
   return KQ_OK;
 }
 

@@ -589,6 +589,33 @@ CovSchedule build_schedule(int64_t n_tok, int64_t d_in, int64_t d_out, bool hx, 
   return S;
 }
 
+// The schedule depends only on the shapes and on which outputs are asked for.
+// Building it takes a few hundred microseconds of host time (as long as the
+// kernels of a small token chunk), so the last one built is kept per thread.
+const CovSchedule& schedule_for(int64_t n_tok, int64_t d_in, int64_t d_out, bool hx, bool d,
+                                bool hg) {
+  struct Cache {
+    bool valid = false;
+    int64_t n_tok = 0, d_in = 0, d_out = 0;
+    bool hx = false, d = false, hg = false;
+    CovSchedule S;
+  };
+  thread_local Cache c;
+  if (!c.valid || c.n_tok != n_tok || c.d_in != d_in || c.d_out != d_out || c.hx != hx ||
+      c.d != d || c.hg != hg) {
+    c.valid = false;
+    c.S = build_schedule(n_tok, d_in, d_out, hx, d, hg);
+    c.n_tok = n_tok;
+    c.d_in = d_in;
+    c.d_out = d_out;
+    c.hx = hx;
+    c.d = d;
+    c.hg = hg;
+    c.valid = true;
+  }
+  return c.S;
+}
+
 size_t sched_bytes(const CovSchedule& S) {
   Arena ar{nullptr, 0, 0};
   ar.take<CovItem>(S.items.size());
@@ -607,7 +634,7 @@ size_t cov_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out, kq_dtype dt, boo
     return ar.used;
   }
   if (d) ar.take<uint16_t>(size_t(n_tok) * d_in);  // bf16 drift
-  return ar.used + 256 + sched_bytes(build_schedule(n_tok, d_in, d_out, hx, d, hg));
+  return ar.used + 256 + sched_bytes(schedule_for(n_tok, d_in, d_out, hx, d, hg));
 }
 
 kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int64_t n_tok,
@@ -638,29 +665,35 @@ kq_status cov_run(const void* X, const void* Xq, const void* G, kq_dtype dt, int
     return mark_kernel(KQ_OP_ACCUMULATE_COV, 1, s);
   }
 
-  const CovSchedule S = build_schedule(n_tok, d_in, d_out, HX != nullptr, D != nullptr, HG != nullptr);
+  const CovSchedule& S = schedule_for(n_tok, d_in, d_out, HX != nullptr, D != nullptr, HG != nullptr);
   if (S.items.empty()) return KQ_OK;
   CovArgs a{};
   a.Xq = static_cast<const uint16_t*>(Xq);
+  uint16_t* dx = nullptr;
   if (D) {
-    uint16_t* dx = ws.take<uint16_t>(size_t(n_tok) * d_in);
+    dx = ws.take<uint16_t>(size_t(n_tok) * d_in);
     if (!dx) return fail(KQ_ERR_WORKSPACE, "accumulate_cov: workspace too small");
-    const int64_t n8 = n_tok * d_in / 8;
-    drift_bf16_kernel<<<unsigned(std::min<int64_t>(cdiv(n8, 256), 16384)), 256, 0, s>>>(
-        static_cast<const uint4*>(X), static_cast<const uint4*>(Xq), reinterpret_cast<uint4*>(dx), n8);
-    KQ_HIP(hipGetLastError());
-    a.dX = dx;
   }
   CovItem* items = ws.take<CovItem>(S.items.size());
   CovRed* reds = ws.take<CovRed>(S.reds.size());
   float* pool = ws.take<float>(size_t(S.slots) * CT * CT);
   if (!items || (!S.reds.empty() && !reds) || (S.slots && !pool))
     return fail(KQ_ERR_WORKSPACE, "accumulate_cov: workspace too small");
+  // the schedule goes up first: a copy from pageable memory can hold the
+  // host until the stream reaches it, and ahead of the drift pass that wait
+  // does not leave the kernels behind it unlaunched
   KQ_HIP(hipMemcpyAsync(items, S.items.data(), S.items.size() * sizeof(CovItem),
                         hipMemcpyHostToDevice, s));
   if (!S.reds.empty())
     KQ_HIP(hipMemcpyAsync(reds, S.reds.data(), S.reds.size() * sizeof(CovRed),
                           hipMemcpyHostToDevice, s));
+  if (D) {
+    const int64_t n8 = n_tok * d_in / 8;
+    drift_bf16_kernel<<<unsigned(std::min<int64_t>(cdiv(n8, 256), 16384)), 256, 0, s>>>(
+        static_cast<const uint4*>(X), static_cast<const uint4*>(Xq), reinterpret_cast<uint4*>(dx), n8);
+    KQ_HIP(hipGetLastError());
+    a.dX = dx;
+  }
   a.G = static_cast<const uint16_t*>(G);
   a.d_in = d_in;
   a.d_out = d_out;

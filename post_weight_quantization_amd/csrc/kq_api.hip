@@ -44,6 +44,29 @@ kq_status mark_kernel(kq_op op, int edge, hipStream_t s) {
 }
 
 namespace {
+// Pinned host landing area for results read back to the host, one per
+// thread, allocated on first use and kept until the process ends.
+constexpr size_t READBACK_BYTES = 64;
+thread_local void* g_readback = nullptr;
+}
+
+kq_status read_to_host(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (bytes > READBACK_BYTES) return fail(KQ_ERR_ARG, "internal read-back of %zu bytes", bytes);
+  if (!g_readback) KQ_HIP(hipHostMalloc(&g_readback, READBACK_BYTES, hipHostMallocDefault));
+  // A copy into pinned memory is truly asynchronous, and polling the stream
+  // notices its completion within microseconds; a blocking synchronize (and
+  // a copy into pageable memory, which waits the same way) wakes the host
+  // only about 0.1 ms after the device has gone idle.
+  KQ_HIP(hipMemcpyAsync(g_readback, src, bytes, hipMemcpyDeviceToHost, s));
+  hipError_t e;
+  while ((e = hipStreamQuery(s)) == hipErrorNotReady) {
+  }
+  KQ_HIP(e);
+  memcpy(dst, g_readback, bytes);
+  return KQ_OK;
+}
+
+namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -282,8 +305,7 @@ kq_status kq_sensitivity(const float* HX, const float* HG, int64_t d_in, int64_t
   KQ_TRY(diag_sum(HX, d_in, dev, stream));
   KQ_TRY(diag_sum(HG, d_out, dev + 1, stream));
   double h[2] = {0.0, 0.0};
-  KQ_HIP(hipMemcpyAsync(h, dev, sizeof(h), hipMemcpyDeviceToHost, stream));
-  KQ_HIP(hipStreamSynchronize(stream));
+  KQ_TRY(read_to_host(h, dev, sizeof(h), stream));
   if (trHX) *trHX = h[0];
   if (trHG) *trHG = h[1];
   if (s) *s = h[0] * h[1];

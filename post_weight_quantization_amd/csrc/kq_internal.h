@@ -100,6 +100,10 @@ GemmArgs gemm_args(const float* A, int64_t lda, const float* B, int64_t ldb, flo
 
 // ------------------------------------------------------------ utilities
 kq_status fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// Copies `bytes` (at most 64) of device memory to the host once the stream's
+// earlier work is done: through a pinned per-thread buffer, polling the
+// stream.
+kq_status read_to_host(void* dst, const void* src, size_t bytes, hipStream_t s);
 kq_status fill_2d(float* p, int64_t rows, int64_t cols, int64_t ld, float v, hipStream_t s);
 
 // ------------------------------------------------------------ covariance

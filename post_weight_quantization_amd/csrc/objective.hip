@@ -77,8 +77,7 @@ kq_status objective_run(const float* W0, const float* What, const float* HX, con
   sum_kernel<<<1, 256, 0, s>>>(part, NPART, part + NPART);
   KQ_HIP(hipGetLastError());
   double h = 0.0;
-  KQ_HIP(hipMemcpyAsync(&h, part + NPART, sizeof(double), hipMemcpyDeviceToHost, s));
-  KQ_HIP(hipStreamSynchronize(s));
+  KQ_TRY(read_to_host(&h, part + NPART, sizeof(double), s));
   *obj = h;
   return KQ_OK;
 }
