@@ -187,7 +187,10 @@ def test_sensitivity_exact_on_gpu_inputs():
 # ------------------------------------------------------------------ stage 3
 
 
-@pytest.mark.parametrize("n,cond", [(128, 1e2), (256, 1e3), (384, 1e3), (640, 1e4), (896, 1e3), (1024, 1e3)])
+# 1664 and 2176: three and four 512-column superblocks and a ragged last one
+# (trailing updates between superblocks, a narrow last superblock)
+@pytest.mark.parametrize("n,cond", [(128, 1e2), (256, 1e3), (384, 1e3), (640, 1e4), (896, 1e3), (1024, 1e3),
+                                    (1664, 1e3), (2176, 1e4)])
 def test_cholesky_inv_backward_error(n, cond):
     rng = np.random.default_rng(n)
     H = spd(rng, n, cond).astype(np.float32)
