@@ -124,16 +124,22 @@ kq_status kq_set_kernel_events(kq_op op, hipEvent_t start, hipEvent_t stop);
 
 /* Testing knob; not part of the method and not needed to use it.
  * The library's fp32 matrix products (factorization updates, triangular
- * inverse, P, the fold and the sweep's lazy updates) run on a 64-, 128- or
- * 256-wide output tile, chosen per product from its shape. After
+ * inverse, P, the fold and the sweep's lazy updates) run either on the fp32
+ * matrix cores with a 64-, 128- or 256-wide output tile, or, for large
+ * products with op(A) = A, on the bf16 matrix cores as six products of
+ * three-term bf16 splits of the fp32 operands (128-wide tile; fp32-level
+ * accuracy, fp32 accumulation), chosen per product from its shape. After
  * kq_set_gemm_tile(tile), later calls made from this thread use:
  *   tile   0: the choice by shape (the default);
- *          64: the 64-wide tile everywhere;
- *          128 or 256: that tile wherever a product allows it (a product
- *          computed in place, and the output-start-masked products of
- *          kq_yaqa_quantize, always take the 64-wide tile).
- * Every tile computes each output from the same operands with fp32
- * accumulation; results differ only in summation order.
+ *          64: the 64-wide fp32 tile everywhere;
+ *          128 or 256: that fp32 tile wherever a product allows it (a
+ *          product computed in place, and the output-start-masked products
+ *          of kq_yaqa_quantize, always take the 64-wide tile);
+ *          3: the three-term bf16 kernel for every product it can take
+ *          (op(A) = A, not in place, no output start), whatever its size;
+ *          the others by shape.
+ * Every choice computes each output from the same operands with fp32
+ * accumulation; results differ only in rounding and summation order.
  * Errors: KQ_ERR_ARG for any other value. */
 kq_status kq_set_gemm_tile(int tile);
 

@@ -279,9 +279,10 @@ def kq_set_kernel_events(op: int, start=None, stop=None, stream=None):
 
 
 def kq_set_gemm_tile(tile: int) -> None:
-    """Force the fp32 product tile of later calls on this thread: 0 chooses by
-    shape (the default), 64, 128 or 256 force one kernel where the product
-    allows it. A testing knob."""
+    """Force the fp32 product kernel of later calls on this thread: 0 chooses
+    by shape (the default), 64, 128 or 256 force that fp32 tile where the
+    product allows it, 3 the three-term bf16 kernel wherever it applies. A
+    testing knob."""
     check(N.lib.kq_set_gemm_tile(int(tile)))
 
 

@@ -6,6 +6,12 @@
 // operands restrict each tile's K range and are masked at load, so the
 // algorithmic (triangle-aware) flop counts are what the kernel executes.
 //
+// Kernels: the fp32 matrix-core kernels below (64-, 128- and 256-wide tiles)
+// and, for large products with op(A) = A, a kernel that runs the fp32
+// product on the bf16 matrix cores as six products of three-term bf16 splits
+// (fp32-level accuracy at 6 x 32 instead of 8 x 64 matrix-core cycles per
+// 16-deep step of a 32 x 32 block; "three bf16 terms" below).
+//
 // Tiling: T x T output tile per workgroup of 4 waves (2 x 2), T = 64 (each
 // wave one 32 x 32 v_mfma_f32_32x32x2_f32 accumulator) or T = 128 (each wave
 // 64 x 64 as 2 x 2 accumulators) where an in-place product needs one tile
@@ -373,6 +379,229 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       }
 }
 
+// ------------------------------------------------------------ three bf16 terms
+// fp32 products on the bf16 matrix cores. Each fp32 operand element is split
+// on the fly into three bf16 terms, x = h + m + l (each the bf16 nearest to
+// what the terms before it leave: 24 significant bits in all), and a product
+// takes the six term products whose weight reaches 2^-16 of the leading one,
+//   l_a h_b + m_a m_b + h_a l_b + m_a h_b + h_a m_b + h_a h_b,
+// on v_mfma_f32_32x32x16_bf16 with fp32 accumulation (a bf16 x bf16 product
+// is exact in fp32). The terms left out are below 2^-24 of the leading one:
+// the result carries fp32 rounding, at 6 x 32 matrix-core cycles per 16-deep
+// step of a 32 x 32 block against 8 x 64 for v_mfma_f32_32x32x2f32.
+//
+// 128 x 128 tile per workgroup of 4 waves (2 x 2, each 64 x 64 as 2 x 2
+// accumulators), K in stages of 32 through double-buffered LDS. Both operands
+// sit in LDS as [row][k] fp32 (row stride 36 floats), so a lane reads the 8
+// consecutive k of its row that an MFMA operand takes as two float4 and
+// splits them in registers. An operand with K contiguous in memory (A; B when
+// stored N x K) is copied as float4; one with N contiguous (B stored K x N)
+// is transposed on the way in, each wave reading 16 rows of 64 bytes so that
+// its scalar LDS stores fall in 64 different banks. Masks and bounds are
+// applied when a stage is stored. A is never transposed here (op(A) = A).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline void split3(f32x8 x, bf16x8& h, bf16x8& m, bf16x8& l) {
+  h = __builtin_convertvector(x, bf16x8);
+  const f32x8 r1 = x - __builtin_convertvector(h, f32x8);
+  m = __builtin_convertvector(r1, bf16x8);
+  const f32x8 r2 = r1 - __builtin_convertvector(m, f32x8);
+  l = __builtin_convertvector(r2, bf16x8);
+}
+
+constexpr int XT = 128;      // output tile
+constexpr int XK = 32;       // K per stage
+constexpr int XLD = XK + 4;  // LDS row stride (floats)
+
+template <bool TB>
+__global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) float As[2][XT * XLD];
+  __shared__ __attribute__((aligned(16))) float Bs[2][XT * XLD];
+  const uint32_t fl = g.flags;
+  int z, tm, tn;
+  tile_of(fl, int(cdiv(g.M, XT)), int(cdiv(g.N, XT)), g.batch > 0 ? g.batch : 1, z, tm, tn);
+  const float* __restrict__ A = g.A + z * g.strideA;
+  const float* __restrict__ B = g.B + z * g.strideB;
+  float* C = g.C + z * g.strideC;
+  const float* Cin = g.Cin ? g.Cin + z * g.strideC : nullptr;
+  const int64_t m0 = int64_t(tm) * XT;
+  const int64_t n0 = int64_t(tn) * XT;
+  if ((fl & G_OUT_LOWER) && n0 > m0 + XT - 1) return;
+  if ((fl & G_OUT_UPPER) && m0 > n0 + XT - 1) return;
+  if ((fl & G_OUT_SUPPER) && m0 >= n0 + XT - 1) return;
+
+  const int64_t ko = g.kbase + z * g.kofs;
+  int64_t klo = 0, khi = g.K;
+  if (fl & G_A_UPPER) klo = max(klo, m0 - ko);
+  if (fl & G_A_SUPPER) klo = max(klo, m0 + 1 - ko);
+  if (fl & G_A_LOWER) khi = min(khi, m0 + XT - ko);
+  if (fl & G_B_UPPER) khi = min(khi, n0 + XT - ko);
+  if (fl & G_B_LOWER) klo = max(klo, n0 - ko);
+  klo = max<int64_t>(0, klo) & ~int64_t(3);
+  if (klo >= khi && g.beta == 1.f && Cin == C) return;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int lr = lane & 31, lk = lane >> 5;
+  const bool amask = fl & (G_A_UPPER | G_A_LOWER | G_A_SUPPER);
+  const bool bmask = fl & (G_B_UPPER | G_B_LOWER);
+  const int64_t lda = g.lda, ldb = g.ldb;
+
+  // stage element mapping. K-contiguous operands: float4 h of thread t is row
+  // (t + 256 h) / 8, k 4 ((t + 256 h) % 8). B stored K x N: wave w's float4 h
+  // covers k 16 (c % 2) + lane / 4 and n 16 (c / 2) + 4 (lane % 4), c = 4 w + h.
+  float4 ra[4], rb[4];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int idx = t + 256 * h;
+      const int row = idx >> 3, k4 = 4 * (idx & 7);
+      const int64_t k = k0 + k4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m0 + row < g.M && k < khi) v = ld4(A + (m0 + row) * lda + k);
+      ra[h] = v;
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (TB) {
+        if (n0 + row < g.N && k < khi) u = ld4(B + (n0 + row) * ldb + k);
+      } else {
+        const int c = 4 * w + h;
+        const int kr = 16 * (c & 1) + (lane >> 2), nc = 16 * (c >> 1) + 4 * (lane & 3);
+        const int64_t kk = k0 + kr;
+        if (n0 + nc < g.N && kk < khi) u = ld4(B + kk * ldb + n0 + nc);
+      }
+      rb[h] = u;
+    }
+  };
+  auto store = [&](int64_t k0, int buf) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int idx = t + 256 * h;
+      const int row = idx >> 3, k4 = 4 * (idx & 7);
+      float4 v = ra[h];
+      if (amask) {
+        const int64_t m = m0 + row, kg = k0 + k4 + ko;
+        float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t kq = kg + q;
+          if (((fl & G_A_UPPER) && kq < m) || ((fl & G_A_SUPPER) && kq <= m) ||
+              ((fl & G_A_LOWER) && kq > m))
+            e[q] = 0.f;
+        }
+        v = make_float4(e[0], e[1], e[2], e[3]);
+      }
+      *reinterpret_cast<float4*>(&As[buf][row * XLD + k4]) = v;
+      float4 u = rb[h];
+      if (TB) {
+        if (bmask) {
+          const int64_t n = n0 + row, kg = k0 + k4 + ko;
+          float e[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t kq = kg + q;
+            if (((fl & G_B_UPPER) && kq > n) || ((fl & G_B_LOWER) && kq < n)) e[q] = 0.f;
+          }
+          u = make_float4(e[0], e[1], e[2], e[3]);
+        }
+        *reinterpret_cast<float4*>(&Bs[buf][row * XLD + k4]) = u;
+      } else {
+        const int c = 4 * w + h;
+        const int kr = 16 * (c & 1) + (lane >> 2), nc = 16 * (c >> 1) + 4 * (lane & 3);
+        float e[4] = {u.x, u.y, u.z, u.w};
+        if (bmask) {
+          const int64_t kg = k0 + kr + ko;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + nc + q;
+            if (((fl & G_B_UPPER) && kg > n) || ((fl & G_B_LOWER) && kg < n)) e[q] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Bs[buf][(nc + q) * XLD + kr] = e[q];
+      }
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int64_t nk = khi > klo ? khi - klo : 0;
+  const int nst = int(cdiv(nk, int64_t(XK)));
+  if (nst > 0) {
+    load(klo);
+    store(klo, 0);
+    __syncthreads();
+  }
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nst;
+    if (more) load(klo + int64_t(st + 1) * XK);
+#pragma unroll
+    for (int ks = 0; ks < XK; ks += 16) {
+      bf16x8 ah[2], am[2], al[2], bh[2], bm[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float* pa = &As[buf][(wm + 32 * i + lr) * XLD + ks + 8 * lk];
+        const float4 x0 = *reinterpret_cast<const float4*>(pa);
+        const float4 x1 = *reinterpret_cast<const float4*>(pa + 4);
+        split3(f32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w}, ah[i], am[i], al[i]);
+        const float* pb = &Bs[buf][(wn + 32 * i + lr) * XLD + ks + 8 * lk];
+        const float4 y0 = *reinterpret_cast<const float4*>(pb);
+        const float4 y1 = *reinterpret_cast<const float4*>(pb + 4);
+        split3(f32x8{y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w}, bh[i], bm[i], bl[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          f32x16 c = acc[i][j];
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[i], bm[j], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[i], bh[j], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bm[j], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], c, 0, 0, 0);
+          acc[i][j] = c;
+        }
+    }
+    if (more) store(klo + int64_t(st + 1) * XK, buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: acc[i][j][r] is element (wm + 32 i + 8 (r / 4) + 4 lk + r % 4,
+  // wn + 32 j + lr); the reads of C of a block are issued together
+  const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float cv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
+        const int64_t n = n0 + wn + 32 * j + lr;
+        cv[r] = (beta != 0.f && m < g.M && n < g.N) ? Cin[m * g.ldc + n] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
+        const int64_t n = n0 + wn + 32 * j + lr;
+        if (m >= g.M || n >= g.N) continue;
+        if ((fl & G_OUT_LOWER) && n > m) continue;
+        if ((fl & G_OUT_UPPER) && n < m) continue;
+        if ((fl & G_OUT_SUPPER) && n <= m) continue;
+        C[m * g.ldc + n] = alpha * acc[i][j][r] + beta * cv[r];
+      }
+    }
+}
+
 // ------------------------------------------------------------ large tiles
 // A 256 x 256 output tile per workgroup of 8 waves (2 x 4); each wave holds
 // 128 x 64 as 8 x 4 accumulators of v_mfma_f32_16x16x4f32 (128 AGPRs), so
@@ -713,12 +942,13 @@ GemmArgs gemm_args(const float* A, int64_t lda, const float* B, int64_t ldb, flo
 // tiles need at least four rounds to balance.
 // set_gemm_tile(64, 128 or 256) forces one kernel where it applies (tests).
 thread_local int t_forced_tile = 0;
+constexpr int X3_FORCED = 3;  // knob value: the three-term kernel wherever it applies
 
 int choose_tile(const GemmArgs& g, int64_t nb) {
   // in-place products need one tile across N; output starts are given in
   // multiples of the 64-wide tile
   if (g.flags & (G_C_ALIASES_A | G_OUT_NSTART | G_OUT_MSTART)) return 64;
-  if (t_forced_tile) return t_forced_tile;
+  if (t_forced_tile && t_forced_tile != X3_FORCED) return t_forced_tile;
   if (g.K < 256) return 64;
   const int64_t t256 = tiles_per_batch(g.flags, cdiv(g.M, 256), cdiv(g.N, 256)) * nb;
   const int64_t t128 = tiles_per_batch(g.flags, cdiv(g.M, 128), cdiv(g.N, 128)) * nb;
@@ -735,6 +965,24 @@ int choose_tile(const GemmArgs& g, int64_t nb) {
   const double e64 = 2.0 * double(t64) * 64.0 * 64.0 * K / (0.62 * chip_peak);
   if (e256 <= e128 && e256 <= e64) return 256;
   return e128 <= e64 ? 128 : 64;
+}
+
+// The three-term bf16 kernel takes products with op(A) = A and a K of at
+// least 256 that give it enough 128-wide tiles: 200 when every tile has the
+// same K range, 1024 (two rounds of two per CU) when a triangular operand
+// makes the K range differ from tile to tile. Below that the 64-wide fp32
+// tile was faster on the solver's products (kernel trace at 4096: the
+// 128-tile trailing update 49 against 39 us, the last triangular-inverse
+// level 177-194 against 125 us, P formation 354-426 against 296-325 us).
+// The testing knob of set_gemm_tile keeps the fp32 kernels.
+bool use_x3(const GemmArgs& g, int64_t nb) {
+  if (t_forced_tile && t_forced_tile != X3_FORCED) return false;
+  if (g.flags & (G_TRANS_A | G_C_ALIASES_A | G_OUT_NSTART | G_OUT_MSTART)) return false;
+  if (t_forced_tile == X3_FORCED) return true;
+  if (g.K < 256) return false;
+  const bool kmask = g.flags & (G_A_UPPER | G_A_SUPPER | G_A_LOWER | G_B_UPPER | G_B_LOWER);
+  const int64_t tiles = tiles_per_batch(g.flags, cdiv(g.M, XT), cdiv(g.N, XT)) * nb;
+  return tiles >= (kmask ? 1024 : 200);
 }
 
 template <int BT>
@@ -782,6 +1030,15 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
     return fail(KQ_ERR_SHAPE, "internal gemm: an in-place product needs N <= 128");
   GemmArgs ga = g;
   if (g.flags & (G_A_UPPER | G_A_SUPPER | G_A_LOWER | G_B_UPPER | G_B_LOWER)) ga.flags |= G_SNAKE;
+  if (use_x3(g, nb)) {
+    const int64_t tiles = tiles_per_batch(g.flags, cdiv(g.M, XT), cdiv(g.N, XT)) * nb;
+    if (tiles > INT32_MAX) return fail(KQ_ERR_SHAPE, "internal gemm: too many tiles");
+    const dim3 grid(static_cast<unsigned>(tiles), 1, 1);
+    if (g.flags & G_TRANS_B) gemm_x3_kernel<true><<<grid, 256, 0, s>>>(ga);
+    else gemm_x3_kernel<false><<<grid, 256, 0, s>>>(ga);
+    KQ_HIP(hipGetLastError());
+    return KQ_OK;
+  }
   const int tile = choose_tile(g, nb);
   if (tile == 256) return launch_big<256>(ga, nb, s);
   if (tile == 128) return launch_big<128>(ga, nb, s);

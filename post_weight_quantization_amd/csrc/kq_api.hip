@@ -171,8 +171,8 @@ const char* kq_version(void) { return "kq 0.1 gfx950"; }
 
 kq_status kq_set_gemm_tile(int tile) {
   clear_error();
-  if (tile != 0 && tile != 64 && tile != 128 && tile != 256)
-    return fail(KQ_ERR_ARG, "set_gemm_tile: tile must be 0 (by shape), 64, 128 or 256");
+  if (tile != 0 && tile != 3 && tile != 64 && tile != 128 && tile != 256)
+    return fail(KQ_ERR_ARG, "set_gemm_tile: tile must be 0 (by shape), 3 (three bf16 terms), 64, 128 or 256");
   set_gemm_tile(tile);
   return KQ_OK;
 }

@@ -1,9 +1,11 @@
-"""GPU parity of the solver with the 128- and 256-wide fp32 product tiles
-forced.
+"""GPU parity of the solver with the 128- and 256-wide fp32 product tiles,
+and the three-term bf16 product kernel, forced.
 
-The library chooses the product tile by shape, and the small shapes of the
-other parity tests all take the 64-wide one. Here kq_set_gemm_tile(128) and
-kq_set_gemm_tile(256) force the large-tile kernel into every product that
+The library chooses the product kernel by shape, and the small shapes of the
+other parity tests all take the 64-wide fp32 tile. Here kq_set_gemm_tile(128)
+and kq_set_gemm_tile(256) force the large-tile kernel, and
+kq_set_gemm_tile(3) the kernel that runs fp32 products as six products of
+three-term bf16 splits on the bf16 matrix cores, into every product that
 allows it, at sizes that are not multiples of the tile (ragged tiles in M,
 N and K), with triangular
 operands (factorization updates, triangular inverse, P, the fold), batched
@@ -24,7 +26,7 @@ if have_gpu():
     import post_weight_quantization_amd as kq
 
 
-@pytest.fixture(autouse=True, params=[128, 256])
+@pytest.fixture(autouse=True, params=[128, 256, 3])
 def large_tiles(request):
     kq.kq_set_gemm_tile(request.param)
     yield request.param
@@ -89,8 +91,8 @@ def test_layer_objective_large_tiles():
 
 
 def test_tiles_agree(large_tiles):
-    """The same factorization on the large and the 64-wide tile: fp32
-    results that differ only in summation order."""
+    """The same factorization on the forced kernel and the 64-wide tile:
+    fp32 results that differ only in rounding and summation order."""
     rng = np.random.default_rng(5)
     n = 640
     H = dev(spd(rng, n, 1e3).astype(np.float32))

@@ -77,9 +77,9 @@ def test_kernel_event_hook_validation():
 
 
 def test_gemm_tile_knob_validation():
-    for bad in (1, 32, 96, 512, -64):
+    for bad in (1, 2, 4, 32, 96, 512, -64):
         assert N.lib.kq_set_gemm_tile(bad) == N.KQ_ERR_ARG
-    for ok in (64, 128, 256, 0):
+    for ok in (3, 64, 128, 256, 0):
         assert N.lib.kq_set_gemm_tile(ok) == N.KQ_OK
 
 
