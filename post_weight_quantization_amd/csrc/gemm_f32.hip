@@ -381,9 +381,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------ three bf16 terms
 // fp32 products on the bf16 matrix cores. Each fp32 operand element is split
-// on the fly into three bf16 terms, x = h + m + l (each the bf16 nearest to
-// what the terms before it leave: 24 significant bits in all), and a product
-// takes the six term products whose weight reaches 2^-16 of the leading one,
+// on the fly into three bf16 terms, x = h + m + l exactly (8 significant bits
+// each, by truncation: 24 in all), and a product takes the six term products
+// whose weight reaches 2^-16 of the leading one,
 //   l_a h_b + m_a m_b + h_a l_b + m_a h_b + h_a m_b + h_a h_b,
 // on v_mfma_f32_32x32x16_bf16 with fp32 accumulation (a bf16 x bf16 product
 // is exact in fp32). The terms left out are below 2^-24 of the leading one:
@@ -400,14 +400,35 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 // its scalar LDS stores fall in 64 different banks. Masks and bounds are
 // applied when a stage is stored. A is never transposed here (op(A) = A).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline void split3(f32x8 x, bf16x8& h, bf16x8& m, bf16x8& l) {
-  h = __builtin_convertvector(x, bf16x8);
-  const f32x8 r1 = x - __builtin_convertvector(h, f32x8);
-  m = __builtin_convertvector(r1, bf16x8);
-  const f32x8 r2 = r1 - __builtin_convertvector(m, f32x8);
-  l = __builtin_convertvector(r2, bf16x8);
+// Two fp32 values -> their three bf16 terms, packed in pairs (element 0 in the
+// low half). The terms are truncations: h keeps the top 8 significant bits of
+// x, m the top 8 of x - h, and l = x - h - m has at most 8 left, so
+// x = h + m + l exactly; each difference is exact in fp32.
+__device__ inline void split3x2(float x0, float x1, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+  h = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // {b0 >> 16, b1 >> 16}
+  const float r0 = x0 - __uint_as_float(b0 & 0xFFFF0000u);
+  const float r1 = x1 - __uint_as_float(b1 & 0xFFFF0000u);
+  const uint32_t c0 = __float_as_uint(r0), c1 = __float_as_uint(r1);
+  m = __builtin_amdgcn_perm(c1, c0, 0x07060302u);
+  const float s0 = r0 - __uint_as_float(c0 & 0xFFFF0000u);
+  const float s1 = r1 - __uint_as_float(c1 & 0xFFFF0000u);
+  l = __builtin_amdgcn_perm(__float_as_uint(s1), __float_as_uint(s0), 0x07060302u);
+}
+
+// 8 consecutive fp32 (two float4) -> three bf16x8 MFMA operands
+__device__ inline void split3(const float4& x0, const float4& x1, bf16x8& h, bf16x8& m, bf16x8& l) {
+  uint32_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;
+  split3x2(x0.x, x0.y, h0, m0, l0);
+  split3x2(x0.z, x0.w, h1, m1, l1);
+  split3x2(x1.x, x1.y, h2, m2, l2);
+  split3x2(x1.z, x1.w, h3, m3, l3);
+  const u32x4 vh = {h0, h1, h2, h3}, vm = {m0, m1, m2, m3}, vl = {l0, l1, l2, l3};
+  h = __builtin_bit_cast(bf16x8, vh);
+  m = __builtin_bit_cast(bf16x8, vm);
+  l = __builtin_bit_cast(bf16x8, vl);
 }
 
 constexpr int XT = 128;      // output tile
@@ -549,13 +570,11 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const float* pa = &As[buf][(wm + 32 * i + lr) * XLD + ks + 8 * lk];
-        const float4 x0 = *reinterpret_cast<const float4*>(pa);
-        const float4 x1 = *reinterpret_cast<const float4*>(pa + 4);
-        split3(f32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w}, ah[i], am[i], al[i]);
+        split3(*reinterpret_cast<const float4*>(pa), *reinterpret_cast<const float4*>(pa + 4), ah[i],
+               am[i], al[i]);
         const float* pb = &Bs[buf][(wn + 32 * i + lr) * XLD + ks + 8 * lk];
-        const float4 y0 = *reinterpret_cast<const float4*>(pb);
-        const float4 y1 = *reinterpret_cast<const float4*>(pb + 4);
-        split3(f32x8{y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w}, bh[i], bm[i], bl[i]);
+        split3(*reinterpret_cast<const float4*>(pb), *reinterpret_cast<const float4*>(pb + 4), bh[i],
+               bm[i], bl[i]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
