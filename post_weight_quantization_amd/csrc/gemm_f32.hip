@@ -431,12 +431,16 @@ __device__ inline void split3(const float4& x0, const float4& x1, bf16x8& h, bf1
   l = __builtin_bit_cast(bf16x8, vl);
 }
 
-constexpr int XT = 128;      // output tile
 constexpr int XK = 32;       // K per stage
 constexpr int XLD = XK + 4;  // LDS row stride (floats)
 
-template <bool TB>
+// XT = 128: 4 waves of 64 x 64 (2 x 2 accumulators); XT = 64: 4 waves of
+// 32 x 32 (one accumulator), for triangular products, whose K range differs
+// from tile to tile and which need more, shorter tiles to spread evenly.
+template <bool TB, int XT>
 __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
+  constexpr int FD = XT / 64;   // accumulators per wave and dimension
+  constexpr int XH = XT / 32;   // float4 per operand per thread and stage
   __shared__ __attribute__((aligned(16))) float As[2][XT * XLD];
   __shared__ __attribute__((aligned(16))) float Bs[2][XT * XLD];
   const uint32_t fl = g.flags;
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int wm = (w >> 1) * (XT / 2), wn = (w & 1) * (XT / 2);
   const int lr = lane & 31, lk = lane >> 5;
   const bool amask = fl & (G_A_UPPER | G_A_LOWER | G_A_SUPPER);
   const bool bmask = fl & (G_B_UPPER | G_B_LOWER);
@@ -472,11 +476,11 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
 
   // stage element mapping. K-contiguous operands: float4 h of thread t is row
   // (t + 256 h) / 8, k 4 ((t + 256 h) % 8). B stored K x N: wave w's float4 h
-  // covers k 16 (c % 2) + lane / 4 and n 16 (c / 2) + 4 (lane % 4), c = 4 w + h.
-  float4 ra[4], rb[4];
+  // covers k 16 (c % 2) + lane / 4 and n 16 (c / 2) + 4 (lane % 4), c = XH w + h.
+  float4 ra[XH], rb[XH];
   auto load = [&](int64_t k0) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < XH; ++h) {
       const int idx = t + 256 * h;
       const int row = idx >> 3, k4 = 4 * (idx & 7);
       const int64_t k = k0 + k4;
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
       if (TB) {
         if (n0 + row < g.N && k < khi) u = ld4(B + (n0 + row) * ldb + k);
       } else {
-        const int c = 4 * w + h;
+        const int c = XH * w + h;
         const int kr = 16 * (c & 1) + (lane >> 2), nc = 16 * (c >> 1) + 4 * (lane & 3);
         const int64_t kk = k0 + kr;
         if (n0 + nc < g.N && kk < khi) u = ld4(B + kk * ldb + n0 + nc);
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
   };
   auto store = [&](int64_t k0, int buf) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < XH; ++h) {
       const int idx = t + 256 * h;
       const int row = idx >> 3, k4 = 4 * (idx & 7);
       float4 v = ra[h];
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
         }
         *reinterpret_cast<float4*>(&Bs[buf][row * XLD + k4]) = u;
       } else {
-        const int c = 4 * w + h;
+        const int c = XH * w + h;
         const int kr = 16 * (c & 1) + (lane >> 2), nc = 16 * (c >> 1) + 4 * (lane & 3);
         float e[4] = {u.x, u.y, u.z, u.w};
         if (bmask) {
@@ -545,11 +549,11 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[FD][FD];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FD; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FD; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -566,9 +570,9 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
     if (more) load(klo + int64_t(st + 1) * XK);
 #pragma unroll
     for (int ks = 0; ks < XK; ks += 16) {
-      bf16x8 ah[2], am[2], al[2], bh[2], bm[2], bl[2];
+      bf16x8 ah[FD], am[FD], al[FD], bh[FD], bm[FD], bl[FD];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < FD; ++i) {
         const float* pa = &As[buf][(wm + 32 * i + lr) * XLD + ks + 8 * lk];
         split3(*reinterpret_cast<const float4*>(pa), *reinterpret_cast<const float4*>(pa + 4), ah[i],
                am[i], al[i]);
@@ -577,9 +581,9 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
                bm[i], bl[i]);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FD; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < FD; ++j) {
           f32x16 c = acc[i][j];
           c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[i], bm[j], c, 0, 0, 0);
@@ -598,9 +602,9 @@ __global__ __launch_bounds__(256) void gemm_x3_kernel(GemmArgs g) {
   // wn + 32 j + lr); the reads of C of a block are issued together
   const float alpha = g.alpha, beta = g.beta;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FD; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < FD; ++j) {
       float cv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -986,22 +990,28 @@ int choose_tile(const GemmArgs& g, int64_t nb) {
   return e128 <= e64 ? 128 : 64;
 }
 
-// The three-term bf16 kernel takes products with op(A) = A and a K of at
-// least 256 that give it enough 128-wide tiles: 200 when every tile has the
-// same K range, 1024 (two rounds of two per CU) when a triangular operand
-// makes the K range differ from tile to tile. Below that the 64-wide fp32
-// tile was faster on the solver's products (kernel trace at 4096: the
-// 128-tile trailing update 49 against 39 us, the last triangular-inverse
-// level 177-194 against 125 us, P formation 354-426 against 296-325 us).
-// The testing knob of set_gemm_tile keeps the fp32 kernels.
-bool use_x3(const GemmArgs& g, int64_t nb) {
-  if (t_forced_tile && t_forced_tile != X3_FORCED) return false;
-  if (g.flags & (G_TRANS_A | G_C_ALIASES_A | G_OUT_NSTART | G_OUT_MSTART)) return false;
-  if (t_forced_tile == X3_FORCED) return true;
-  if (g.K < 256) return false;
+// The three-term bf16 kernel's tile for a product, or 0 for the fp32
+// kernels. It takes products with op(A) = A and a K of at least 256:
+//  - with the same K range for every tile, on 128-wide tiles when there are
+//    at least 200 of them (below that the 64-wide fp32 tile was faster:
+//    136 tiles of 128 took 46 us against 26 us in the kernel trace at 4096);
+//  - where a triangular operand makes the K range differ from tile to tile,
+//    on 128-wide tiles from 1024 of them (two rounds of two per CU), else on
+//    64-wide tiles, whose larger number spreads the long tiles evenly (at
+//    4096: P formation 221 + 266 us against 303 + 336 on the 64-wide fp32
+//    tile and 303 + 384 on 128-wide ones; the fold, 1024 tiles of 128,
+//    490 us against 604 on 64-wide ones).
+// The testing knob of set_gemm_tile keeps the fp32 kernels, or forces this
+// one (64-wide for triangular products, else 128-wide) wherever it applies.
+int x3_tile(const GemmArgs& g, int64_t nb) {
+  if (t_forced_tile && t_forced_tile != X3_FORCED) return 0;
+  if (g.flags & (G_TRANS_A | G_C_ALIASES_A | G_OUT_NSTART | G_OUT_MSTART)) return 0;
   const bool kmask = g.flags & (G_A_UPPER | G_A_SUPPER | G_A_LOWER | G_B_UPPER | G_B_LOWER);
-  const int64_t tiles = tiles_per_batch(g.flags, cdiv(g.M, XT), cdiv(g.N, XT)) * nb;
-  return tiles >= (kmask ? 1024 : 200);
+  if (t_forced_tile == X3_FORCED) return kmask ? 64 : 128;
+  if (g.K < 256) return 0;
+  const int64_t t128 = tiles_per_batch(g.flags, cdiv(g.M, 128), cdiv(g.N, 128)) * nb;
+  if (kmask) return t128 >= 1024 ? 128 : 64;
+  return t128 >= 200 ? 128 : 0;
 }
 
 template <int BT>
@@ -1049,12 +1059,18 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
     return fail(KQ_ERR_SHAPE, "internal gemm: an in-place product needs N <= 128");
   GemmArgs ga = g;
   if (g.flags & (G_A_UPPER | G_A_SUPPER | G_A_LOWER | G_B_UPPER | G_B_LOWER)) ga.flags |= G_SNAKE;
-  if (use_x3(g, nb)) {
-    const int64_t tiles = tiles_per_batch(g.flags, cdiv(g.M, XT), cdiv(g.N, XT)) * nb;
+  if (const int xt = x3_tile(g, nb)) {
+    const int64_t tiles = tiles_per_batch(g.flags, cdiv(g.M, xt), cdiv(g.N, xt)) * nb;
     if (tiles > INT32_MAX) return fail(KQ_ERR_SHAPE, "internal gemm: too many tiles");
     const dim3 grid(static_cast<unsigned>(tiles), 1, 1);
-    if (g.flags & G_TRANS_B) gemm_x3_kernel<true><<<grid, 256, 0, s>>>(ga);
-    else gemm_x3_kernel<false><<<grid, 256, 0, s>>>(ga);
+    const bool tb = g.flags & G_TRANS_B;
+    if (xt == 128) {
+      if (tb) gemm_x3_kernel<true, 128><<<grid, 256, 0, s>>>(ga);
+      else gemm_x3_kernel<false, 128><<<grid, 256, 0, s>>>(ga);
+    } else {
+      if (tb) gemm_x3_kernel<true, 64><<<grid, 256, 0, s>>>(ga);
+      else gemm_x3_kernel<false, 64><<<grid, 256, 0, s>>>(ga);
+    }
     KQ_HIP(hipGetLastError());
     return KQ_OK;
   }
