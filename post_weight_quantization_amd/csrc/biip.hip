@@ -84,6 +84,73 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(float* M, int64_t rows, 
   }
 }
 
+// Row pass for Hadamard blocks of 4096: one block of one row per workgroup
+// of 256 threads, 16 elements per thread, the 12 butterfly levels in three
+// register stages of 4 with two exchanges through LDS between them (against
+// four radix-8 LDS passes plus the staging copies in the kernel above):
+//   stage 1: elements 4 t + e + 1024 k (index bits 0, 1 in e and 10, 11 in
+//            k), four float4 loads straight from memory, scaling applied;
+//   stage 2: elements t % 4 + 4 r + 64 (t / 4) (bits 2..5 in r);
+//   stage 3: elements t % 64 + 64 r + 1024 (t / 64) (bits 6..9 in r), stored
+//            straight to memory (each store 64 consecutive floats a wave).
+// LDS index i sits at i + 4 (i / 64): the float4 writes of stage 1 and the
+// reads and writes of stages 2 and 3 are free of bank conflicts.
+__device__ inline void bfly16(float (&v)[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (!(j & h)) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+}
+
+__device__ __host__ constexpr int pad64(int i) { return i + 4 * (i >> 6); }
+
+__global__ __launch_bounds__(256) void fwht_rows4096_kernel(float* M, int64_t rows, int64_t cols,
+                                                            const float* rowf, const float* colf,
+                                                            float gain) {
+  __shared__ __attribute__((aligned(16))) float sx[pad64(4096)];
+  const int64_t nblk = cols >> 12;
+  const int64_t row = blockIdx.x / nblk;
+  const int64_t c0 = (blockIdx.x % nblk) << 12;
+  float* p = M + row * cols + c0;
+  const float f = gain * (rowf ? rowf[row] : 1.f);
+  const int t = threadIdx.x;
+  float v[16];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * t + 1024 * k;
+    float4 x = *reinterpret_cast<const float4*>(p + i);
+    float4 g = colf ? *reinterpret_cast<const float4*>(colf + c0 + i) : make_float4(1.f, 1.f, 1.f, 1.f);
+    v[4 * k] = x.x * f * g.x;
+    v[4 * k + 1] = x.y * f * g.y;
+    v[4 * k + 2] = x.z * f * g.z;
+    v[4 * k + 3] = x.w * f * g.w;
+  }
+  bfly16(v);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<float4*>(sx + pad64(4 * t + 1024 * k)) =
+        make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  __syncthreads();
+  const int i2 = (t & 3) + 64 * (t >> 2);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = sx[pad64(i2 + 4 * r)];
+  bfly16(v);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sx[pad64(i2 + 4 * r)] = v[r];
+  __syncthreads();
+  const int i3 = (t & 63) + 1024 * (t >> 6);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = sx[pad64(i3 + 64 * r)];
+  bfly16(v);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p[i3 + 64 * r] = v[r];
+}
+
 // Column pass: chunk = nr rows (at row stride rs, starting at a group base)
 // x W cols, nr * W <= CH. Transforms over the nr rows.
 __global__ __launch_bounds__(256) void fwht_cols_kernel(float* M, int64_t rows, int64_t cols,
@@ -209,7 +276,9 @@ kq_status fwht_rows(float* M, int64_t rows, int64_t cols, int64_t blk, const flo
   if (L > CHR) return fail(KQ_ERR_UNSUPPORTED, "biip: Hadamard blocks above %d are not supported", CHR);
   const int64_t chunks = cdiv(rows, R) * (cols / L);
   const int lgb = ilog2(blk);
-  if (lgb == 12)
+  if (lgb == 12 && cols % 4096 == 0 && rows * (cols >> 12) <= INT32_MAX) {
+    fwht_rows4096_kernel<<<unsigned(rows * (cols >> 12)), 256, 0, s>>>(M, rows, cols, rowf, colf, gain);
+  } else if (lgb == 12)
     fwht_rows_kernel<12><<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, ilog2(L), lgb, rowf, colf, gain);
   else if (lgb == 13)
     fwht_rows_kernel<13><<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, ilog2(L), lgb, rowf, colf, gain);
