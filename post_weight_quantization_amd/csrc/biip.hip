@@ -186,6 +186,53 @@ __global__ __launch_bounds__(256) void fwht_cols_kernel(float* M, int64_t rows, 
   }
 }
 
+// Column pass over 6 row-index bits, 64 rows x 64 columns per workgroup (the
+// passes of 4096 blocks), in two register stages with one LDS exchange:
+//   stage 1: column t % 64, rows a = t / 64 + 4 j (bits 2..5 of a in j),
+//            loaded straight from memory (a wave reads 256 contiguous bytes
+//            of a row per load);
+//   stage 2: columns 4 (t % 16) .. + 3, rows a = 4 (t / 16) + e (bits 0, 1
+//            in e), stored straight to memory as float4.
+// Rows are taken as in fwht_cols_kernel: the chunk's row a is
+// rbase + a rs.
+__global__ __launch_bounds__(256) void fwht_cols64_kernel(float* M, int64_t rows, int64_t cols,
+                                                          int64_t rs, int64_t group_rows) {
+  constexpr int LD = 68;
+  __shared__ __attribute__((aligned(16))) float sx[64 * LD];
+  const int64_t col_chunks = cols >> 6;
+  const int64_t rchunk = blockIdx.x / col_chunks;
+  const int64_t c0 = (blockIdx.x % col_chunks) * 64;
+  const int64_t grp = rchunk / rs, off = rchunk % rs;
+  const int64_t rbase = grp * group_rows + off;
+  const int t = threadIdx.x;
+  {
+    const int c = t & 63, q = t >> 6;
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = M[(rbase + int64_t(q + 4 * j) * rs) * cols + c0 + c];
+    bfly16(v);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sx[(q + 4 * j) * LD + c] = v[j];
+  }
+  __syncthreads();
+  const int cg = t & 15, h = t >> 4;
+  float4 u[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) u[e] = *reinterpret_cast<const float4*>(&sx[(4 * h + e) * LD + 4 * cg]);
+  auto bf = [](float4& a, float4& b) {
+    const float4 x = a, y = b;
+    a = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+    b = make_float4(x.x - y.x, x.y - y.y, x.z - y.z, x.w - y.w);
+  };
+  bf(u[0], u[1]);
+  bf(u[2], u[3]);
+  bf(u[0], u[2]);
+  bf(u[1], u[3]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    *reinterpret_cast<float4*>(M + (rbase + int64_t(4 * h + e) * rs) * cols + c0 + 4 * cg) = u[e];
+}
+
 // Sum of squares of each row (one wave per row).
 __global__ __launch_bounds__(256) void row_sumsq_kernel(const float* W, int64_t rows, int64_t cols,
                                                         float* out) {
@@ -301,8 +348,12 @@ kq_status fwht_cols(float* M, int64_t rows, int64_t cols, int64_t blk, hipStream
     int lgW = 12 - k;
     while (lgW > 2 && cols % (int64_t(1) << lgW) != 0) --lgW;
     const int64_t row_chunks = (rows / group_rows) * rs;
-    const int64_t chunks = row_chunks * (cols >> lgW);
-    fwht_cols_kernel<<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, k, lgW, rs, group_rows);
+    if (k == 6 && cols % 64 == 0) {
+      fwht_cols64_kernel<<<unsigned(row_chunks * (cols >> 6)), 256, 0, s>>>(M, rows, cols, rs, group_rows);
+    } else {
+      const int64_t chunks = row_chunks * (cols >> lgW);
+      fwht_cols_kernel<<<unsigned(chunks), 256, 0, s>>>(M, rows, cols, k, lgW, rs, group_rows);
+    }
     KQ_HIP(hipGetLastError());
     lo += k;
   }
