@@ -37,15 +37,26 @@ constexpr int NB = 128;   // leaf (diagonal block) size
 constexpr int SB = 512;   // superblock: columns between two full trailing updates
 
 // A[i][j] = H[n-1-i][n-1-j] + delta [i == j] for i >= j (reads H's upper triangle)
+// A[i][j] = H[n-1-i][n-1-j] (+ delta on the diagonal) for j <= i, four
+// columns per thread: the float4 at H[n-1-i][n-4-j ..] reversed lands at
+// A[i][j ..]; columns past the diagonal are left alone. n % 4 == 0. Grid:
+// (column quads / 256, n).
 __global__ void reverse_damp_kernel(const float* __restrict__ H, int64_t n, const double* dsum,
                                     float damp, float* __restrict__ A) {
   const int64_t i = blockIdx.y;
+  const int64_t j = 4 * (int64_t(blockIdx.x) * blockDim.x + threadIdx.x);
+  if (j > i) return;
   const float delta = float(double(damp) * (*dsum) / double(n));
-  for (int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; j <= i;
-       j += int64_t(gridDim.x) * blockDim.x) {
-    float v = H[(n - 1 - i) * n + (n - 1 - j)];
-    if (i == j) v += delta;
-    A[i * n + j] = v;
+  const float4 h = *reinterpret_cast<const float4*>(H + (n - 1 - i) * n + (n - 4 - j));
+  float v[4] = {h.w, h.z, h.y, h.x};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] += j + q == i ? delta : 0.f;
+  if (j + 3 <= i) {
+    *reinterpret_cast<float4*>(A + i * n + j) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (j + q <= i) A[i * n + j + q] = v[q];
   }
 }
 
@@ -442,22 +453,34 @@ __global__ void place_diag_kernel(const float* __restrict__ Dinv, int64_t nblk, 
 }
 
 // In-place reversal: U[n-1-i][n-1-j] = X[i][j] for i >= j, zeros below.
+// U[n-1-i][n-1-j] = A[i][j] for j < i (zeroing A[i][j]) and the diagonal
+// reversed, in place, four columns per thread: A[i][j ..] (float4) goes
+// reversed to A[n-1-i][n-4-j ..]. Row n-1-i's target columns lie above its
+// diagonal, which no thread reads. n % 4 == 0. Grid: (column quads / 256, n).
 __global__ void reverse_out_kernel(float* A, int64_t n) {
   const int64_t i = blockIdx.y;
-  for (int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; j <= i;
-       j += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t ii = n - 1 - i, jj = n - 1 - j;
-    if (i == j) {
-      if (i < ii) {  // swap the diagonal pair once
-        const float a = A[i * n + i];
-        const float b = A[ii * n + ii];
-        A[i * n + i] = b;
-        A[ii * n + ii] = a;
-      }
-    } else {
-      const float v = A[i * n + j];
-      A[ii * n + jj] = v;
-      A[i * n + j] = 0.f;
+  const int64_t j = 4 * (int64_t(blockIdx.x) * blockDim.x + threadIdx.x);
+  if (j > i) return;
+  const int64_t ii = n - 1 - i;
+  if (j + 3 < i) {
+    const float4 v = *reinterpret_cast<const float4*>(A + i * n + j);
+    *reinterpret_cast<float4*>(A + ii * n + (n - 4 - j)) = make_float4(v.w, v.z, v.y, v.x);
+    *reinterpret_cast<float4*>(A + i * n + j) = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  // the quad that holds the diagonal: strictly-lower entries as above, then
+  // the diagonal pair swapped once (by the row with i < n-1-i)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t jq = j + q;
+    if (jq < i) {
+      A[ii * n + (n - 1 - jq)] = A[i * n + jq];
+      A[i * n + jq] = 0.f;
+    } else if (jq == i && i < ii) {
+      const float a = A[i * n + i];
+      const float b = A[ii * n + ii];
+      A[i * n + i] = b;
+      A[ii * n + ii] = a;
     }
   }
 }
@@ -537,7 +560,7 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
   set_int_kernel<<<1, 1, 0, s>>>(dinfo, INT_MAX);
   KQ_HIP(hipGetLastError());
   KQ_TRY(diag_sum(H, n, dsum, s));
-  reverse_damp_kernel<<<dim3(unsigned(cdiv(n, 256)), unsigned(n)), 256, 0, s>>>(H, n, dsum, damp, U);
+  reverse_damp_kernel<<<dim3(unsigned(cdiv(n / 4, 256)), unsigned(n)), 256, 0, s>>>(H, n, dsum, damp, U);
   KQ_HIP(hipGetLastError());
 
   KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(leaf_kernel),
@@ -611,7 +634,7 @@ kq_status chol_inv_run(const float* H, int64_t n, float damp, float* U, int32_t*
   place_diag_kernel<<<dim3(NB, unsigned(nb)), NB, 0, s>>>(Dinv, nb, A, n);
   KQ_HIP(hipGetLastError());
   KQ_TRY(trtri_levels(A, n, T, s));
-  reverse_out_kernel<<<dim3(unsigned(cdiv(n, 256)), unsigned(n)), 256, 0, s>>>(A, n);
+  reverse_out_kernel<<<dim3(unsigned(cdiv(n / 4, 256)), unsigned(n)), 256, 0, s>>>(A, n);
   KQ_HIP(hipGetLastError());
   return KQ_OK;
 }
