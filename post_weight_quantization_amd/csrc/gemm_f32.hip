@@ -405,7 +405,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Two fp32 values -> their three bf16 terms, packed in pairs (element 0 in the
 // low half). The terms are truncations: h keeps the top 8 significant bits of
 // x, m the top 8 of x - h, and l = x - h - m has at most 8 left, so
-// x = h + m + l exactly; each difference is exact in fp32.
+// x = h + m + l exactly (each difference is exact in fp32) wherever the
+// residuals are normal numbers, i.e. for |x| above about 2^-100.
 __device__ inline void split3x2(float x0, float x1, uint32_t& h, uint32_t& m, uint32_t& l) {
   const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
   h = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // {b0 >> 16, b1 >> 16}
