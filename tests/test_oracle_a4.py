@@ -26,6 +26,20 @@ def test_quantize_hand_worked():
     assert list(r["q"][0]) == [3, -3, 0]
 
 
+def test_quantize_divides_in_fp32():
+    """The rounded value is the fp32 quotient x2 / s, not x2 times the fp32
+    reciprocal of s. With max |x| = 0.1875, s = fl(0.1875 / 7) and
+    x = fl(1.5 s): the quotient is exactly 1.5, which rounds to 2 (ties to
+    even), while x * fl(1 / s) = 1.4999999 would round to 1."""
+    f = np.float32
+    s = f(0.1875) / f(7)
+    x = f(1.5) * s
+    assert x / s == f(1.5) and x * (f(1) / s) < f(1.5)
+    r = deploy.quantize_activations(np.array([[float(x), 0.1875]]), 4, 1.0)
+    assert r["s"][0] == s and r["t"][0, 0] == f(1.5)
+    assert list(r["q"][0]) == [2, 7]
+
+
 @pytest.mark.parametrize("bits,clip", [(4, 1.0), (4, 0.9), (4, 0.6), (3, 1.0), (8, 0.8)])
 def test_quantize_is_the_nearest_level(bits, clip):
     """Each code is the level nearest to x2 / s (brute force over all levels)."""

@@ -118,6 +118,13 @@ def test_covariances_chunked_equal_whole():
                                         for c in range(0, 96, 40)), 96)
     for w, p in zip(whole, parts):
         np.testing.assert_allclose(p, w, rtol=1e-13, atol=0)
+    # the diagonals alone, chunk by chunk, divide by the whole stream's count
+    dx = dg = 0.0
+    for c in range(0, 96, 40):
+        a, b = oracle.covariance_diagonals(Xq[c:c + 40], G[c:c + 40], 96)
+        dx, dg = dx + a, dg + b
+    np.testing.assert_allclose(dx, np.diag(whole[0]), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(dg, np.diag(whole[2]), rtol=1e-13, atol=0)
 
 
 def test_kronecker_vec_identity():
@@ -397,14 +404,22 @@ def test_sweep_matches_textbook_obs_with_explicit_inverses():
 
 
 def test_sweep_reduces_to_rtn_when_hx_identity_and_no_drift():
+    """With H_X = I and no drift nothing is fed back: the sweep is
+    round-to-nearest, group by group, with each group's grid (a ragged last
+    group included) stored in its own slot."""
     rng = np.random.default_rng(13)
-    W0 = rng.standard_normal((16, 64)).astype(np.float32)
-    for group in (0, 32):
-        U = oracle.inv_factor(np.eye(64), 0.01)
+    for n, group in ((64, 0), (64, 32), (104, 16)):
+        W0 = rng.standard_normal((16, n)).astype(np.float32)
+        U = oracle.inv_factor(np.eye(n), 0.01)
         res = oracle.sweep(W0, U, None, 2, group, block=32)
         codes, what = oracle.rtn(W0, 2, group)
         np.testing.assert_array_equal(res["codes"], codes)
         np.testing.assert_allclose(res["what"], what, rtol=0, atol=1e-15)
+        gs = group or n
+        for k, g0 in enumerate(range(0, n, gs)):
+            sc, zr = oracle.grid_fp32(W0[:, g0:g0 + gs], 2)
+            np.testing.assert_array_equal(res["scale"][:, k], sc)
+            np.testing.assert_array_equal(res["zero"][:, k], zr)
 
 
 def test_blocked_equals_unblocked():
@@ -420,6 +435,51 @@ def test_blocked_equals_unblocked():
         blk = oracle.sweep(W0, U, P, 2, group, block=8, forced_codes=ref["codes"])
         assert all(m[4] < 1e-9 for m in blk["mismatches"])
         np.testing.assert_allclose(blk["what"], ref["what"], atol=1e-12)
+
+
+def test_forced_replay_midpoint_distance_hand_worked():
+    """The replay diagnostic measures the pre-rounding value's distance to the
+    midpoint between the two codes, in grid steps and relative to the zero
+    point. Row [-0.25, 0.5] at 2 bits: scale 0.75/3 = 0.25, zero rint(1) = 1.
+    Column 0: w/scale = -1 -> code 0; forced to 1, the midpoint of codes 0
+    and 1 sits at 0.5 - 1 = -0.5 grid steps, so the distance is 0.5. Forced
+    to 2 (not adjacent) the distance is infinite. With U = I nothing moves
+    column 1: 0.5/0.25 = 2 -> code 3."""
+    W0 = np.array([[-0.25, 0.5]])
+    res = oracle.sweep(W0, np.eye(2), None, 2, 0, block=2, forced_codes=np.array([[1, 3]]))
+    assert res["scale"][0, 0] == np.float32(0.25) and res["zero"][0, 0] == 1.0
+    assert res["mismatches"] == [(0, 0, 0, 1, 0.5)]
+    np.testing.assert_array_equal(res["codes"], [[1, 3]])
+    np.testing.assert_array_equal(res["what"], [[0.0, 0.5]])
+    far = oracle.sweep(W0, np.eye(2), None, 2, 0, block=2, forced_codes=np.array([[2, 3]]))
+    assert far["mismatches"][0][:4] == (0, 0, 0, 2) and far["mismatches"][0][4] == np.inf
+
+
+def test_solve_layer_chains_the_pinned_stages():
+    """The whole-layer entry is the composition of the stages pinned above:
+    the sensitivity agrees with the diagonal shortcut taken straight from the
+    raw covariances and W (another route than the post-BiIP traces), each
+    stored intermediate is its stage applied to the previous one, and the
+    drift term reaches the sweep (dropping it changes codes here)."""
+    x, xq, g, W, si, so = _small_problem(seed=9, n=256, d_in=64, d_out=16)
+    HX, D, HG = oracle.covariances(x, xq, g)
+    out = oracle.solve_layer(HX, D, HG, W, si, so, bits=2, group=0, block=16, damp=0.01)
+    s_diag = oracle.scaled_traces(np.diag(HX), W, np.diag(HG))[2]
+    assert out["s"] == pytest.approx(s_diag, rel=1e-12)
+    np.testing.assert_allclose(out["U"].T @ out["U"],
+                               np.linalg.inv(oracle.damped(out["HX2"], 0.01)), rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(out["P"], oracle.form_p(out["D2"], out["U"]), rtol=0, atol=0)
+    with_p = oracle.sweep(out["W2"], out["U"], out["P"], 2, 0, 16)
+    no_p = oracle.sweep(out["W2"], out["U"], None, 2, 0, 16)
+    np.testing.assert_array_equal(out["codes"], with_p["codes"])
+    assert np.any(no_p["codes"] != with_p["codes"])
+    assert out["obj"] == pytest.approx(oracle.objective(out["W2"], with_p["what"], out["HX2"],
+                                                        out["D2"], out["HG2"]), rel=1e-12)
+    # the baseline rounds the same processed weights
+    codes_rtn, what_rtn = oracle.rtn(out["W2"], 2)
+    np.testing.assert_array_equal(out["codes_rtn"], codes_rtn)
+    assert out["obj_rtn"] == pytest.approx(oracle.objective(out["W2"], what_rtn, out["HX2"],
+                                                            out["D2"], out["HG2"]), rel=1e-12)
 
 
 def test_grid_golden():
@@ -474,9 +534,10 @@ def test_config0_objective_beats_rtn():
 
 
 def test_allocation_golden():
-    a = _load("allocation.json")
-    got = oracle.allocate_bits(a["s"], a["n_params"], a["widths"], a["avg_budget"])
-    assert got == a["bits"], a["why"]
+    for name in ("allocation.json", "allocation_ties.json"):
+        a = _load(name)
+        got = oracle.allocate_bits(a["s"], a["n_params"], a["widths"], a["avg_budget"])
+        assert got == a["bits"], a["why"]
 
 
 def _brute_force_alloc(s, n, widths, avg):

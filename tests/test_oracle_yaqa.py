@@ -81,6 +81,43 @@ def test_fixed_point_settles_by_antidiagonals():
         np.testing.assert_array_equal(part[done], full[done])
 
 
+def test_fixed_point_default_covers_the_longest_chain():
+    """A 3 x 4 case whose codes settle only after m + n - 2 = 5 iterations
+    (the longest above-left chain of a 3 x 4 array, key design 1): the
+    default count reaches the row-major result, one iteration fewer does not,
+    so a count tied to max(m, n) alone would stop too early. Found by a
+    search over seeds of this recipe (well-conditioned random factors,
+    condition number up to 1e3, N(0, 1) weights, 3 bits)."""
+    rng = np.random.default_rng(50)
+    m, n, bits = 3, 4, 3
+
+    def spd(k):
+        q, _ = np.linalg.qr(rng.standard_normal((k, k)))
+        return (q * np.exp(rng.uniform(0, np.log(1e3), k))) @ q.T
+
+    HI, HO = spd(n), spd(m)
+    W0 = rng.standard_normal((m, n))
+    sc, zr = kronq.grid_fp32(W0.astype(np.float32), bits)
+    ref = yaqa.round_two_sided(W0, kronq.inv_factor(HI, 0.0), kronq.inv_factor(HO, 0.0), sc, zr, bits)
+    codes, _, changed = yaqa.fixed_point(W0, HI, HO, sc, zr, bits)
+    assert not changed
+    np.testing.assert_array_equal(codes, ref["codes"])
+    early, _, changed = yaqa.fixed_point(W0, HI, HO, sc, zr, bits, iters=m + n - 3)
+    assert changed or np.any(early != ref["codes"])
+
+
+def test_forced_replay_midpoint_distance_hand_worked():
+    """Row [-0.25, 0.5] on the grid scale 0.25, zero 1 (2 bits), no feedback:
+    entry 0 has w/scale = -1 -> code 0; forced to 1 the midpoint of codes 0
+    and 1 lies at 0.5 - 1 = -0.5 grid steps, a distance of 0.5; entry 1 is
+    0.5/0.25 = 2 -> code 3."""
+    res = yaqa.round_two_sided(np.array([[-0.25, 0.5]]), np.eye(2), np.eye(1), np.float32(0.25),
+                               np.float32(1.0), 2, forced_codes=np.array([[1, 3]]))
+    assert res["mismatches"] == [(0, 0, 0, 1, 0.5)]
+    np.testing.assert_array_equal(res["codes"], [[1, 3]])
+    np.testing.assert_array_equal(res["what"], [[0.0, 0.5]])
+
+
 @pytest.mark.parametrize("m,n,bits", [(16, 24, 2), (24, 16, 4)])
 def test_residuals_decouple_the_kronecker_objective(m, n, bits):
     """tr(Delta H_I Delta^T H_O) = sum_ij eps_ij^2 d_O,i d_I,j with
