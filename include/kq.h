@@ -61,7 +61,7 @@ typedef enum {
   KQ_ERR_NONFINITE = 4,    /* NaN or Inf met where a finite value is required */
   KQ_ERR_WORKSPACE = 5,    /* ws_bytes smaller than kq_workspace_size */
   KQ_ERR_HIP = 6,          /* a HIP runtime call failed */
-  KQ_ERR_UNSUPPORTED = 7   /* valid request this build does not implement */
+  KQ_ERR_UNSUPPORTED = 7   /* valid request this library does not implement */
 } kq_status;
 
 typedef enum { KQ_BF16 = 0, KQ_F32 = 1 } kq_dtype;
