@@ -232,7 +232,7 @@ kq_status kq_form_p(const float* D, const float* U, int64_t n, float* P,
  * channel from W0', or per group of 128 columns from the working values when
  * the sweep reaches the group. Outputs: codes (d_out x d_in, uint8),
  * scale, zero (d_out x n_groups fp32, n_groups = 1 per channel, else
- * ceil(d_in / 128)). d_in must be a multiple of 128. */
+ * ceil(d_in / 128)). d_in must be a positive multiple of 128. */
 kq_status kq_gptaq_quantize(float* W, const float* U, const float* D,
                             int64_t d_out, int64_t d_in, const kq_quant_cfg* cfg,
                             uint8_t* codes, float* scale, float* zero,

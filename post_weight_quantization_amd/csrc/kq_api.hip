@@ -99,7 +99,8 @@ kq_status check_cfg(const kq_quant_cfg* cfg, int64_t d_in) {
     return fail(KQ_ERR_UNSUPPORTED, "gptaq_quantize: group must be 0 (per channel) or 128");
   if (cfg->block != 128) return fail(KQ_ERR_UNSUPPORTED, "gptaq_quantize: block must be 128");
   if (cfg->flags != 0) return fail(KQ_ERR_ARG, "gptaq_quantize: flags must be 0");
-  if (d_in % 128 != 0) return fail(KQ_ERR_SHAPE, "gptaq_quantize: d_in must be a multiple of 128");
+  if (d_in < 128 || d_in % 128 != 0)
+    return fail(KQ_ERR_SHAPE, "gptaq_quantize: d_in must be a positive multiple of 128");
   return KQ_OK;
 }
 
