@@ -40,6 +40,20 @@ def test_cost_model_at_the_bench_layer():
     assert abs(c["solve_flops"] / 1.832e11 - 1) < 1e-3
 
 
+def test_cost_model_at_the_down_proj_layer():
+    """W 8192 x 28672, 131072 tokens: S1 = n(n+1)N + 2n^2 N + m(m+1)N, the
+    factorization and P 2n^3/3 each, the trailing updates 2 m n^2, BiIP two
+    single-side passes over W, H_X, D and H_G (31.1 GB) plus the norm read of
+    W (0.94 GB), against a read-once floor of 15.6 GB."""
+    b = _bench()
+    c = b.stage_costs(SimpleNamespace(d_out=8192, d_in=28672, n_tok=131072))
+    assert abs(c["cov_flops"] / 3.3206e14 - 1) < 1e-4
+    assert abs(c["chol_flops"] / 1.5714e13 - 1) < 1e-4
+    assert abs(c["solve_flops"] / (1.5714e13 + 1.3469e13) - 1) < 1e-4
+    assert abs((c["biip_bytes"] - 4 * 8192 * 28672) / 31.14e9 - 1) < 1e-3
+    assert abs(c["biip_min_bytes"] / 15.57e9 - 1) < 1e-3
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
