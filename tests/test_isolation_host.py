@@ -80,3 +80,15 @@ def test_bench_and_entry_use_the_oracle_only_where_allowed():
     module only from smoke()."""
     assert set(_oracle_imports_by_function(os.path.join(ROOT, "bench.py"))) == {"cpu_baseline"}
     assert set(_oracle_imports_by_function(os.path.join(ROOT, "__graft_entry__.py"))) <= {"smoke"}
+
+
+def test_every_source_is_built_for_gfx950_without_packed_fp32():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("kq_build", os.path.join(PKG, "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    hip = {f for f in os.listdir(os.path.join(PKG, "csrc")) if f.endswith(".hip")}
+    assert hip == set(b.SOURCES) | set(b.PEAKS_SOURCES)
+    flags = " ".join(b.FLAGS)
+    assert "--offload-arch=gfx950" in flags
+    assert "-Xclang -target-feature -Xclang -packed-fp32-ops" in flags
