@@ -62,6 +62,10 @@ def test_apply_against_oracle(bits, group, bi, bo, batch):
     x = rng.standard_normal((batch, 512)).astype(np.float32)
     got, want = _run(*c, bits, group, x, bi, bo)
     assert rel_fro(got, want) < 1e-5
+    # and 32 outputs at a time, vector by vector: one wrong segment of small
+    # outputs cannot hide behind the rest
+    for v in range(batch):
+        assert tile_rel_fro(got[v:v + 1], want[v:v + 1], 32) < 1e-4, v
 
 
 def test_apply_on_the_pipeline_output():
@@ -96,6 +100,8 @@ def test_apply_ragged(bits, group, batch):
     x = rng.standard_normal((batch, 2176)).astype(np.float32)
     got, want = _run(*c, bits, group, x)
     assert rel_fro(got, want) < 1e-5
+    for v in range(batch):
+        assert tile_rel_fro(got[v:v + 1], want[v:v + 1], 32) < 1e-4, v
 
 
 @pytest.mark.parametrize("batch", [3, 4, 5, 6, 7, 9])
